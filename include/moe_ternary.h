@@ -1,0 +1,176 @@
+/*
+ * moe_ternary.h - C ABI of the MI355X (gfx950) ternary-expert MoE block.
+ *
+ * The library computes the forward pass of one mixture-of-experts block whose
+ * expert weights are ternary {-1, 0, +1} times one fp16 scale per group of 128
+ * weights, stored in one of two containers:
+ *
+ *   PQ2_0  (id 142): 34 bytes per 128 weights, 2.125 bits per weight.
+ *          Scion-35B-A3B card, "Weight Representation: ternary PQ2_0 + trained
+ *          corrections" and "About the Hub's quant chip" (2-bit codes plus one
+ *          fp16 group scale per 128; the legacy Q1_0_g128 name has the same
+ *          byte layout).
+ *          bytes 0..31: weight j in byte j/4, bits 2(j%4)..2(j%4)+1, LSB first;
+ *          code 00 = 0, 01 = +1, 11 = -1 (10 is invalid);
+ *          bytes 32..33: the scale, IEEE binary16, little-endian.
+ *
+ *   PTQ1_0 (id 143): 28 bytes per 128 weights, 1.75 bits per weight.
+ *          Scion-FlashNext-176B-A6B card, "Weight Representation: ternary
+ *          PTQ1_0 + trained corrections + Q4_0 PLE" (24 bytes of 5-trit data,
+ *          2 bytes holding the remaining trits, the 2-byte group scale) and
+ *          "Highlights" (5 trits per byte, about 10% over the 1.585 bpw entropy).
+ *          bytes 0..23: byte b holds weights 5b..5b+4 as sum_i d_i 3^i (<= 242);
+ *          bytes 24..25: byte 24+m holds weights 120+4m..123+4m as sum_i d_i 3^i
+ *          (<= 80); digit d = t mod 3 (0 -> 0, 1 -> +1, 2 -> -1);
+ *          bytes 26..27: the scale, IEEE binary16, little-endian.
+ *
+ *   The format ids are the type ids the fork gives the two containers
+ *   (35B-A3B card, "Quickstart": GGML_TYPE_PQ2_0 = 142; FlashNext card,
+ *   "About the Hub's quant chip": PTQ1_0 is type id 143).  A weight's value is
+ *   scale * t.  Groups of 128 run along the input (K) dimension of each row.
+ *
+ * The forward pass (Scion project README, "The idea" and "Serving notes";
+ * FlashNext card, "Model Overview"):
+ *   l = (W_r + dW_r) x                       router logits plus router delta
+ *   s_1..s_k = top-k of l                    ties go to the lower expert index
+ *   w_i = softmax over the k selected logits
+ *   grouping of (token, slot) pairs per expert
+ *   o(t, e) = W_down,e (silu(W_gate,e x_t) * (W_up,e x_t))   ternary SwiGLU expert
+ *   y_t = sum_i w_i o(t, s_i) + sum_shared o(t, shared) + B (A x_t)
+ * The last term is the rank-r correction branch on the MoE block output, on the
+ * residual stream (README, "What the experiments established": the placement
+ * rule; 35B-A3B card, "Weight Representation": rank-512 branches and exact
+ * router deltas).
+ *
+ * Numerics: activations x and y are bfloat16; all products accumulate in fp32 on
+ * matrix cores; the intermediate h = silu(g) * u and z = A x are rounded to
+ * bfloat16; router, router delta, A and B (fp16) enter the matrix cores as an
+ * exact two-term bfloat16 split (the router and its delta are first summed in
+ * fp32).  Gate weights use fp32 exp.
+ *
+ * Ownership and ordering: the caller allocates and frees every buffer.  The
+ * library allocates no device memory, keeps no pointer after a call returns and
+ * holds no state except a thread-local error message.  Device entry points are
+ * ordered on the given stream (a hipStream_t; NULL means the null stream) and
+ * return once the work is enqueued: inputs must stay alive and unchanged until
+ * the stream reaches the call, and concurrent streams need separate workspaces.
+ *
+ * Errors: every argument, shape and format check happens on the host before the
+ * first launch, so a call that returns an error has enqueued nothing.  A failed
+ * launch returns MOE_E_DEVICE.  No C++ exception crosses this interface.
+ */
+#ifndef MOE_TERNARY_H
+#define MOE_TERNARY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { MOE_PQ2_0 = 142, MOE_PTQ1_0 = 143 };
+
+enum {
+  MOE_OK = 0,
+  MOE_E_ARG = -1,        /* NULL pointer or out-of-range scalar argument       */
+  MOE_E_FORMAT = -2,     /* unknown container id                                 */
+  MOE_E_SHAPE = -3,      /* a dimension is not a multiple of 128, or k > E       */
+  MOE_E_CODE = -4,       /* invalid code byte (2-bit 10, base-3 byte too large)  */
+  MOE_E_NONFINITE = -5,  /* NaN or Inf group scale                                */
+  MOE_E_SPACE = -6,      /* destination or workspace too small                    */
+  MOE_E_DEVICE = -7      /* a HIP launch or runtime call failed                   */
+};
+
+/* Bytes per 128-weight group: 34 (PQ2_0), 28 (PTQ1_0), -1 for an unknown id. */
+int64_t moe_block_bytes(int32_t fmt);
+
+/* Container bytes for n_weights weights; -1 if fmt is unknown or n_weights is
+ * negative or not a multiple of 128. */
+int64_t moe_packed_bytes(int32_t fmt, int64_t n_weights);
+
+/* Host: pack n_weights trits (int8 in {-1,0,+1}) and n_weights/128 fp16 scale
+ * bit patterns into dst (dst_bytes >= moe_packed_bytes).  Errors: MOE_E_FORMAT,
+ * MOE_E_SHAPE (n % 128), MOE_E_ARG (NULL, trit outside {-1,0,1}),
+ * MOE_E_NONFINITE (NaN/Inf scale), MOE_E_SPACE. */
+int32_t moe_pack(int32_t fmt, const int8_t* trits, const uint16_t* scales_f16,
+                 int64_t n_weights, uint8_t* dst, int64_t dst_bytes);
+
+/* Host: validate and unpack a container into trits and scale bits.  An invalid
+ * code byte returns MOE_E_CODE and the message names the group and byte. */
+int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* trits,
+                   uint16_t* scales_f16, int64_t n_weights);
+
+/* Device: decode a container already in device memory (d_src) into device
+ * trits (int8, n_weights) and scale bits (uint16, n_weights/128) with the same
+ * in-register decoders the expert kernels use.  No code validation: the
+ * container must come from moe_pack or have passed moe_unpack. */
+int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n_weights, int8_t* d_trits,
+                          uint16_t* d_scales, void* stream);
+
+/* One layer's expert banks: E routed experts, then S always-on shared experts
+ * (FlashNext card, "Model Overview": top-10 routed + 1 shared).  Bank e starts
+ * at byte offsets[e] of `banks` and holds three containers back to back:
+ * gate [d_ff x d_model], up [d_ff x d_model], down [d_model x d_ff], row-major,
+ * groups of 128 along each row, all in format formats[e].  Offsets must be
+ * multiples of 4 and every bank must lie inside banks_bytes. */
+typedef struct moe_expert_banks {
+  int32_t d_model;              /* d: multiple of 128                              */
+  int32_t d_ff;                 /* f: multiple of 128                              */
+  int32_t n_experts;            /* E >= 1 routed experts                           */
+  int32_t n_shared;             /* S >= 0 shared experts (weight 1, no gate)       */
+  const uint8_t* banks;         /* device: all containers                          */
+  int64_t banks_bytes;          /* size of `banks` in bytes (bounds check)         */
+  const int64_t* offsets;       /* device int64[E+S]                               */
+  const uint8_t* formats;       /* device uint8[E+S]: 142 or 143                   */
+  const int64_t* offsets_host;  /* host copy of offsets (validation)               */
+  const uint8_t* formats_host;  /* host copy of formats (validation, dispatch)     */
+} moe_expert_banks;
+
+/* Workspace bytes moe_ternary_forward needs for n_tokens tokens. */
+int64_t moe_workspace_bytes(const moe_expert_banks* banks, int64_t n_tokens, int32_t top_k,
+                            int32_t corr_rank);
+
+/* The block's forward pass.
+ *   x            device bf16 [n_tokens x d_model] (bit patterns), row-major
+ *   router       device fp16 [E x d_model]
+ *   router_delta device fp16 [E x d_model], or NULL for a zero delta
+ *   corr_A       device fp16 [corr_rank x d_model], corr_B fp16 [d_model x corr_rank];
+ *                both NULL with corr_rank = 0 for the uncorrected block
+ *   top_k        1 <= top_k <= E
+ *   y            device bf16 [n_tokens x d_model]; must not alias x
+ *   workspace    device, >= moe_workspace_bytes(...) bytes, 256-byte aligned
+ * n_tokens = 0 is a no-op.  The banks must come from moe_pack (codes are not
+ * re-validated on the device). */
+int32_t moe_ternary_forward(const uint16_t* x, int64_t n_tokens, const uint16_t* router,
+                            const uint16_t* router_delta, const moe_expert_banks* banks,
+                            const uint16_t* corr_A, const uint16_t* corr_B, int32_t corr_rank,
+                            int32_t top_k, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes moe_route needs. */
+int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts,
+                                  int32_t top_k);
+
+/* The routing half of the forward pass, with every intermediate exported
+ * (device buffers):
+ *   logits  fp32 [n_tokens x E]       the same fp32 logits the forward pass uses
+ *   topk_idx int32 [n_tokens x k]     selected experts in rank order
+ *   topk_w  fp32 [n_tokens x k]       softmax over the selected logits
+ *   counts  int32 [E]                 slots per expert
+ *   offsets int32 [E+1]               exclusive scan of counts
+ *   perm    int32 [n_tokens * k]      flat slot ids t*k+i ordered by (expert, token)
+ * Runs the same kernels as moe_ternary_forward on the same inputs. */
+int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t n_experts,
+                  const uint16_t* router, const uint16_t* router_delta, int32_t top_k,
+                  float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                  int32_t* offsets, int32_t* perm, void* workspace, int64_t workspace_bytes,
+                  void* stream);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_TERNARY_H */

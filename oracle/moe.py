@@ -68,6 +68,39 @@ class Banks:
         return tuple(out)
 
 
+class LazyBanks(Banks):
+    """Banks whose containers are packed with the oracle codec on first use.
+    source(e) returns ([gate, up, down] trits, [gate, up, down] scale bits)."""
+
+    def __init__(self, source, formats, d_model, d_ff, n_experts, n_shared, cache=16):
+        self.source = source
+        self.formats = np.asarray(formats, dtype=np.uint8)
+        self.d_model, self.d_ff = d_model, d_ff
+        self.n_experts, self.n_shared = n_experts, n_shared
+        self._cache = {}
+        self._cache_size = cache
+
+    def container(self, e: int) -> np.ndarray:
+        """Bank e's [gate | up | down] container bytes, packed by the oracle codec."""
+        trits, scales = self.source(e)
+        return np.concatenate([codec.pack(int(self.formats[e]), t, s) for t, s in zip(trits, scales)])
+
+    def matrices(self, e: int):
+        if e not in self._cache:
+            if len(self._cache) >= self._cache_size:
+                self._cache.pop(next(iter(self._cache)))
+            fmt = int(self.formats[e])
+            data = self.container(e)
+            d, f = self.d_model, self.d_ff
+            out, pos = [], 0
+            for rows, cols in ((f, d), (f, d), (d, f)):
+                nbytes = codec.packed_bytes(fmt, rows * cols)
+                out.append(codec.decode(fmt, data[pos:pos + nbytes], rows * cols).reshape(rows, cols))
+                pos += nbytes
+            self._cache[e] = tuple(out)
+        return self._cache[e]
+
+
 def pack_banks(trits_scales, formats, d_model, d_ff, n_experts, n_shared) -> Banks:
     """Build a Banks from per-bank ([gate, up, down] trits, [gate, up, down] scale bits)."""
     chunks, offsets, pos = [], [], 0

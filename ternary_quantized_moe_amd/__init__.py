@@ -1,0 +1,13 @@
+"""MI355X-native forward pass of a ternary-expert (PQ2_0 / PTQ1_0) MoE block.
+
+The compute path is the HIP library libmoe_ternary.so (C ABI in
+include/moe_ternary.h); this package is its thin Python binding.
+"""
+from .binding import (EXPORTS, PQ2_0, PTQ1_0, ExpertBanks, MoeError, alloc_workspace, block_bytes,
+                      forward, lib, pack, packed_bytes, route, unpack, unpack_device,
+                      workspace_bytes)
+from .layers import build_banks, pack_expert
+
+__all__ = ["EXPORTS", "PQ2_0", "PTQ1_0", "ExpertBanks", "MoeError", "alloc_workspace", "block_bytes",
+           "forward", "lib", "pack", "packed_bytes", "route", "unpack", "unpack_device",
+           "workspace_bytes", "build_banks", "pack_expert"]

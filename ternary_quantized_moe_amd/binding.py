@@ -1,0 +1,244 @@
+"""ctypes binding of libmoe_ternary.so (argument marshalling only).
+
+Every step of the block runs in the library's HIP kernels; this module only
+turns numpy arrays and torch device tensors into the pointers and sizes the C
+ABI takes (include/moe_ternary.h), and raises MoeError on a non-zero status.
+PyTorch provides device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+PQ2_0 = 142
+PTQ1_0 = 143
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ternary.so")
+
+_ERRORS = {
+    -1: "MOE_E_ARG", -2: "MOE_E_FORMAT", -3: "MOE_E_SHAPE", -4: "MOE_E_CODE",
+    -5: "MOE_E_NONFINITE", -6: "MOE_E_SPACE", -7: "MOE_E_DEVICE",
+}
+
+EXPORTS = [
+    "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
+    "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
+    "moe_last_error",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{_ERRORS.get(code, code)}: {message}")
+        self.code = code
+        self.name = _ERRORS.get(code, str(code))
+
+
+class ExpertBanksC(ctypes.Structure):
+    _fields_ = [
+        ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+        ("n_experts", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+        ("banks", ctypes.c_void_p), ("banks_bytes", ctypes.c_int64),
+        ("offsets", ctypes.c_void_p), ("formats", ctypes.c_void_p),
+        ("offsets_host", ctypes.c_void_p), ("formats_host", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library; fails loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: run `python -m ternary_quantized_moe_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+        sig = {
+            "moe_block_bytes": (i64, [i32]),
+            "moe_packed_bytes": (i64, [i32, i64]),
+            "moe_pack": (i32, [i32, vp, vp, i64, vp, i64]),
+            "moe_unpack": (i32, [i32, vp, i64, vp, vp, i64]),
+            "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
+            "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
+            "moe_ternary_forward": (i32, [vp, i64, vp, vp, ctypes.POINTER(ExpertBanksC), vp, vp, i32,
+                                          i32, vp, vp, i64, vp]),
+            "moe_route_workspace_bytes": (i64, [i64, i32, i32, i32]),
+            "moe_route": (i32, [vp, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise MoeError(rc, lib().moe_last_error().decode())
+
+
+def _np_ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _dev_ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ------------------------------------------------------------------ host codec
+def block_bytes(fmt: int) -> int:
+    return lib().moe_block_bytes(fmt)
+
+
+def packed_bytes(fmt: int, n_weights: int) -> int:
+    return lib().moe_packed_bytes(fmt, n_weights)
+
+
+def pack(fmt: int, trits: np.ndarray, scale_bits: np.ndarray) -> np.ndarray:
+    trits = np.ascontiguousarray(trits, dtype=np.int8).reshape(-1)
+    scale_bits = np.ascontiguousarray(scale_bits, dtype=np.uint16).reshape(-1)
+    n = trits.size
+    nbytes = lib().moe_packed_bytes(fmt, n)
+    if nbytes < 0:
+        # let the library produce the error message
+        _check(lib().moe_pack(fmt, _np_ptr(trits), _np_ptr(scale_bits), n, None, 0))
+    if scale_bits.size != n // 128:
+        raise MoeError(-1, f"need {n // 128} scales, got {scale_bits.size}")
+    out = np.empty(nbytes, dtype=np.uint8)
+    _check(lib().moe_pack(fmt, _np_ptr(trits), _np_ptr(scale_bits), n, _np_ptr(out), nbytes))
+    return out
+
+
+def unpack(fmt: int, data: np.ndarray, n_weights: int):
+    data = np.ascontiguousarray(data, dtype=np.uint8).reshape(-1)
+    trits = np.empty(n_weights, dtype=np.int8)
+    scales = np.empty(max(n_weights // 128, 1), dtype=np.uint16)
+    _check(lib().moe_unpack(fmt, _np_ptr(data), data.size, _np_ptr(trits), _np_ptr(scales), n_weights))
+    return trits, scales[: n_weights // 128]
+
+
+# ------------------------------------------------------------------ device
+def unpack_device(fmt: int, d_src, n_weights: int, stream=None):
+    import torch
+    trits = torch.empty(n_weights, dtype=torch.int8, device=d_src.device)
+    scales = torch.empty(max(n_weights // 128, 1), dtype=torch.int16, device=d_src.device)
+    _check(lib().moe_unpack_device(fmt, _dev_ptr(d_src), n_weights, _dev_ptr(trits), _dev_ptr(scales),
+                                   _stream(stream)))
+    return trits, scales[: n_weights // 128]
+
+
+class ExpertBanks:
+    """One layer's expert containers in device memory plus the host copies the
+    library validates against.  `data` is the concatenation of every bank's
+    [gate | up | down] containers; bank e starts at offsets[e]."""
+
+    def __init__(self, data: np.ndarray, offsets: np.ndarray, formats: np.ndarray, d_model: int,
+                 d_ff: int, n_experts: int, n_shared: int, device="cuda"):
+        import torch
+        self.d_model, self.d_ff, self.n_experts, self.n_shared = d_model, d_ff, n_experts, n_shared
+        self.offsets_host = np.ascontiguousarray(offsets, dtype=np.int64)
+        self.formats_host = np.ascontiguousarray(formats, dtype=np.uint8)
+        self.data = torch.from_numpy(np.ascontiguousarray(data, dtype=np.uint8)).to(device)
+        self.offsets = torch.from_numpy(self.offsets_host).to(device)
+        self.formats = torch.from_numpy(self.formats_host).to(device)
+        self.nbytes = int(data.size)
+        self._c = ExpertBanksC(d_model, d_ff, n_experts, n_shared, self.data.data_ptr(), self.nbytes,
+                               self.offsets.data_ptr(), self.formats.data_ptr(),
+                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data)
+
+    @classmethod
+    def from_tensors(cls, data_dev, offsets_host, formats_host, d_model, d_ff, n_experts, n_shared):
+        """Wrap a device byte tensor that already holds the containers."""
+        import torch
+        self = cls.__new__(cls)
+        self.d_model, self.d_ff, self.n_experts, self.n_shared = d_model, d_ff, n_experts, n_shared
+        self.offsets_host = np.ascontiguousarray(offsets_host, dtype=np.int64)
+        self.formats_host = np.ascontiguousarray(formats_host, dtype=np.uint8)
+        self.data = data_dev
+        self.offsets = torch.from_numpy(self.offsets_host).to(data_dev.device)
+        self.formats = torch.from_numpy(self.formats_host).to(data_dev.device)
+        self.nbytes = int(data_dev.numel())
+        self._c = ExpertBanksC(d_model, d_ff, n_experts, n_shared, data_dev.data_ptr(), self.nbytes,
+                               self.offsets.data_ptr(), self.formats.data_ptr(),
+                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data)
+        return self
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def workspace_bytes(banks: ExpertBanks, n_tokens: int, top_k: int, corr_rank: int) -> int:
+    return lib().moe_workspace_bytes(banks.c, n_tokens, top_k, corr_rank)
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 256) + 256, dtype=torch.uint8, device=device)
+
+
+def _aligned(ws):
+    p = ws.data_ptr()
+    off = (-p) % 256
+    return p + off, ws.numel() - off
+
+
+def forward(x, router, router_delta, banks: ExpertBanks, corr_a, corr_b, top_k: int, y=None,
+            workspace=None, stream=None):
+    """x: bf16 [T, d] (torch.bfloat16 or int16 bits) on the GPU; returns y (same dtype as x)."""
+    import torch
+    T = x.shape[0]
+    r = 0 if corr_a is None else corr_a.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    need = workspace_bytes(banks, T, top_k, r)
+    if need < 0:
+        raise MoeError(-1, "invalid arguments for the workspace size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_ternary_forward(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta), banks.c,
+                                     _dev_ptr(corr_a), _dev_ptr(corr_b), r, top_k, _dev_ptr(y), wp, wn,
+                                     _stream(stream)))
+    return y
+
+
+def route(x, router, router_delta, n_experts: int, top_k: int, workspace=None, stream=None):
+    """Routing half of the block; returns dict of device tensors
+    (logits, idx, w, counts, offsets, perm)."""
+    import torch
+    T, d = x.shape
+    dev = x.device
+    out = dict(
+        logits=torch.empty((T, n_experts), dtype=torch.float32, device=dev),
+        idx=torch.empty((T, top_k), dtype=torch.int32, device=dev),
+        w=torch.empty((T, top_k), dtype=torch.float32, device=dev),
+        counts=torch.empty(n_experts, dtype=torch.int32, device=dev),
+        offsets=torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+        perm=torch.empty(max(T * top_k, 1), dtype=torch.int32, device=dev),
+    )
+    need = lib().moe_route_workspace_bytes(T, d, n_experts, top_k)
+    if need < 0:
+        raise MoeError(-1, "invalid arguments for the routing workspace size")
+    if workspace is None:
+        workspace = alloc_workspace(need, dev)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_route(_dev_ptr(x), T, d, n_experts, _dev_ptr(router), _dev_ptr(router_delta), top_k,
+                           _dev_ptr(out["logits"]), _dev_ptr(out["idx"]), _dev_ptr(out["w"]),
+                           _dev_ptr(out["counts"]), _dev_ptr(out["offsets"]), _dev_ptr(out["perm"]),
+                           wp, wn, _stream(stream)))
+    out["perm"] = out["perm"][: T * top_k]
+    return out

@@ -1,0 +1,203 @@
+// Device helpers shared by the kernels: matrix-core wrappers, bf16 rounding and
+// the in-register container decoders.
+//
+// Both decoders turn one lane's quarter of a 128-weight group into matrix-core
+// B operands for v_mfma_f32_16x16x32_bf16.  A weight t in {-1, 0, +1} becomes
+// the bfloat16 value 2t, whose bit pattern is the 2-bit two's-complement code
+// shifted to bits 14..15 (00 -> 0x0000, 01 -> 0x4000 = +2, 11 -> 0xC000 = -2);
+// the factor 2 is folded into the group scale.  Inside a group the order of the
+// K dimension is free as long as the activation operand uses the same order, so
+// each decoder fixes the order that is cheapest to produce (kslot_* below) and
+// the activation loaders follow it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef uint32_t __attribute__((aligned(2))) u32_a2;
+typedef u32x2 __attribute__((aligned(2))) u32x2_a2;
+typedef u32x2 __attribute__((aligned(4))) u32x2_a4;
+typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
+
+constexpr int kPQ2 = 142;
+constexpr int kPTQ1 = 143;
+constexpr int kLutCopies = 16;   // PTQ1_0 byte table copies (one per LDS bank pair)
+
+// D = A(16x32) * B(32x16) + C, fp32 accumulate.  Lane l supplies row l%16 of A
+// and column l%16 of B for its k-slot quarter; D lane l holds column l%16, rows
+// 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// ---------------------------------------------------------------- PQ2_0
+// Lane quarter q of a group covers weights 32q .. 32q+31: code dwords w0, w1 at
+// block bytes 8q .. 8q+7.  MFMA m takes code word m>>1 and the four pairs
+// jj = 4(m&1) .. 4(m&1)+3, each pair being weights (jj, jj+8) of that word.
+//   k-slot (m, q, j) -> weight 32q + 16(m>>1) + 4(m&1) + (j>>1) + 8(j&1)
+__device__ __forceinline__ int kslot_pq2(int m, int q, int j) {
+  return 32 * q + 16 * (m >> 1) + 4 * (m & 1) + (j >> 1) + 8 * (j & 1);
+}
+
+__device__ __forceinline__ void decode_pq2(uint32_t w0, uint32_t w1, u32x4 out[4]) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t w = (m >> 1) ? w1 : w0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jj = 4 * (m & 1) + i;
+      out[m][i] = (w << (14 - 2 * jj)) & 0xC000C000u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- PTQ1_0
+// Byte table: entry v (0..242) holds the five digits of v as bytes c<<6 with
+// c the 2-bit code of the digit's trit (0 -> 0x00, 1 -> 0x40, 2 -> 0xC0):
+// lo = digits 0..3, hi = digit 4.  A tail byte (< 81) reads the same table.
+// Lane quarter q covers data bytes 6q .. 6q+5 (weights 30q .. 30q+29) and the
+// tail digits 2(q&1), 2(q&1)+1 of tail byte 24 + (q>>1) (weights 120+2q, 121+2q).
+// Pairs P = 0..15 (MFMA m = P/4) are consecutive weights:
+//   k-slot (m, q, j) -> weight 30q + 8m + j for 8m + j < 30, else 120 + 2q + (j&1)
+__device__ __forceinline__ int kslot_ptq1(int m, int q, int j) {
+  const int r = 8 * m + j;
+  return r < 30 ? 30 * q + r : 120 + 2 * q + (j & 1);
+}
+
+__device__ __forceinline__ u32x2 ptq1_lut_entry(int v) {
+  uint32_t b[5];
+  int r = v;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int d = r % 3;
+    r /= 3;
+    b[i] = d == 0 ? 0u : (d == 1 ? 0x40u : 0xC0u);
+  }
+  u32x2 e;
+  e.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  e.y = b[4];
+  return e;
+}
+
+// Fill the LDS byte table (all threads of the block take part; caller syncs).
+__device__ __forceinline__ void ptq1_lut_fill(u32x2* lut, int tid, int nthreads) {
+  for (int idx = tid; idx < 256 * kLutCopies; idx += nthreads) lut[idx] = ptq1_lut_entry(idx / kLutCopies);
+}
+
+__device__ __forceinline__ u32x2 lut_get(const u32x2* lut, uint32_t v, int copy) {
+  return lut[v * kLutCopies + copy];
+}
+
+// sel for perm_b32 building a bf16 pair from two table bytes: byte `a` of
+// {s0:s1} to bits 8..15 and byte `b` to bits 24..31, low bytes zero.
+__host__ __device__ constexpr uint32_t pair_sel(uint32_t a, uint32_t b) {
+  return 0x0Cu | (a << 8) | (0x0Cu << 16) | (b << 24);
+}
+
+// d0, d1: block bytes 6q .. 6q+7; tail: block bytes 24 .. 27.
+__device__ __forceinline__ void decode_ptq1(const u32x2* lut, int copy, uint32_t d0, uint32_t d1,
+                                            uint32_t tail, int q, u32x4 out[4]) {
+  u32x2 L[6];
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint32_t src = b < 4 ? d0 : d1;
+    L[b] = lut_get(lut, (src >> (8 * (b & 3))) & 0xFFu, copy);
+  }
+  const u32x2 Lt = lut_get(lut, (tail >> (8 * (q >> 1))) & 0xFFu, copy);
+  uint32_t P[16];
+#pragma unroll
+  for (int bp = 0; bp < 3; ++bp) {
+    const u32x2 A = L[2 * bp], B = L[2 * bp + 1];
+    P[5 * bp + 0] = perm_b32(0u, A.x, pair_sel(0, 1));
+    P[5 * bp + 1] = perm_b32(0u, A.x, pair_sel(2, 3));
+    P[5 * bp + 2] = perm_b32(B.x, A.y, pair_sel(0, 4));
+    P[5 * bp + 3] = perm_b32(0u, B.x, pair_sel(1, 2));
+    P[5 * bp + 4] = perm_b32(B.y, B.x, pair_sel(3, 4));
+  }
+  const uint32_t ts = (q & 1) ? pair_sel(2, 3) : pair_sel(0, 1);
+  P[15] = perm_b32(0u, Lt.x, ts);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) out[m] = u32x4{P[4 * m], P[4 * m + 1], P[4 * m + 2], P[4 * m + 3]};
+}
+
+// Load one lane's quarter of a block and decode it; returns the group scale
+// (already multiplied by 0.5 to undo the +-2 encoding).
+template <int FMT>
+__device__ __forceinline__ float load_decode_block(const uint8_t* blk, const u32x2* lut, int copy,
+                                                   int q, u32x4 out[4]) {
+  if (FMT == kPQ2) {
+    const u32x2 w = *(const u32x2_a2*)(blk + 8 * q);
+    const uint32_t s = *(const uint16_t*)(blk + 32);
+    decode_pq2(w.x, w.y, out);
+    return 0.5f * f16_to_f32(s);
+  } else {
+    const u32x2 w = *(const u32x2_a2*)(blk + 6 * q);
+    const uint32_t t = *(const uint32_t*)(blk + 24);
+    decode_ptq1(lut, copy, w.x, w.y, t, q, out);
+    return 0.5f * f16_to_f32(t >> 16);
+  }
+}
+
+template <int FMT>
+__host__ __device__ constexpr int block_bytes_c() {
+  return FMT == kPQ2 ? 34 : 28;
+}
+
+// ---------------------------------------------------------------- activations
+// Matrix-core A operands (bf16) for one row of activations and one group, in the
+// k-slot order of the container format.  `row` points at the row start.
+__device__ __forceinline__ void load_act_pq2(const uint16_t* row, int g, int q, u32x4 out[4]) {
+  const u32x4* p = (const u32x4*)(row + g * 128 + 32 * q);
+  u32x4 X[4] = {p[0], p[1], p[2], p[3]};
+  uint32_t x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[4 * i + 0] = X[i].x;
+    x[4 * i + 1] = X[i].y;
+    x[4 * i + 2] = X[i].z;
+    x[4 * i + 3] = X[i].w;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d1 = 8 * (m >> 1) + 2 * (m & 1) + (i >> 1);
+      out[m][i] = perm_b32(x[d1 + 4], x[d1], (i & 1) ? 0x07060302u : 0x05040100u);
+    }
+  }
+}
+
+__device__ __forceinline__ void load_act_ptq1(const uint16_t* row, int g, int q, u32x4 out[4]) {
+  const uint32_t* p = (const uint32_t*)(row + g * 128 + 30 * q);
+  uint32_t x[16];
+#pragma unroll
+  for (int i = 0; i < 15; ++i) x[i] = p[i];
+  x[15] = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) out[m] = u32x4{x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
+}
+
+}  // namespace moe

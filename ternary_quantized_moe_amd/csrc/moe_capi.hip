@@ -1,0 +1,409 @@
+// Host side of the C ABI: the container codec, argument validation, workspace
+// carving and the launch sequence of one forward pass.  Container layouts:
+// Scion-35B-A3B card, "Weight Representation" (PQ2_0) and Scion-FlashNext card,
+// "Weight Representation" (PTQ1_0); see include/moe_ternary.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe_ternary.h"
+#include "moe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int32_t ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+bool known_fmt(int32_t fmt) { return fmt == MOE_PQ2_0 || fmt == MOE_PTQ1_0; }
+
+int32_t bad_fmt(int32_t fmt) {
+  return fail(MOE_E_FORMAT, "unknown container id %d; valid ids are 142 (PQ2_0) and 143 (PTQ1_0)",
+              (int)fmt);
+}
+
+bool finite_f16(uint16_t h) { return (h & 0x7C00u) != 0x7C00u; }
+
+int32_t device_fail(hipError_t e, const char* what) {
+  return fail(MOE_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+// --------------------------------------------------------------- workspace plan
+constexpr int64_t kAlign = 256;
+int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t T, Tk, n_pos, nb, max_items;
+  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, h, slots;
+  int64_t route_end, total;
+};
+
+Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
+  Plan p{};
+  p.T = T;
+  p.Tk = T * k;
+  p.n_pos = p.Tk + (int64_t)S * T;
+  p.nb = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
+  p.max_items = p.Tk / moe::kChunk + std::min<int64_t>(E, p.Tk) +
+                (int64_t)S * ((T + moe::kChunk - 1) / moe::kChunk);
+  int64_t o = 0;
+  p.logits = o; o += up(T * E * 4);
+  p.idx = o; o += up(p.Tk * 4);
+  p.w = o; o += up(p.Tk * 4);
+  p.rank = o; o += up(p.Tk * 4);
+  p.bcnt = o; o += up(p.nb * E * 4);
+  p.bbase = o; o += up(p.nb * E * 4);
+  p.counts = o; o += up((int64_t)E * 4);
+  p.offsets = o; o += up((int64_t)(E + 1) * 4);
+  p.perm = o; o += up(p.Tk * 4);
+  p.items = o; o += up(std::max<int64_t>(p.max_items, 1) * (int64_t)sizeof(moe::Item));
+  p.nitems = o; o += up(4);
+  p.route_end = o;
+  p.z = o; o += up(T * (int64_t)r * 2);
+  p.h = o; o += up(p.n_pos * f * 2);
+  p.slots = o; o += up(p.n_pos * d * 2);
+  p.total = o;
+  return p;
+}
+
+template <class T>
+T* at(void* ws, int64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int32_t check_dims(int64_t T, int d, int E, int k) {
+  if (T < 0) return fail(MOE_E_ARG, "n_tokens must be >= 0 (got %lld)", (long long)T);
+  if (d <= 0 || d % 128) return fail(MOE_E_SHAPE, "d_model must be a positive multiple of 128 (got %d)", d);
+  if (d > 8192) return fail(MOE_E_SHAPE, "d_model above 8192 is not supported (got %d)", d);
+  if (E < 1 || E > moe::kMaxExperts)
+    return fail(MOE_E_SHAPE, "n_experts must be in [1, %d] (got %d)", moe::kMaxExperts, E);
+  if (k < 1 || k > E) return fail(MOE_E_SHAPE, "top_k must be in [1, n_experts=%d] (got %d)", E, k);
+  if (T * (int64_t)k > (int64_t)1 << 30)
+    return fail(MOE_E_SHAPE, "n_tokens * top_k above 2^30 is not supported");
+  return MOE_OK;
+}
+
+int32_t check_banks(const moe_expert_banks* b) {
+  if (!b) return fail(MOE_E_ARG, "expert_banks is NULL");
+  if (b->d_model <= 0 || b->d_model % 128)
+    return fail(MOE_E_SHAPE, "d_model must be a positive multiple of 128 (got %d)", b->d_model);
+  if (b->d_ff <= 0 || b->d_ff % 128)
+    return fail(MOE_E_SHAPE, "d_ff must be a positive multiple of 128 (got %d)", b->d_ff);
+  if (b->d_ff > 8192) return fail(MOE_E_SHAPE, "d_ff above 8192 is not supported (got %d)", b->d_ff);
+  if (b->n_shared < 0 || b->n_shared > 8)
+    return fail(MOE_E_SHAPE, "n_shared must be in [0, 8] (got %d)", b->n_shared);
+  if (b->n_experts < 1 || b->n_experts > moe::kMaxExperts)
+    return fail(MOE_E_SHAPE, "n_experts must be in [1, %d] (got %d)", moe::kMaxExperts, b->n_experts);
+  if (!b->banks || !b->offsets || !b->formats || !b->formats_host || !b->offsets_host)
+    return fail(MOE_E_ARG, "expert_banks has a NULL pointer");
+  const int nb = b->n_experts + b->n_shared;
+  const int64_t nblocks = 3 * (int64_t)b->d_ff * b->d_model / 128;
+  for (int e = 0; e < nb; ++e) {
+    const int fmt = b->formats_host[e];
+    if (!known_fmt(fmt))
+      return fail(MOE_E_FORMAT, "bank %d: unknown container id %d; valid ids are 142 (PQ2_0) and 143 (PTQ1_0)",
+                  e, fmt);
+    const int64_t off = b->offsets_host[e];
+    const int64_t bytes = nblocks * moe_block_bytes(fmt);
+    if (off < 0 || off % 4) return fail(MOE_E_ARG, "bank %d: offset %lld is not a non-negative multiple of 4", e, (long long)off);
+    if (off + bytes > b->banks_bytes)
+      return fail(MOE_E_SPACE, "bank %d: bytes [%lld, %lld) exceed banks_bytes %lld", e, (long long)off,
+                  (long long)(off + bytes), (long long)b->banks_bytes);
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+int64_t moe_block_bytes(int32_t fmt) {
+  if (fmt == MOE_PQ2_0) return 34;
+  if (fmt == MOE_PTQ1_0) return 28;
+  return -1;
+}
+
+int64_t moe_packed_bytes(int32_t fmt, int64_t n) {
+  if (!known_fmt(fmt) || n < 0 || n % 128) return -1;
+  return n / 128 * moe_block_bytes(fmt);
+}
+
+int32_t moe_pack(int32_t fmt, const int8_t* trits, const uint16_t* scales, int64_t n, uint8_t* dst,
+                 int64_t dst_bytes) {
+  try {
+    if (!known_fmt(fmt)) return bad_fmt(fmt);
+    if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
+    if (n > 0 && (!trits || !scales || !dst)) return fail(MOE_E_ARG, "NULL pointer");
+    const int64_t need = moe_packed_bytes(fmt, n);
+    if (dst_bytes < need)
+      return fail(MOE_E_SPACE, "dst holds %lld bytes, %lld needed", (long long)dst_bytes, (long long)need);
+    const int64_t nb = n / 128;
+    for (int64_t b = 0; b < nb; ++b)
+      if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
+    for (int64_t i = 0; i < n; ++i)
+      if (trits[i] < -1 || trits[i] > 1)
+        return fail(MOE_E_ARG, "weight %lld is %d, not in {-1, 0, +1}", (long long)i, (int)trits[i]);
+    if (fmt == MOE_PQ2_0) {
+      for (int64_t b = 0; b < nb; ++b) {
+        const int8_t* t = trits + b * 128;
+        uint8_t* o = dst + b * 34;
+        for (int j = 0; j < 32; ++j) {
+          uint32_t v = 0;
+          for (int i = 0; i < 4; ++i) v |= (uint32_t)(t[4 * j + i] & 3) << (2 * i);  // 0->00, 1->01, -1->11
+          o[j] = (uint8_t)v;
+        }
+        o[32] = (uint8_t)(scales[b] & 0xFF);
+        o[33] = (uint8_t)(scales[b] >> 8);
+      }
+    } else {
+      for (int64_t b = 0; b < nb; ++b) {
+        const int8_t* t = trits + b * 128;
+        uint8_t* o = dst + b * 28;
+        auto digit = [](int8_t v) { return v < 0 ? 2u : (uint32_t)v; };
+        for (int j = 0; j < 24; ++j) {
+          uint32_t v = 0, p = 1;
+          for (int i = 0; i < 5; ++i, p *= 3) v += digit(t[5 * j + i]) * p;
+          o[j] = (uint8_t)v;
+        }
+        for (int m = 0; m < 2; ++m) {
+          uint32_t v = 0, p = 1;
+          for (int i = 0; i < 4; ++i, p *= 3) v += digit(t[120 + 4 * m + i]) * p;
+          o[24 + m] = (uint8_t)v;
+        }
+        o[26] = (uint8_t)(scales[b] & 0xFF);
+        o[27] = (uint8_t)(scales[b] >> 8);
+      }
+    }
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_pack");
+  }
+}
+
+int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* trits, uint16_t* scales,
+                   int64_t n) {
+  try {
+    if (!known_fmt(fmt)) return bad_fmt(fmt);
+    if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
+    if (n > 0 && (!trits || !scales || !src)) return fail(MOE_E_ARG, "NULL pointer");
+    const int64_t need = moe_packed_bytes(fmt, n);
+    if (src_bytes < need)
+      return fail(MOE_E_SPACE, "container holds %lld bytes, %lld needed", (long long)src_bytes, (long long)need);
+    const int64_t nb = n / 128;
+    if (fmt == MOE_PQ2_0) {
+      for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = src + b * 34;
+        for (int j = 0; j < 32; ++j) {
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t c = (blk[j] >> (2 * i)) & 3u;
+            if (c == 2)
+              return fail(MOE_E_CODE, "invalid 2-bit code 10 in group %lld, byte %d", (long long)b, j);
+            trits[b * 128 + 4 * j + i] = c == 3 ? -1 : (int8_t)c;
+          }
+        }
+        scales[b] = (uint16_t)(blk[32] | (blk[33] << 8));
+        if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
+      }
+    } else {
+      for (int64_t b = 0; b < nb; ++b) {
+        const uint8_t* blk = src + b * 28;
+        for (int j = 0; j < 26; ++j) {
+          const int nd = j < 24 ? 5 : 4;
+          const uint32_t lim = j < 24 ? 243u : 81u;
+          if (blk[j] >= lim)
+            return fail(MOE_E_CODE, "base-3 %s byte %d > %u in group %lld, byte %d", j < 24 ? "data" : "tail",
+                        (int)blk[j], lim - 1, (long long)b, j);
+          uint32_t v = blk[j];
+          const int base = j < 24 ? 5 * j : 120 + 4 * (j - 24);
+          for (int i = 0; i < nd; ++i) {
+            const uint32_t dgt = v % 3;
+            v /= 3;
+            trits[b * 128 + base + i] = dgt == 2 ? -1 : (int8_t)dgt;
+          }
+        }
+        scales[b] = (uint16_t)(blk[26] | (blk[27] << 8));
+        if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
+      }
+    }
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_unpack");
+  }
+}
+
+int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n, int8_t* d_trits, uint16_t* d_scales,
+                          void* stream) {
+  if (!known_fmt(fmt)) return bad_fmt(fmt);
+  if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
+  if (n == 0) return ok();
+  if (!d_src || !d_trits || !d_scales) return fail(MOE_E_ARG, "NULL pointer");
+  if ((uintptr_t)d_src % 4) return fail(MOE_E_ARG, "d_src must be 4-byte aligned");
+  hipError_t e = moe::launch_unpack_device(fmt, d_src, n, d_trits, d_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "moe_unpack_device launch");
+  return ok();
+}
+
+int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k) {
+  if (n_tokens < 0 || n_experts < 1 || top_k < 1) return -1;
+  return make_plan(n_tokens, d_model, n_experts, 0, 128, top_k, 0).route_end;
+}
+
+int64_t moe_workspace_bytes(const moe_expert_banks* banks, int64_t n_tokens, int32_t top_k, int32_t corr_rank) {
+  if (!banks || n_tokens < 0 || top_k < 1 || corr_rank < 0) return -1;
+  return make_plan(n_tokens, banks->d_model, banks->n_experts, banks->n_shared, banks->d_ff, top_k, corr_rank).total;
+}
+
+static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, const uint16_t* router,
+                          const uint16_t* delta, const uint16_t* corr_A, int r, int k, const Plan& p,
+                          void* ws, hipStream_t stream, float* logits, int32_t* idx, float* w,
+                          int32_t* counts, int32_t* offsets, int32_t* perm) {
+  moe::DenseArgs da{};
+  da.act = x;
+  da.lda = d;
+  da.T = T;
+  da.K = d;
+  da.w0 = router;
+  da.w0b = delta;
+  da.N0 = E;
+  da.w1 = corr_A;
+  da.N1 = corr_A ? r : 0;
+  da.logits = logits;
+  da.z = at<uint16_t>(ws, p.z);
+  hipError_t e = moe::launch_xproj(da, stream);
+  if (e != hipSuccess) return device_fail(e, "xproj launch");
+
+  moe::RouteArgs ra{};
+  ra.logits = logits;
+  ra.T = T;
+  ra.E = E;
+  ra.k = k;
+  ra.S = S;
+  ra.idx = idx;
+  ra.w = w;
+  ra.slot_rank = at<int32_t>(ws, p.rank);
+  ra.block_cnt = at<int32_t>(ws, p.bcnt);
+  ra.block_base = at<int32_t>(ws, p.bbase);
+  ra.counts = counts;
+  ra.offsets = offsets;
+  ra.perm = perm;
+  ra.items = at<moe::Item>(ws, p.items);
+  ra.n_items = at<int32_t>(ws, p.nitems);
+  e = moe::launch_route(ra, p.max_items, stream);
+  if (e != hipSuccess) return device_fail(e, "routing launch");
+  return MOE_OK;
+}
+
+int32_t moe_route(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint16_t* router,
+                  const uint16_t* delta, int32_t k, float* logits, int32_t* idx, float* w, int32_t* counts,
+                  int32_t* offsets, int32_t* perm, void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    int32_t rc = check_dims(T, d, E, k);
+    if (rc) return rc;
+    if (T == 0) return ok();
+    if (!x || !router || !logits || !idx || !w || !counts || !offsets || !perm || !ws)
+      return fail(MOE_E_ARG, "NULL pointer");
+    if ((uintptr_t)ws % kAlign || (uintptr_t)x % 16) return fail(MOE_E_ARG, "workspace must be 256-byte and x 16-byte aligned");
+    const Plan p = make_plan(T, d, E, 0, 128, k, 0);
+    if (ws_bytes < p.route_end)
+      return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.route_end);
+    rc = route_impl(x, T, d, E, 0, router, delta, nullptr, 0, k, p, ws, (hipStream_t)stream, logits, idx, w,
+                    counts, offsets, perm);
+    if (rc) return rc;
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_route");
+  }
+}
+
+int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
+                            const moe_expert_banks* banks, const uint16_t* corr_A, const uint16_t* corr_B,
+                            int32_t r, int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    int32_t rc = check_banks(banks);
+    if (rc) return rc;
+    const int d = banks->d_model, f = banks->d_ff, E = banks->n_experts, S = banks->n_shared;
+    rc = check_dims(T, d, E, k);
+    if (rc) return rc;
+    if (r < 0) return fail(MOE_E_ARG, "corr_rank must be >= 0 (got %d)", r);
+    if ((corr_A == nullptr) != (corr_B == nullptr))
+      return fail(MOE_E_ARG, "corr_A and corr_B must both be given or both be NULL");
+    if (corr_A && r == 0) return fail(MOE_E_ARG, "corr_rank is 0 but corr_A/corr_B are given");
+    if (!corr_A) r = 0;
+    if (r % 8) return fail(MOE_E_SHAPE, "corr_rank must be a multiple of 8 (got %d)", r);
+    if (r > 4096) return fail(MOE_E_SHAPE, "corr_rank above 4096 is not supported (got %d)", r);
+    if (T == 0) return ok();
+    if (!x || !router || !y || !ws) return fail(MOE_E_ARG, "NULL pointer");
+    if (x == y) return fail(MOE_E_ARG, "y must not alias x");
+    if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 4) return fail(MOE_E_ARG, "x must be 16-byte and y 4-byte aligned");
+    const Plan p = make_plan(T, d, E, S, f, k, r);
+    if (ws_bytes < p.total)
+      return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
+    const hipStream_t st = (hipStream_t)stream;
+
+    rc = route_impl(x, T, d, E, S, router, delta, corr_A, r, k, p, ws, st, at<float>(ws, p.logits),
+                    at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
+                    at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm));
+    if (rc) return rc;
+
+    moe::ExpertArgs ea{};
+    ea.banks = banks->banks;
+    ea.offsets = banks->offsets;
+    ea.formats = banks->formats;
+    ea.d = d;
+    ea.f = f;
+    ea.E = E;
+    ea.S = S;
+    ea.k = k;
+    ea.T = T;
+    ea.Tk = T * k;
+    ea.items = at<moe::Item>(ws, p.items);
+    ea.n_items = at<int32_t>(ws, p.nitems);
+    ea.perm = at<int32_t>(ws, p.perm);
+    ea.topk_w = at<float>(ws, p.w);
+    ea.x = x;
+    ea.h = at<uint16_t>(ws, p.h);
+    ea.slots = at<uint16_t>(ws, p.slots);
+    hipError_t e = moe::launch_experts(ea, p.max_items, st);
+    if (e != hipSuccess) return device_fail(e, "expert launch");
+
+    moe::DenseArgs ca{};
+    ca.act = at<uint16_t>(ws, p.z);
+    ca.lda = r;
+    ca.T = T;
+    ca.K = r;
+    ca.w0 = corr_B;
+    ca.N0 = d;
+    ca.slots = at<uint16_t>(ws, p.slots);
+    ca.top_k = k;
+    ca.n_shared = S;
+    ca.y = y;
+    e = moe::launch_combine(ca, st);
+    if (e != hipSuccess) return device_fail(e, "combine launch");
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_ternary_forward");
+  }
+}
+
+}  // extern "C"

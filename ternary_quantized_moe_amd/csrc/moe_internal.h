@@ -1,0 +1,84 @@
+// Internal interface between the C-ABI host layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 128;     // weights per container group
+constexpr int kChunk = 16;      // tokens per expert work item (one MFMA M tile)
+constexpr int kRouteBlock = 256;  // tokens per ranking block
+constexpr int kMaxExperts = 1024;
+
+// Work item of the grouped expert kernels: bank, first position in the
+// (expert, token)-ordered slot space, number of tokens (<= kChunk).
+struct Item {
+  int32_t bank;
+  int32_t pos;
+  int32_t n;
+  int32_t pad;
+};
+
+struct DenseArgs {
+  const uint16_t* act;  // bf16 [T x K], row stride lda (elements)
+  int64_t lda;
+  int64_t T;
+  int K;
+  // weight rows [0, N0) = w0 (+ w0b, summed in fp32), rows [N0, N0+N1) = w1; fp16, row stride K
+  const uint16_t* w0;
+  const uint16_t* w0b;
+  int N0;
+  const uint16_t* w1;
+  int N1;
+  // xproj epilogue
+  float* logits;   // fp32 [T x N0]
+  uint16_t* z;     // bf16 [T x N1]
+  // combine epilogue: y = acc + sum of the token's slots
+  const uint16_t* slots;  // bf16 [(T*k + S*T) x N0]
+  int top_k;
+  int n_shared;
+  uint16_t* y;     // bf16 [T x N0]
+};
+
+struct RouteArgs {
+  const float* logits;  // [T x E]
+  int64_t T;
+  int E;
+  int k;
+  int S;
+  int32_t* idx;         // [T x k]
+  float* w;             // [T x k]
+  int32_t* slot_rank;   // [T x k]
+  int32_t* block_cnt;   // [nb x E]
+  int32_t* block_base;  // [nb x E]
+  int32_t* counts;      // [E]
+  int32_t* offsets;     // [E+1]
+  int32_t* perm;        // [T x k]
+  Item* items;          // [max_items]
+  int32_t* n_items;     // [1]
+};
+
+struct ExpertArgs {
+  const uint8_t* banks;
+  const int64_t* offsets;
+  const uint8_t* formats;
+  int d, f, E, S, k;
+  int64_t T, Tk;
+  const Item* items;
+  const int32_t* n_items;
+  const int32_t* perm;
+  const float* topk_w;
+  const uint16_t* x;   // bf16 [T x d]
+  uint16_t* h;         // bf16 [(Tk + S*T) x f]
+  uint16_t* slots;     // bf16 [(Tk + S*T) x d]
+};
+
+hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
+                                uint16_t* scales, hipStream_t stream);
+hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream);
+hipError_t launch_combine(const DenseArgs& a, hipStream_t stream);
+hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream);
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream);
+
+}  // namespace moe

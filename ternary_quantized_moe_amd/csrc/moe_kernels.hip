@@ -1,0 +1,545 @@
+// HIP kernels of the ternary-expert MoE block for gfx950 (CDNA4).
+//
+// Pipeline of one forward pass (all on one stream, no host synchronisation):
+//   xproj     router logits (W_r + dW_r) x  and  z = A x          matrix cores
+//   topk      per token: top-k with lower-index ties, softmax over the k
+//   rank      per 256-token block: rank of each slot among the block's slots of
+//             the same expert (LDS ballot masks), block histograms
+//   scan      per expert: offsets, per-block bases, expert work items
+//   scatter   perm[base + rank] = slot id        (counting sort, no atomics)
+//   experts   grouped gate/up + SwiGLU, then grouped down + gate weight
+//   combine   y = sum of the token's slots + B z                  matrix cores
+//
+// The forward pass follows the release cards (Scion project README, "The idea"
+// and "Serving notes"; FlashNext card, "Model Overview"; container layouts from
+// the 35B-A3B card "Weight Representation" and the FlashNext card "Weight
+// Representation").
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// ============================================================ container decode
+// One wave decodes 16 groups: lane l takes quarter q = l/16 of group l%16 with
+// the same decoder the expert kernels inline, then writes trits back in
+// natural order.
+template <int FMT>
+__global__ __launch_bounds__(64) void unpack_device_kernel(const uint8_t* __restrict__ src,
+                                                          int64_t n_blocks,
+                                                          int8_t* __restrict__ trits,
+                                                          uint16_t* __restrict__ scales) {
+  __shared__ u32x2 lut[FMT == kPTQ1 ? 256 * kLutCopies : 1];
+  const int lane = threadIdx.x;
+  if (FMT == kPTQ1) {
+    ptq1_lut_fill(lut, lane, 64);
+    __syncthreads();
+  }
+  const int r = lane & 15, q = lane >> 4;
+  const int64_t b = (int64_t)blockIdx.x * 16 + r;
+  if (b >= n_blocks) return;
+  const uint8_t* blk = src + b * block_bytes_c<FMT>();
+  u32x4 W[4];
+  float s = load_decode_block<FMT>(blk, lut, lane % kLutCopies, q, W);
+  (void)s;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t bits = (W[m][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+      const int8_t t = bits == 0x4000u ? 1 : (bits == 0xC000u ? -1 : 0);
+      const int wi = FMT == kPQ2 ? kslot_pq2(m, q, j) : kslot_ptq1(m, q, j);
+      trits[b * 128 + wi] = t;
+    }
+  }
+  if (q == 0) scales[b] = *(const uint16_t*)(blk + (FMT == kPQ2 ? 32 : 26));
+}
+
+hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
+                                uint16_t* scales, hipStream_t stream) {
+  const int64_t nb = n_weights / kGroup;
+  if (nb == 0) return hipSuccess;
+  dim3 grid((unsigned)((nb + 15) / 16));
+  if (fmt == kPQ2)
+    unpack_device_kernel<kPQ2><<<grid, 64, 0, stream>>>(src, nb, trits, scales);
+  else
+    unpack_device_kernel<kPTQ1><<<grid, 64, 0, stream>>>(src, nb, trits, scales);
+  return hipGetLastError();
+}
+
+// ============================================================ dense projections
+// out[t][n] = sum_k act[t][k] W[n][k] with fp16 weight rows split exactly into
+// two bfloat16 terms (hi + lo) so bf16 matrix cores give fp32-accurate products.
+// Block: KS waves splitting K; one 16-token x 16-row tile per block.
+constexpr int EPI_XPROJ = 0;
+constexpr int EPI_COMBINE = 1;
+
+// fp16 x8 (4 dwords) -> exact bf16 hi/lo operand pairs (truncated hi).
+__device__ __forceinline__ void split_f16x8(u32x4 w, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = f16_to_f32(w[i] & 0xFFFFu), b = f16_to_f32(w[i] >> 16);
+    const uint32_t ha = __float_as_uint(a) & 0xFFFF0000u, hb = __float_as_uint(b) & 0xFFFF0000u;
+    const uint32_t la = __float_as_uint(a - __uint_as_float(ha)), lb = __float_as_uint(b - __uint_as_float(hb));
+    hi[i] = perm_b32(hb, ha, 0x07060302u);
+    lo[i] = perm_b32(lb, la, 0x07060302u);
+  }
+}
+
+// fp16 x8 from two sources summed in fp32 -> bf16 hi (round to nearest even) +
+// bf16 lo (round to nearest even); |error| <= 2^-18 |a + b|.
+__device__ __forceinline__ void split_sum_f16x8(u32x4 w, u32x4 v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = f16_to_f32(w[i] & 0xFFFFu) + f16_to_f32(v[i] & 0xFFFFu);
+    const float b = f16_to_f32(w[i] >> 16) + f16_to_f32(v[i] >> 16);
+    const uint32_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+    const uint32_t la = f32_to_bf16(a - bf16_to_f32(ha)), lb = f32_to_bf16(b - bf16_to_f32(hb));
+    hi[i] = ha | (hb << 16);
+    lo[i] = la | (lb << 16);
+  }
+}
+
+template <int EPI, int KS>
+__global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
+  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const int n0 = blockIdx.x * 16;
+  const int N = a.N0 + a.N1;
+  const int64_t t = t0 + i16;
+  const int n = n0 + i16;
+
+  const int nsteps = (a.K + 31) / 32;
+  const int spw = (nsteps + KS - 1) / KS;
+  const int s_begin = wave * spw, s_end = min(nsteps, s_begin + spw);
+
+  const uint16_t* arow = t < a.T ? a.act + t * a.lda : nullptr;
+  const uint16_t* wrow = nullptr;
+  const uint16_t* wrowb = nullptr;
+  bool summed = false;
+  if (n < a.N0) {
+    wrow = a.w0 + (int64_t)n * a.K;
+    if (a.w0b) {
+      wrowb = a.w0b + (int64_t)n * a.K;
+      summed = true;
+    }
+  } else if (n < N) {
+    wrow = a.w1 + (int64_t)(n - a.N0) * a.K;
+  }
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = s_begin; s < s_end; ++s) {
+    const int kb = 32 * s + 8 * q;
+    const bool kin = kb < a.K;
+    u32x4 av = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
+    if (arow && kin) av = *(const u32x4*)(arow + kb);
+    if (wrow && kin) wv = *(const u32x4_a4*)(wrow + kb);
+    if (summed && kin) wb = *(const u32x4_a4*)(wrowb + kb);
+    u32x4 hi, lo;
+    if (summed)
+      split_sum_f16x8(wv, wb, hi, lo);
+    else
+      split_f16x8(wv, hi, lo);
+    acc = mfma16(av, hi, acc);
+    acc = mfma16(av, lo, acc);
+  }
+
+  if (KS > 1) {
+    if (wave > 0) red[wave - 1][lane] = acc;
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w) acc += red[w][lane];
+  }
+
+  // lane holds tokens t0 + 4q + j, row n0 + i16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t tt = t0 + 4 * q + j;
+    if (tt >= a.T || n >= N) continue;
+    if (EPI == EPI_XPROJ) {
+      if (n < a.N0)
+        a.logits[tt * a.N0 + n] = acc[j];
+      else
+        a.z[tt * a.N1 + (n - a.N0)] = (uint16_t)f32_to_bf16(acc[j]);
+    } else {
+      const int d = a.N0;
+      float v = acc[j];
+      const int64_t Tk = a.T * a.top_k;
+      for (int i = 0; i < a.top_k; ++i) v += bf16_to_f32(a.slots[(tt * a.top_k + i) * d + n]);
+      for (int sh = 0; sh < a.n_shared; ++sh) v += bf16_to_f32(a.slots[(Tk + sh * a.T + tt) * d + n]);
+      a.y[tt * d + n] = (uint16_t)f32_to_bf16(v);
+    }
+  }
+}
+
+hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
+  const int N = a.N0 + a.N1;
+  dim3 grid((unsigned)((N + 15) / 16), (unsigned)((a.T + 15) / 16));
+  dense_kernel<EPI_XPROJ, 8><<<grid, 512, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)((a.N0 + 15) / 16), (unsigned)((a.T + 15) / 16));
+  dense_kernel<EPI_COMBINE, 4><<<grid, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ============================================================ routing
+// One wave per token: k rounds of a wave-wide argmax over the E logits (larger
+// value first, equal values to the lower expert index; -0.0 equals +0.0), then
+// the softmax over the selected logits.
+constexpr int kMaxPerLane = kMaxExperts / 64;
+
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  __shared__ float selv[4][kMaxExperts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  const bool active = t < a.T;
+  const int E = a.E, k = a.k;
+  float v[kMaxPerLane];
+  uint32_t avail = 0;
+#pragma unroll
+  for (int c = 0; c < kMaxPerLane; ++c) {
+    const int e = lane + 64 * c;
+    v[c] = 0.f;
+    if (active && e < E) {
+      v[c] = a.logits[t * E + e];
+      avail |= 1u << c;
+    }
+  }
+  for (int i = 0; active && i < k; ++i) {
+    float bv = 0.f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int c = 0; c < kMaxPerLane; ++c) {
+      if (!((avail >> c) & 1u)) continue;
+      if (be == 0x7fffffff || v[c] > bv) {  // e grows with c, so ties keep the lower e
+        bv = v[c];
+        be = lane + 64 * c;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const bool take = (oe != 0x7fffffff) &&
+                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (take) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    if (lane == 0) {
+      a.idx[t * k + i] = be;
+      selv[wave][i] = bv;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+  const float m = selv[wave][0];
+  float part = 0.f;
+  for (int i = lane; i < k; i += 64) part += __expf(selv[wave][i] - m);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  const float inv = 1.f / part;
+  for (int i = lane; i < k; i += 64) a.w[t * k + i] = __expf(selv[wave][i] - m) * inv;
+}
+
+// Lane = token.  Each wave of the 256-token block sets bit `lane` of
+// mask[wave][e] for each expert e the token selected; a slot's rank inside the
+// block is the number of earlier tokens (lower waves, then lower lanes) that
+// selected the same expert.
+__global__ __launch_bounds__(256) void rank_kernel(RouteArgs a) {
+  extern __shared__ unsigned long long mask[];  // [4][E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = a.E, k = a.k;
+  for (int i = threadIdx.x; i < 4 * E; i += 256) mask[i] = 0ull;
+  __syncthreads();
+  const int64_t t = (int64_t)blockIdx.x * kRouteBlock + threadIdx.x;
+  const bool valid = t < a.T;
+  if (valid)
+    for (int i = 0; i < k; ++i) atomicOr(&mask[wave * E + a.idx[t * k + i]], 1ull << lane);
+  __syncthreads();
+  if (valid) {
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int i = 0; i < k; ++i) {
+      const int e = a.idx[t * k + i];
+      int r = __popcll(mask[wave * E + e] & below);
+      for (int w = 0; w < wave; ++w) r += __popcll(mask[w * E + e]);
+      a.slot_rank[t * k + i] = r;
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int c = 0;
+    for (int w = 0; w < 4; ++w) c += __popcll(mask[w * E + e]);
+    a.block_cnt[(int64_t)blockIdx.x * E + e] = c;
+  }
+}
+
+// One block of 1024 threads, thread = expert.
+__global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
+  __shared__ int sh[1024];
+  const int e = threadIdx.x;
+  const int E = a.E;
+  int total = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = a.block_cnt[(int64_t)b * E + e];
+      a.block_base[(int64_t)b * E + e] = total;
+      total += c;
+    }
+  }
+  // exclusive scan of totals
+  sh[e] = total;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? sh[e - off] : 0;
+    __syncthreads();
+    sh[e] += v;
+    __syncthreads();
+  }
+  const int off_e = sh[e] - total;
+  if (e < E) {
+    a.counts[e] = total;
+    a.offsets[e] = off_e;
+    for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off_e;
+  }
+  if (e == 0) a.offsets[E] = (int)(a.T * a.k);
+  __syncthreads();
+  // work items: ceil(count / kChunk) per routed expert, then the shared experts
+  const int chunks = e < E ? (total + kChunk - 1) / kChunk : 0;
+  sh[e] = chunks;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? sh[e - off] : 0;
+    __syncthreads();
+    sh[e] += v;
+    __syncthreads();
+  }
+  const int istart = sh[e] - chunks;
+  const int routed_items = sh[1023];
+  for (int c = 0; c < chunks; ++c) {
+    Item it;
+    it.bank = e;
+    it.pos = off_e + c * kChunk;
+    it.n = min(kChunk, total - c * kChunk);
+    it.pad = 0;
+    a.items[istart + c] = it;
+  }
+  const int per_shared = (int)((a.T + kChunk - 1) / kChunk);
+  const int64_t Tk = a.T * a.k;
+  for (int idx = e; idx < a.S * per_shared; idx += 1024) {
+    const int s = idx / per_shared, c = idx % per_shared;
+    Item it;
+    it.bank = E + s;
+    it.pos = (int)(Tk + (int64_t)s * a.T + (int64_t)c * kChunk);
+    it.n = (int)min((int64_t)kChunk, a.T - (int64_t)c * kChunk);
+    it.pad = 0;
+    a.items[routed_items + idx] = it;
+  }
+  if (e == 0) *a.n_items = routed_items + a.S * per_shared;
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
+  const int64_t s = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (s >= a.T * a.k) return;
+  const int64_t t = s / a.k;
+  const int e = a.idx[s];
+  const int64_t b = t / kRouteBlock;
+  a.perm[a.block_base[b * a.E + e] + a.slot_rank[s]] = (int)s;
+}
+
+hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream) {
+  (void)max_items;
+  const int nb = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  topk_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, stream>>>(a);
+  rank_kernel<<<nb, 256, 4 * a.E * sizeof(unsigned long long), stream>>>(a);
+  scan_kernel<<<1, 1024, 0, stream>>>(a, nb);
+  scatter_kernel<<<(unsigned)((a.T * a.k + 255) / 256), 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+// ============================================================ grouped experts
+// Work item = (bank, up to 16 tokens).  Lane l feeds token l%16 as the A
+// operand (activations, held in registers for the wave's K range) and weight
+// row l%16 of each 16-row tile as the B operand (decoded in registers); the KS
+// waves of a block split K and reduce through LDS.
+constexpr int MODE_GATEUP = 0;
+constexpr int MODE_DOWN = 1;
+
+template <int FMT, int MODE, int NG, int KS, int RT>
+__device__ __forceinline__ void expert_tile(const ExpertArgs& a, const Item& it, int tile,
+                                            const u32x2* lut, f32x4 (*red)[RT][64]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int K = MODE == MODE_GATEUP ? a.d : a.f;
+  const int G = K / kGroup;
+  const int BB = block_bytes_c<FMT>();
+  const int64_t row_bytes = (int64_t)G * BB;
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;  // one gate or up matrix
+
+  // activation row of this lane's token
+  const uint16_t* arow = nullptr;
+  if (i16 < it.n) {
+    const int64_t p = it.pos + i16;
+    if (MODE == MODE_GATEUP) {
+      const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
+      arow = a.x + tok * a.d;
+    } else {
+      arow = a.h + p * a.f;
+    }
+  }
+
+  const int g0 = wave * NG;
+  u32x4 A[NG][4];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = g0 + gi;
+    if (arow && g < G) {
+      if (FMT == kPQ2)
+        load_act_pq2(arow, g, q, A[gi]);
+      else
+        load_act_ptq1(arow, g, q, A[gi]);
+    } else {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[gi][m] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // weight rows of the RT tiles
+  const uint8_t* rows[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    if (MODE == MODE_GATEUP) {
+      // r = 0: gate rows, r = 1: up rows (same features)
+      const int64_t row = (int64_t)tile * 16 + i16;
+      rows[r] = bank + (r == 0 ? 0 : gu_bytes) + row * row_bytes;
+    } else {
+      const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
+      rows[r] = bank + 2 * gu_bytes + row * row_bytes;
+    }
+  }
+
+  f32x4 acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int copy = lane % kLutCopies;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int g = g0 + gi;
+    if (g >= G) break;
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      u32x4 W[4];
+      const float s = load_decode_block<FMT>(rows[r] + (int64_t)g * BB, lut, copy, q, W);
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) tmp = mfma16(A[gi][m], W[m], tmp);
+      acc[r] += s * tmp;
+    }
+  }
+
+  if (KS > 1) {
+    if (wave > 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) red[wave - 1][r][lane] = acc[r];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] += red[w][r][lane];
+  }
+
+  // lane holds tokens 4q + j of the item, column i16 of each tile
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ti = 4 * q + j;
+    if (ti >= it.n) continue;
+    const int64_t p = it.pos + ti;
+    if (MODE == MODE_GATEUP) {
+      const float g = acc[0][j], u = acc[1][j];
+      const float hv = g / (1.f + __expf(-g)) * u;
+      a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
+    } else {
+      int64_t slot;
+      float wgt;
+      if (p < a.Tk) {
+        slot = a.perm[p];
+        wgt = a.topk_w[slot];
+      } else {
+        slot = p;
+        wgt = 1.f;
+      }
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
+        a.slots[slot * a.d + row] = (uint16_t)f32_to_bf16(wgt * acc[r][j]);
+      }
+    }
+  }
+}
+
+template <int MODE, int NG, int KS, int RT>
+__global__ __launch_bounds__(64 * KS) void expert_kernel(ExpertArgs a) {
+  __shared__ u32x2 lut[256 * kLutCopies];
+  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][RT][64];
+  if ((int)blockIdx.y >= *a.n_items) return;
+  const Item it = a.items[blockIdx.y];
+  const int fmt = a.formats[it.bank];
+  if (fmt == kPTQ1) {
+    ptq1_lut_fill(lut, threadIdx.x, 64 * KS);
+    __syncthreads();
+    expert_tile<kPTQ1, MODE, NG, KS, RT>(a, it, blockIdx.x, lut, red);
+  } else {
+    expert_tile<kPQ2, MODE, NG, KS, RT>(a, it, blockIdx.x, lut, red);
+  }
+}
+
+template <int MODE, int NG, int RT>
+static void launch_ng(const ExpertArgs& a, dim3 grid, int ks, hipStream_t stream) {
+  switch (ks) {
+    case 1: expert_kernel<MODE, NG, 1, RT><<<grid, 64, 0, stream>>>(a); break;
+    case 2: expert_kernel<MODE, NG, 2, RT><<<grid, 128, 0, stream>>>(a); break;
+    case 3: expert_kernel<MODE, NG, 3, RT><<<grid, 192, 0, stream>>>(a); break;
+    case 4: expert_kernel<MODE, NG, 4, RT><<<grid, 256, 0, stream>>>(a); break;
+    case 5: expert_kernel<MODE, NG, 5, RT><<<grid, 320, 0, stream>>>(a); break;
+    case 6: expert_kernel<MODE, NG, 6, RT><<<grid, 384, 0, stream>>>(a); break;
+    case 7: expert_kernel<MODE, NG, 7, RT><<<grid, 448, 0, stream>>>(a); break;
+    default: expert_kernel<MODE, NG, 8, RT><<<grid, 512, 0, stream>>>(a); break;
+  }
+}
+
+// NG groups per wave (the smallest supported NG >= G/8), KS = ceil(G / NG) waves.
+template <int MODE, int RT>
+static hipError_t launch_expert_mode(const ExpertArgs& a, int64_t max_items, int tiles, int G,
+                                     hipStream_t stream) {
+  dim3 grid((unsigned)tiles, (unsigned)max_items);
+  const int need = (G + 7) / 8;
+  if (need <= 1) launch_ng<MODE, 1, RT>(a, grid, G, stream);
+  else if (need <= 2) launch_ng<MODE, 2, RT>(a, grid, (G + 1) / 2, stream);
+  else if (need <= 3) launch_ng<MODE, 3, RT>(a, grid, (G + 2) / 3, stream);
+  else if (need <= 4) launch_ng<MODE, 4, RT>(a, grid, (G + 3) / 4, stream);
+  else if (need <= 6) launch_ng<MODE, 6, RT>(a, grid, (G + 5) / 6, stream);
+  else if (need <= 8) launch_ng<MODE, 8, RT>(a, grid, (G + 7) / 8, stream);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  if (max_items <= 0) return hipSuccess;
+  hipError_t e = launch_expert_mode<MODE_GATEUP, 2>(a, max_items, a.f / 16, a.d / kGroup, stream);
+  if (e != hipSuccess) return e;
+  return launch_expert_mode<MODE_DOWN, 2>(a, max_items, a.d / 32, a.f / kGroup, stream);
+}
+
+}  // namespace moe

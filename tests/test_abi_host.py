@@ -1,0 +1,163 @@
+"""The C-ABI library on the host (no GPU): exports, the host container codec
+against the oracle codec, and every argument/format/code error path, all of
+which are decided before any launch."""
+import ctypes
+import re
+
+import numpy as np
+import pytest
+
+import ternary_quantized_moe_amd as tq
+from ternary_quantized_moe_amd import binding
+from golden_io import read_block_fixture
+from oracle import codec
+from synthetic import CONFIGS, LayerGen
+
+PQ2_0, PTQ1_0 = 142, 143
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(binding.__file__.replace("ternary_quantized_moe_amd/binding.py", "include/moe_ternary.h")).read()
+    declared = set(re.findall(r"^\s*(?:int64_t|int32_t|const char\*)\s+(moe_\w+)\(", header, re.M))
+    assert declared == set(binding.EXPORTS)
+    L = tq.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_block_sizes():
+    assert tq.block_bytes(PQ2_0) == 34 and tq.block_bytes(PTQ1_0) == 28
+    assert tq.block_bytes(42) == -1
+    assert tq.packed_bytes(PQ2_0, 256) == 68 and tq.packed_bytes(PTQ1_0, 100) == -1
+
+
+@pytest.mark.parametrize("fmt,name", [(PQ2_0, "pq2_0_block.txt"), (PTQ1_0, "ptq1_0_block.txt")])
+def test_golden_blocks(fmt, name):
+    trits, scale, data = read_block_fixture(name)
+    assert tq.pack(fmt, trits, np.array([scale], np.uint16)).tobytes() == data.tobytes()
+    t2, s2 = tq.unpack(fmt, data, 128)
+    assert np.array_equal(t2, trits) and int(s2[0]) == scale
+
+
+@pytest.mark.parametrize("fmt", [PQ2_0, PTQ1_0])
+def test_pack_matches_oracle_codec_bitwise(fmt):
+    g = LayerGen(CONFIGS["olmoe"])
+    for e in (0, 17):
+        for t, s in zip(g.expert_trits(e), g.expert_scales(e)):
+            mine = tq.pack(fmt, t, s)
+            ref = codec.pack(fmt, t, s)
+            assert mine.tobytes() == ref.tobytes()
+            tt, ss = tq.unpack(fmt, mine, t.size)
+            assert np.array_equal(tt, t.reshape(-1)) and np.array_equal(ss, s.reshape(-1))
+
+
+def test_unpack_exhaustive_pq2_bytes():
+    blocks = np.zeros((256, 34), np.uint8)
+    blocks[:, 5] = np.arange(256)
+    for v in range(256):
+        raw = blocks[v]
+        valid = all(((v >> (2 * i)) & 3) != 2 for i in range(4))
+        if valid:
+            t, s = tq.unpack(PQ2_0, raw, 128)
+            t2, s2 = codec.unpack(PQ2_0, raw, 128)
+            assert np.array_equal(t, t2)
+        else:
+            with pytest.raises(tq.MoeError) as ei:
+                tq.unpack(PQ2_0, raw, 128)
+            assert ei.value.name == "MOE_E_CODE" and "group 0, byte 5" in str(ei.value)
+
+
+def test_unpack_exhaustive_ptq1_bytes():
+    for pos, lim in ((3, 243), (25, 81)):
+        for v in range(256):
+            raw = np.zeros(56, np.uint8)
+            raw[28 + pos] = v
+            if v < lim:
+                t, _ = tq.unpack(PTQ1_0, raw, 256)
+                t2, _ = codec.unpack(PTQ1_0, raw, 256)
+                assert np.array_equal(t, t2)
+            else:
+                with pytest.raises(tq.MoeError) as ei:
+                    tq.unpack(PTQ1_0, raw, 256)
+                assert ei.value.name == "MOE_E_CODE" and f"group 1, byte {pos}" in str(ei.value)
+
+
+def test_codec_error_codes():
+    t = np.zeros(256, np.int8)
+    s = np.full(2, 0x3C00, np.uint16)
+    with pytest.raises(tq.MoeError) as ei:
+        tq.pack(42, t, s)
+    assert ei.value.name == "MOE_E_FORMAT" and "142" in str(ei.value) and "143" in str(ei.value)
+    with pytest.raises(tq.MoeError) as ei:
+        tq.pack(PQ2_0, np.zeros(100, np.int8), s[:0])
+    assert ei.value.name == "MOE_E_SHAPE"
+    bad = t.copy()
+    bad[7] = 3
+    with pytest.raises(tq.MoeError) as ei:
+        tq.pack(PTQ1_0, bad, s)
+    assert ei.value.name == "MOE_E_ARG"
+    for nf in (0x7C00, 0xFE00):
+        with pytest.raises(tq.MoeError) as ei:
+            tq.pack(PQ2_0, t, np.array([0x3C00, nf], np.uint16))
+        assert ei.value.name == "MOE_E_NONFINITE"
+    L = tq.lib()
+    out = np.zeros(10, np.uint8)
+    rc = L.moe_pack(PQ2_0, t.ctypes.data, s.ctypes.data, 256, out.ctypes.data, 10)
+    assert rc == -6
+    raw = np.zeros(28, np.uint8)
+    raw[27] = 0x7C
+    with pytest.raises(tq.MoeError) as ei:
+        tq.unpack(PTQ1_0, raw, 128)
+    assert ei.value.name == "MOE_E_NONFINITE"
+
+
+def _fake_banks(d=256, f=128, E=8, S=0, fmts=None, offsets=None, nbytes=None):
+    fmts = np.full(E + S, PQ2_0, np.uint8) if fmts is None else np.asarray(fmts, np.uint8)
+    size = 3 * d * f // 128 * 34
+    offsets = np.arange(E + S, dtype=np.int64) * size if offsets is None else np.asarray(offsets, np.int64)
+    keep = (fmts, offsets)
+    c = binding.ExpertBanksC(d, f, E, S, 0x1000, nbytes if nbytes is not None else size * (E + S), 0x2000,
+                             0x3000, offsets.ctypes.data, fmts.ctypes.data)
+    return c, keep
+
+
+def _forward_rc(c, T=4, k=2, r=16, x=0x10000, y=0x20000, ws=0x40000, ws_bytes=1 << 40, A=0x50000, B=0x60000,
+                router=0x70000):
+    L = tq.lib()
+    return L.moe_ternary_forward(x, T, router, None, ctypes.byref(c), A, B, r, k, y, ws, ws_bytes, None)
+
+
+def test_forward_validation_happens_before_launch():
+    L = tq.lib()
+    c, keep = _fake_banks()
+    assert _forward_rc(c, k=9) == -3                   # k > E
+    assert _forward_rc(c, k=0) == -3
+    assert _forward_rc(c, r=12) == -3                  # rank not a multiple of 8
+    assert _forward_rc(c, A=None) == -1                # A without B
+    assert _forward_rc(c, x=0x10000, y=0x10000) == -1  # aliasing
+    assert _forward_rc(c, ws_bytes=10) == -6
+    assert _forward_rc(c, ws=0x40010) == -1            # misaligned workspace
+    assert _forward_rc(c, T=0) == 0                    # no-op, nothing launched
+    assert "" == L.moe_last_error().decode()
+    c2, keep2 = _fake_banks(d=200)
+    assert _forward_rc(c2) == -3
+    c3, keep3 = _fake_banks(fmts=[142] * 7 + [99])
+    assert _forward_rc(c3) == -2
+    assert "bank 7" in L.moe_last_error().decode()
+    c4, keep4 = _fake_banks(nbytes=100)
+    assert _forward_rc(c4) == -6
+    c5, keep5 = _fake_banks(offsets=np.arange(8) * 2)
+    assert _forward_rc(c5) == -1                      # offsets not multiples of 4
+    assert L.moe_workspace_bytes(ctypes.byref(c), 16, 2, 16) > 0
+    assert L.moe_workspace_bytes(None, 16, 2, 16) == -1
+
+
+def test_route_validation():
+    L = tq.lib()
+    assert L.moe_route(0x1000, 4, 100, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
+    assert L.moe_route(0x1000, 4, 256, 8, 0x2000, None, 9, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
+    assert L.moe_route(0x1000, 4, 256, 2000, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
+    assert L.moe_route(0x1000, 4, 256, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 16, None) == -6
+    assert L.moe_route(0x1000, 0, 256, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 0, None) == 0
+    assert L.moe_unpack_device(99, 1, 128, 1, 1, None) == -2
+    assert L.moe_unpack_device(142, 1, 100, 1, 1, None) == -3
