@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Forward-pass throughput of the ternary-expert MoE block on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep FILE]
+
+A step is one forward pass of the whole block (router + delta, top-k, grouping,
+gate/up, down, combine + correction) over one batch of synthetic tokens, with
+every input already resident in HBM.  Each step uses the next of R copies of
+the layer's expert banks (R chosen so the copies exceed 1 GB, more than the
+256 MB Infinity Cache) and the next of P activation sets, so routing changes
+from step to step and weights come from HBM.
+
+Prints one JSON line: whole-job tokens/s, the roofline of the dominant kernel
+(the gate/up expert kernel) from the library's stage events inside the timed
+region, and the fp64 oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-block tokens/s (decode b=1..64, prefill 4k) + % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+# name -> (layer config, tokens, mode)
+WORKLOADS = {
+    "olmoe-b1": ("olmoe", 1, "decode"), "olmoe-b8": ("olmoe", 8, "decode"),
+    "olmoe-b64": ("olmoe", 64, "decode"),
+    "a3b35-b1": ("a3b35", 1, "decode"), "a3b35-b8": ("a3b35", 8, "decode"),
+    "a3b35-b32": ("a3b35", 32, "decode"), "a3b35-p4096": ("a3b35", 4096, "prefill"),
+    "flashnext-b1": ("flashnext", 1, "decode"), "flashnext-b8": ("flashnext", 8, "decode"),
+    "flashnext-b64": ("flashnext", 64, "decode"), "flashnext-p4096": ("flashnext", 4096, "prefill"),
+    "skewed-p16384": ("skewed", 16384, "prefill"),
+}
+DEFAULT_WORKLOAD = "olmoe-b64"
+DESCR = {
+    "olmoe": "OLMoE-shaped MoE block (d=2048, 64 PQ2_0 experts, ffn 1024, top-8, rank-512 correction)",
+    "a3b35": "35B-A3B-class MoE block (d=2048, 128 PQ2_0 experts, ffn 768, top-8, rank-512 correction)",
+    "flashnext": "Flash-Next-shaped MoE block (d=3072, 512 PTQ1_0 experts top-10 + 1 shared, ffn 512, "
+                 "rank-512 correction)",
+    "skewed": "Skewed-routing stress at Flash-Next shape (Zipf 1.1 popularity, mixed PQ2_0/PTQ1_0, "
+              "1% x50 outliers)",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ternary_quantized_moe_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """Measured HBM traffic of the dominant kernel (profiles/traffic.json), or
+    None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path)).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("src_sha") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+class Bench:
+    def __init__(self, workload: str):
+        import numpy as np
+        import torch
+
+        import ternary_quantized_moe_amd as tq
+        from synthetic import CONFIGS, LayerGen
+
+        self.np, self.torch, self.tq = np, torch, tq
+        self.workload = workload
+        cname, self.T, self.mode = WORKLOADS[workload]
+        self.cfg = c = CONFIGS[cname]
+        self.gen = g = LayerGen(c)
+        self.formats = g.formats()
+        dev = self.dev = torch.device("cuda:0")
+        t0 = time.time()
+        data, offsets = tq.build_banks(self.source, c.n_banks, self.formats, c.d_model, c.d_ff)
+        self.offsets = offsets
+        self.bank_bytes = int(data.size)
+        base = torch.from_numpy(data).to(dev)
+        self.R = max(1, math.ceil(1.0e9 / self.bank_bytes))
+        self.banks = [tq.ExpertBanks.from_tensors(base if i == 0 else base.clone(), offsets, self.formats,
+                                                  c.d_model, c.d_ff, c.n_experts, c.n_shared)
+                      for i in range(self.R)]
+        self.gu_bytes = np.where(self.formats == 142, 34, 28).astype(np.int64) * 2 * c.d_ff * c.d_model // 128
+        self.dn_bytes = self.gu_bytes // 2
+        t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+        self.router_bits, self.delta_bits = g.router_bits(), g.delta_bits()
+        self.a_bits, self.b_bits = g.corr_a_bits(), g.corr_b_bits()
+        self.router, self.delta = t(self.router_bits), t(self.delta_bits)
+        self.corr_a, self.corr_b = t(self.a_bits), t(self.b_bits)
+        self.P = 16 if self.mode == "decode" else 2
+        self.x_bits = [g.tokens(self.T, p) for p in range(self.P)]
+        self.x = [t(xb) for xb in self.x_bits]
+        self.y = torch.empty_like(self.x[0])
+        self.ws = tq.alloc_workspace(tq.workspace_bytes(self.banks[0], self.T, c.top_k, c.rank), dev)
+        # realised routing of every activation set (untimed): touched banks, slots
+        self.touched, self.idx = [], []
+        for p in range(self.P):
+            r = tq.route(self.x[p], self.router, self.delta, c.n_experts, c.top_k)
+            counts = r["counts"].cpu().numpy()
+            touched = np.nonzero(counts)[0]
+            self.touched.append(np.concatenate([touched, np.arange(c.n_experts, c.n_banks)]))
+            self.idx.append(r["idx"].cpu().numpy())
+        torch.cuda.synchronize()
+        self.setup_s = time.time() - t0
+
+    def source(self, e):
+        return self.gen.expert_trits(e), self.gen.expert_scales(e)
+
+    def step(self, i: int):
+        c = self.cfg
+        self.tq.forward(self.x[i % self.P], self.router, self.delta, self.banks[i % self.R], self.corr_a,
+                        self.corr_b, c.top_k, y=self.y, workspace=self.ws)
+
+    # ---- parity before timing ----------------------------------------------------
+    def parity(self, n_tokens: int = 4) -> float:
+        np = self.np
+        from oracle import moe as omoe
+        c = self.cfg
+        self.step(0)
+        self.torch.cuda.synchronize()
+        y = self.y.cpu().numpy().view(np.uint16)
+        T = self.T
+        toks = np.unique(np.linspace(0, T - 1, min(n_tokens, T)).astype(int))
+        ob = omoe.LazyBanks(self.source, self.formats, c.d_model, c.d_ff, c.n_experts, c.n_shared)
+        ref = omoe.forward(self.x_bits[0][toks], self.router_bits, self.delta_bits, ob, self.a_bits,
+                           self.b_bits, c.top_k, forced_idx=self.idx[0][toks])
+        yg = omoe.bf16_to_f64(y[toks])
+        return float((np.abs(yg - ref.y).max(axis=1) / np.linalg.norm(ref.y, axis=1)).max())
+
+    # ---- algorithmic work ----------------------------------------------------------
+    def alg(self, p: int):
+        """(whole-block bytes, gate/up bytes, whole-block flops, gate/up flops) of one
+        step on activation set p, from its realised routing."""
+        c = self.cfg
+        T, d, f, E, r, k, S = self.T, c.d_model, c.d_ff, c.n_experts, c.rank, c.top_k, c.n_shared
+        touched = self.touched[p]
+        n_pos = T * k + S * T
+        expert_bytes = int((self.gu_bytes[touched] + self.dn_bytes[touched]).sum())
+        block_bytes = expert_bytes + 4 * E * d + 4 * r * d + 4 * T * d
+        gu_bytes = int(self.gu_bytes[touched].sum()) + 2 * T * d + 2 * n_pos * f
+        block_flops = 2 * (n_pos * 3 * d * f + T * E * d + 2 * T * r * d)
+        gu_flops = 2 * n_pos * 2 * f * d
+        return block_bytes, gu_bytes, block_flops, gu_flops
+
+
+def cpu_baseline(b: Bench, budget_s: float = 25.0):
+    """The fp64 oracle, as it stands, on the first s tokens of activation set 0."""
+    np = b.np
+    from oracle import codec, moe as omoe
+    c = b.cfg
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    x = omoe.bf16_to_f64(b.x_bits[0])
+    w = omoe.f16_to_f64(b.router_bits) + omoe.f16_to_f64(b.delta_bits)
+    order = np.argsort(-(x @ w.T), axis=1, kind="stable")[:, :c.top_k]
+
+    def needed(s):
+        return sorted(set(order[:s].reshape(-1).tolist()) | set(range(c.n_experts, c.n_banks)))
+
+    # cost of one bank decode (untimed probe)
+    probe = omoe.LazyBanks(b.source, b.formats, c.d_model, c.d_ff, c.n_experts, c.n_shared)
+    blob = probe.container(0)
+    t0 = time.perf_counter()
+    codec.decode(int(b.formats[0]), blob, 3 * c.d_model * c.d_ff)
+    per_bank = time.perf_counter() - t0
+    s = min(b.T, 64)
+    while s > 1 and len(needed(s)) * per_bank > budget_s:
+        s //= 2
+    banks_needed = needed(s)
+    # pre-pack (untimed) the banks the sample touches with the oracle codec
+    offsets = np.zeros(c.n_banks, dtype=np.int64)
+    chunks, pos = [], 0
+    for e in banks_needed:
+        blob = probe.container(e)
+        offsets[e] = pos
+        chunks.append(blob)
+        pos += blob.size
+    banks = omoe.Banks(np.concatenate(chunks), offsets, b.formats, c.d_model, c.d_ff, c.n_experts,
+                       c.n_shared)
+    t0 = time.perf_counter()
+    omoe.forward(b.x_bits[0][:s], b.router_bits, b.delta_bits, banks, b.a_bits, b.b_bits, c.top_k)
+    dt = time.perf_counter() - t0
+    return {"value": s / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {s} of {b.T} tokens of activation set 0 "
+                      f"({len(banks_needed)} expert banks decoded), {dt:.1f} s"}
+
+
+def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
+    import numpy as np
+    import torch
+    import ternary_quantized_moe_amd as tq
+
+    b = Bench(workload)
+    c = b.cfg
+    par = b.parity()
+    for i in range(warmup):
+        b.step(i)
+    timer = tq.StageTimer(steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        with timer.step():
+            b.step(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stage_ms = timer.ms()
+
+    works = [b.alg((warmup + i) % b.P) for i in range(steps)]
+    block_bytes = float(np.mean([w[0] for w in works]))
+    gu_bytes = float(np.mean([w[1] for w in works]))
+    block_flops = float(np.mean([w[2] for w in works]))
+    gu_flops = float(np.mean([w[3] for w in works]))
+    ms_step = elapsed * 1e3 / steps
+    gu_s = stage_ms[2] * 1e-3
+    if b.mode == "decode":
+        ach = gu_bytes / gu_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload),
+                "kernel": "expert_kernel<gate/up>", "alg_bytes_per_launch": int(gu_bytes),
+                "avg_launch_us": round(gu_s * 1e6, 2)}
+        block = {"alg_bytes": int(block_bytes), "achieved_GBs": round(block_bytes / (ms_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(block_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    else:
+        ach = gu_flops / gu_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": load_traffic(workload),
+                "kernel": "expert_kernel<gate/up>", "alg_flops_per_launch": int(gu_flops),
+                "avg_launch_us": round(gu_s * 1e6, 2)}
+        block = {"alg_flops": int(block_flops),
+                 "achieved_TFLOPs": round(block_flops / (ms_step * 1e-3) / 1e12, 1),
+                 "mfma_frac": round(block_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    rec = {
+        "metric": METRIC,
+        "value": round(steps * b.T / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{DESCR[c.name]}, {b.mode} {b.T} tokens", "name": workload,
+                   "tokens": b.T, "mode": b.mode, "bank_replicas": b.R, "activation_sets": b.P,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "block": block,
+        "stages_ms": {n: round(float(v), 4) for n, v in zip(tq.STAGES, stage_ms)},
+        "parity_max_row_err": par,
+    }
+    if with_cpu:
+        rec["cpu_baseline"] = cpu_baseline(b)
+    del b
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
+    ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the block's forward pass is data-parallel over tokens with no "
+              f"cross-GPU exchange, and this build runs on a single MI355X (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    if args.sweep:
+        names = [n for n in WORKLOADS if not args.only or n in args.only.split(",")]
+        for name in names:
+            steps = args.steps if WORKLOADS[name][2] == "decode" else max(5, args.steps // 10)
+            rec = run(name, steps, args.warmup, with_cpu=not args.no_cpu)
+            with open(args.sweep, "a") as f:
+                f.write(json.dumps(rec) + "\n")
+            print(f"{name}: {rec['value']:.0f} tokens/s, {rec['ms_per_step']:.4f} ms/step, "
+                  f"{rec['roofline']['bound']} frac {rec['roofline']['frac']:.3f}, stages_us "
+                  + " ".join(f"{k}={v * 1e3:.1f}" for k, v in rec["stages_ms"].items())
+                  + f", parity {rec['parity_max_row_err']:.1e}", file=sys.stderr, flush=True)
+        return
+    rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -112,14 +112,17 @@ int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n_weights, 
  * at byte offsets[e] of `banks` and holds three containers back to back:
  * gate [d_ff x d_model], up [d_ff x d_model], down [d_model x d_ff], row-major,
  * groups of 128 along each row, all in format formats[e].  Offsets must be
- * multiples of 4 and every bank must lie inside banks_bytes. */
+ * multiples of 4, and the buffer must extend at least MOE_BANK_SLACK bytes past
+ * the end of every bank (the expert kernels read each block with one 12-byte
+ * load that can run 2 bytes past the block); the slack's content is ignored. */
+enum { MOE_BANK_SLACK = 16 };
 typedef struct moe_expert_banks {
   int32_t d_model;              /* d: multiple of 128                              */
   int32_t d_ff;                 /* f: multiple of 128                              */
   int32_t n_experts;            /* E >= 1 routed experts                           */
   int32_t n_shared;             /* S >= 0 shared experts (weight 1, no gate)       */
   const uint8_t* banks;         /* device: all containers                          */
-  int64_t banks_bytes;          /* size of `banks` in bytes (bounds check)         */
+  int64_t banks_bytes;          /* size of `banks` in bytes, slack included        */
   const int64_t* offsets;       /* device int64[E+S]                               */
   const uint8_t* formats;       /* device uint8[E+S]: 142 or 143                   */
   const int64_t* offsets_host;  /* host copy of offsets (validation)               */
@@ -165,6 +168,16 @@ int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t 
                   float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
                   int32_t* offsets, int32_t* perm, void* workspace, int64_t workspace_bytes,
                   void* stream);
+
+/* Measurement hook.  With events != NULL (n_events >= 2 * MOE_N_STAGES
+ * hipEvent_t handles created by the caller), every later moe_ternary_forward
+ * call on this thread records events[2s] before and events[2s+1] after stage s
+ * on the call's stream; NULL (or n_events = 0) turns recording off.  Stages:
+ * 0 router/correction projection, 1 routing (top-k, ranking, scan, scatter),
+ * 2 gate/up experts, 3 down experts, 4 combine.  The library keeps the pointer
+ * until it is replaced; the caller keeps the events alive meanwhile. */
+enum { MOE_N_STAGES = 5 };
+int32_t moe_set_stage_events(void** events, int32_t n_events);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char* moe_last_error(void);

@@ -26,8 +26,10 @@ _ERRORS = {
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
     "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
-    "moe_last_error",
+    "moe_set_stage_events", "moe_last_error",
 ]
+N_STAGES = 5
+STAGES = ["xproj", "routing", "gate_up", "down", "combine"]
 
 
 class MoeError(RuntimeError):
@@ -69,6 +71,7 @@ def lib():
                                           i32, vp, vp, i64, vp]),
             "moe_route_workspace_bytes": (i64, [i64, i32, i32, i32]),
             "moe_route": (i32, [vp, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_set_stage_events": (i32, [ctypes.POINTER(ctypes.c_void_p), i32]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -242,3 +245,42 @@ def route(x, router, router_delta, n_experts: int, top_k: int, workspace=None, s
                            wp, wn, _stream(stream)))
     out["perm"] = out["perm"][: T * top_k]
     return out
+
+
+class StageTimer:
+    """Per-stage device time of forward calls, from the library's stage events.
+
+    Create once, then `with timer.step():` around each forward call; events are
+    recorded on the call's stream.  `ms()` synchronises and returns the mean
+    duration per stage over the recorded steps."""
+
+    def __init__(self, n_steps: int):
+        import torch
+        self._ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * N_STAGES)] for _ in range(n_steps)]
+        for evs in self._ev:          # torch creates the HIP event on first record
+            for e in evs:
+                e.record()
+        torch.cuda.synchronize()
+        self._arr = [(ctypes.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in evs]) for evs in self._ev]
+        self._i = 0
+
+    def step(self):
+        timer = self
+
+        class _Ctx:
+            def __enter__(self_inner):
+                _check(lib().moe_set_stage_events(timer._arr[timer._i], 2 * N_STAGES))
+
+            def __exit__(self_inner, *exc):
+                _check(lib().moe_set_stage_events(None, 0))
+                timer._i += 1
+        return _Ctx()
+
+    def ms(self):
+        import torch
+        torch.cuda.synchronize()
+        out = np.zeros(N_STAGES)
+        for evs in self._ev[: self._i]:
+            for s in range(N_STAGES):
+                out[s] += evs[2 * s].elapsed_time(evs[2 * s + 1])
+        return out / max(self._i, 1)

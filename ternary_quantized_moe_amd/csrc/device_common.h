@@ -87,24 +87,33 @@ __device__ __forceinline__ int kslot_ptq1(int m, int q, int j) {
   return r < 30 ? 30 * q + r : 120 + 2 * q + (j & 1);
 }
 
-__device__ __forceinline__ u32x2 ptq1_lut_entry(int v) {
-  uint32_t b[5];
+// The byte table as a compile-time constant in the code object (2 KB).
+struct Ptq1Table {
+  uint32_t lo[256];
+  uint32_t hi[256];
+};
+__host__ __device__ constexpr uint32_t ptq1_code_byte(int v, int i) {
   int r = v;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    const int d = r % 3;
-    r /= 3;
-    b[i] = d == 0 ? 0u : (d == 1 ? 0x40u : 0xC0u);
-  }
-  u32x2 e;
-  e.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-  e.y = b[4];
-  return e;
+  for (int j = 0; j < i; ++j) r /= 3;
+  return r % 3 == 0 ? 0u : (r % 3 == 1 ? 0x40u : 0xC0u);
 }
+__host__ __device__ constexpr Ptq1Table make_ptq1_table() {
+  Ptq1Table t{};
+  for (int v = 0; v < 256; ++v) {
+    t.lo[v] = ptq1_code_byte(v, 0) | (ptq1_code_byte(v, 1) << 8) | (ptq1_code_byte(v, 2) << 16) |
+              (ptq1_code_byte(v, 3) << 24);
+    t.hi[v] = ptq1_code_byte(v, 4);
+  }
+  return t;
+}
+__device__ constexpr Ptq1Table kPtq1Table = make_ptq1_table();
 
 // Fill the LDS byte table (all threads of the block take part; caller syncs).
 __device__ __forceinline__ void ptq1_lut_fill(u32x2* lut, int tid, int nthreads) {
-  for (int idx = tid; idx < 256 * kLutCopies; idx += nthreads) lut[idx] = ptq1_lut_entry(idx / kLutCopies);
+  for (int idx = tid; idx < 256 * kLutCopies; idx += nthreads) {
+    const int v = idx / kLutCopies;
+    lut[idx] = u32x2{kPtq1Table.lo[v], kPtq1Table.hi[v]};
+  }
 }
 
 __device__ __forceinline__ u32x2 lut_get(const u32x2* lut, uint32_t v, int copy) {
@@ -143,21 +152,38 @@ __device__ __forceinline__ void decode_ptq1(const u32x2* lut, int copy, uint32_t
   for (int m = 0; m < 4; ++m) out[m] = u32x4{P[4 * m], P[4 * m + 1], P[4 * m + 2], P[4 * m + 3]};
 }
 
-// Load one lane's quarter of a block and decode it; returns the group scale
-// (already multiplied by 0.5 to undo the +-2 encoding).
+// One load per lane per block: three dwords from byte 8q (PQ2_0) or 6q
+// (PTQ1_0) of the block.  The first two are the lane's code dwords (PQ2_0:
+// bytes 8q .. 8q+7; PTQ1_0: bytes 6q .. 6q+7); quarter 3's load also covers the
+// bytes after the data (PQ2_0: the scale at 32..33; PTQ1_0: tail bytes 24..25
+// and the scale at 26..27) and runs 2 bytes past the block, which is why
+// expert banks carry 16 bytes of readable slack after their last block.  The
+// row's four lanes are l%16 + 16q, so quarter 3's bytes reach the others with
+// one cross-lane read.
+typedef __attribute__((ext_vector_type(3))) uint32_t u32x3;
+typedef u32x3 __attribute__((aligned(2))) u32x3_a2;
+
 template <int FMT>
-__device__ __forceinline__ float load_decode_block(const uint8_t* blk, const u32x2* lut, int copy,
-                                                   int q, u32x4 out[4]) {
+__device__ __forceinline__ u32x3 load_block_x3(const uint8_t* blk, int q) {
+  return *(const u32x3_a2*)(blk + (FMT == kPQ2 ? 8 : 6) * q);
+}
+
+// Decode one lane's quarter of a block fetched with load_block_x3 into the
+// B operands; returns the group scale.  The operands encode 2t, so results
+// carry a factor 2 that the caller removes once.
+template <int FMT>
+__device__ __forceinline__ float decode_block_x3(u32x3 v, const u32x2* lut, int lane, u32x4 out[4]) {
+  const int q = lane >> 4;
+  // PQ2_0: quarter 3's third dword holds bytes 32..35 (scale low half);
+  // PTQ1_0: bytes 24..27 (tail bytes low half, scale high half).
+  const uint32_t mine = FMT == kPQ2 ? v.z : __builtin_amdgcn_alignbit(v.z, v.y, 16);
+  const uint32_t shared = __shfl(mine, (lane & 15) + 48, 64);
   if (FMT == kPQ2) {
-    const u32x2 w = *(const u32x2_a2*)(blk + 8 * q);
-    const uint32_t s = *(const uint16_t*)(blk + 32);
-    decode_pq2(w.x, w.y, out);
-    return 0.5f * f16_to_f32(s);
+    decode_pq2(v.x, v.y, out);
+    return f16_to_f32(shared & 0xFFFFu);
   } else {
-    const u32x2 w = *(const u32x2_a2*)(blk + 6 * q);
-    const uint32_t t = *(const uint32_t*)(blk + 24);
-    decode_ptq1(lut, copy, w.x, w.y, t, q, out);
-    return 0.5f * f16_to_f32(t >> 16);
+    decode_ptq1(lut, lane % kLutCopies, v.x, v.y, shared, q, out);
+    return f16_to_f32(shared >> 16);
   }
 }
 
@@ -168,36 +194,59 @@ __host__ __device__ constexpr int block_bytes_c() {
 
 // ---------------------------------------------------------------- activations
 // Matrix-core A operands (bf16) for one row of activations and one group, in the
-// k-slot order of the container format.  `row` points at the row start.
-__device__ __forceinline__ void load_act_pq2(const uint16_t* row, int g, int q, u32x4 out[4]) {
-  const u32x4* p = (const u32x4*)(row + g * 128 + 32 * q);
-  u32x4 X[4] = {p[0], p[1], p[2], p[3]};
-  uint32_t x[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[4 * i + 0] = X[i].x;
-    x[4 * i + 1] = X[i].y;
-    x[4 * i + 2] = X[i].z;
-    x[4 * i + 3] = X[i].w;
+// k-slot order of the container format.  The raw loads and the reordering are
+// separate so a prefetch ring can hold the raw dwords.
+//   PQ2_0: raw = elements 32q .. 32q+31 of the group (16 dwords);
+//   PTQ1_0: raw = elements 30q .. 30q+29 and the tail pair 120+2q, 121+2q.
+struct ActRaw {
+  u32x4 v[4];
+};
+
+template <int FMT>
+__device__ __forceinline__ ActRaw load_act_raw(const uint16_t* row, int g, int q) {
+  ActRaw r;
+  if (FMT == kPQ2) {
+    const u32x4* p = (const u32x4*)(row + g * 128 + 32 * q);
+    r.v[0] = p[0];
+    r.v[1] = p[1];
+    r.v[2] = p[2];
+    r.v[3] = p[3];
+  } else {
+    const uint16_t* p = row + g * 128 + 30 * q;  // 4-byte aligned
+    r.v[0] = *(const u32x4_a4*)(p + 0);
+    r.v[1] = *(const u32x4_a4*)(p + 8);
+    r.v[2] = *(const u32x4_a4*)(p + 16);
+    const u32x2 w = *(const u32x2_a4*)(p + 24);
+    const uint32_t w2 = *(const uint32_t*)(p + 28);
+    const uint32_t t = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
+    r.v[3] = u32x4{w.x, w.y, w2, t};
   }
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d1 = 8 * (m >> 1) + 2 * (m & 1) + (i >> 1);
-      out[m][i] = perm_b32(x[d1 + 4], x[d1], (i & 1) ? 0x07060302u : 0x05040100u);
-    }
-  }
+  return r;
 }
 
-__device__ __forceinline__ void load_act_ptq1(const uint16_t* row, int g, int q, u32x4 out[4]) {
-  const uint32_t* p = (const uint32_t*)(row + g * 128 + 30 * q);
-  uint32_t x[16];
+template <int FMT>
+__device__ __forceinline__ void act_operands(const ActRaw& r, u32x4 out[4]) {
+  if (FMT == kPQ2) {
+    uint32_t x[16];
 #pragma unroll
-  for (int i = 0; i < 15; ++i) x[i] = p[i];
-  x[15] = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
+    for (int i = 0; i < 4; ++i) {
+      x[4 * i + 0] = r.v[i].x;
+      x[4 * i + 1] = r.v[i].y;
+      x[4 * i + 2] = r.v[i].z;
+      x[4 * i + 3] = r.v[i].w;
+    }
 #pragma unroll
-  for (int m = 0; m < 4; ++m) out[m] = u32x4{x[4 * m], x[4 * m + 1], x[4 * m + 2], x[4 * m + 3]};
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d1 = 8 * (m >> 1) + 2 * (m & 1) + (i >> 1);
+        out[m][i] = perm_b32(x[d1 + 4], x[d1], (i & 1) ? 0x07060302u : 0x05040100u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) out[m] = r.v[m];
+  }
 }
 
 }  // namespace moe

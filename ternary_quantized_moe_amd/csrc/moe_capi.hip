@@ -17,6 +17,13 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local void** g_stage_events = nullptr;
+
+// Record the stage's start (end=false) or end event if measurement is on.
+hipError_t stage_mark(int stage, bool end, hipStream_t st) {
+  if (!g_stage_events) return hipSuccess;
+  return hipEventRecord((hipEvent_t)g_stage_events[2 * stage + (end ? 1 : 0)], st);
+}
 
 int32_t fail(int32_t code, const char* fmt, ...) {
   char buf[512];
@@ -124,9 +131,9 @@ int32_t check_banks(const moe_expert_banks* b) {
     const int64_t off = b->offsets_host[e];
     const int64_t bytes = nblocks * moe_block_bytes(fmt);
     if (off < 0 || off % 4) return fail(MOE_E_ARG, "bank %d: offset %lld is not a non-negative multiple of 4", e, (long long)off);
-    if (off + bytes > b->banks_bytes)
-      return fail(MOE_E_SPACE, "bank %d: bytes [%lld, %lld) exceed banks_bytes %lld", e, (long long)off,
-                  (long long)(off + bytes), (long long)b->banks_bytes);
+    if (off + bytes + MOE_BANK_SLACK > b->banks_bytes)
+      return fail(MOE_E_SPACE, "bank %d: bytes [%lld, %lld) plus %d bytes of slack exceed banks_bytes %lld", e,
+                  (long long)off, (long long)(off + bytes), (int)MOE_BANK_SLACK, (long long)b->banks_bytes);
   }
   return MOE_OK;
 }
@@ -136,6 +143,17 @@ int32_t check_banks(const moe_expert_banks* b) {
 extern "C" {
 
 const char* moe_last_error(void) { return g_err.c_str(); }
+
+int32_t moe_set_stage_events(void** events, int32_t n_events) {
+  if (events == nullptr || n_events == 0) {
+    g_stage_events = nullptr;
+    return ok();
+  }
+  if (n_events < 2 * MOE_N_STAGES)
+    return fail(MOE_E_ARG, "need %d events, got %d", 2 * MOE_N_STAGES, (int)n_events);
+  g_stage_events = events;
+  return ok();
+}
 
 int64_t moe_block_bytes(int32_t fmt) {
   if (fmt == MOE_PQ2_0) return 34;
@@ -289,7 +307,9 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.N1 = corr_A ? r : 0;
   da.logits = logits;
   da.z = at<uint16_t>(ws, p.z);
-  hipError_t e = moe::launch_xproj(da, stream);
+  hipError_t e = stage_mark(0, false, stream);
+  if (e == hipSuccess) e = moe::launch_xproj(da, stream);
+  if (e == hipSuccess) e = stage_mark(0, true, stream);
   if (e != hipSuccess) return device_fail(e, "xproj launch");
 
   moe::RouteArgs ra{};
@@ -308,7 +328,9 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.perm = perm;
   ra.items = at<moe::Item>(ws, p.items);
   ra.n_items = at<int32_t>(ws, p.nitems);
-  e = moe::launch_route(ra, p.max_items, stream);
+  e = stage_mark(1, false, stream);
+  if (e == hipSuccess) e = moe::launch_route(ra, p.max_items, stream);
+  if (e == hipSuccess) e = stage_mark(1, true, stream);
   if (e != hipSuccess) return device_fail(e, "routing launch");
   return MOE_OK;
 }
@@ -384,7 +406,10 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     ea.x = x;
     ea.h = at<uint16_t>(ws, p.h);
     ea.slots = at<uint16_t>(ws, p.slots);
-    hipError_t e = moe::launch_experts(ea, p.max_items, st);
+    ea.nmax = (int)std::min<int64_t>(T, moe::kChunk);
+    ea.fmt_mask = 0;
+    for (int e = 0; e < E + S; ++e) ea.fmt_mask |= banks->formats_host[e] == MOE_PQ2_0 ? 1 : 2;
+    hipError_t e = moe::launch_experts(ea, p.max_items, st, g_stage_events);
     if (e != hipSuccess) return device_fail(e, "expert launch");
 
     moe::DenseArgs ca{};
@@ -398,7 +423,9 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     ca.top_k = k;
     ca.n_shared = S;
     ca.y = y;
-    e = moe::launch_combine(ca, st);
+    e = stage_mark(4, false, st);
+    if (e == hipSuccess) e = moe::launch_combine(ca, st);
+    if (e == hipSuccess) e = stage_mark(4, true, st);
     if (e != hipSuccess) return device_fail(e, "combine launch");
     return ok();
   } catch (...) {

@@ -1,0 +1,500 @@
+// Grouped ternary expert kernels (gate/up + SwiGLU, down + gate weight).
+//
+// Work item = (bank, up to 16 consecutive positions of the (expert, token)
+// order).  A unit of work is (item, block tile): the block stages the item's
+// activation rows in LDS once (coalesced, already in matrix-core operand order)
+// and its waves take 16-row tiles of the bank's containers and stream them
+// along K with a register prefetch ring.
+// Every 128-weight block is decoded in registers into bf16 B operands (+-2
+// encoding, see device_common.h), multiplied with v_mfma_f32_16x16x32_bf16
+// (tokens are the M dimension, rows the N dimension), and the group scale is
+// applied to the fp32 accumulator.  With KS > 1 the waves of a tile split K and
+// reduce through LDS.  Blocks are persistent: each loops over units, so the
+// PTQ1_0 byte table is filled once per block.
+// Expert FFN: Scion README "Serving notes" (per-expert mul_mat_id); SwiGLU
+// reading and container layouts: include/moe_ternary.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int MODE_GATEUP = 0;
+constexpr int MODE_DOWN = 1;
+
+// Stage the item's activation rows (n tokens x K) into LDS as matrix-core A
+// operands in the container format's k-slot order: row i, group g, MFMA m,
+// quarter q -> 16 bytes at i * stride + ((g * 4 + m) * 4 + q) * 16.  The
+// 16-byte row padding puts the 16 token rows of one operand read on different
+// LDS banks.
+__host__ __device__ constexpr int stage_stride(int K) { return 2 * K + 16; }
+
+template <int FMT, int MODE>
+__device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Item& it, char* xs, int K) {
+  const int G = K / kGroup;
+  const int units = it.n * G * 4;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int i = u / (G * 4), rem = u % (G * 4), g = rem >> 2, q = rem & 3;
+    const int64_t p = it.pos + i;
+    const uint16_t* row;
+    if (MODE == MODE_GATEUP) {
+      const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
+      row = a.x + tok * a.d;
+    } else {
+      row = a.h + p * a.f;
+    }
+    u32x4 out[4];
+    act_operands<FMT>(load_act_raw<FMT>(row, g, q), out);
+    char* dst = xs + i * stage_stride(K) + (g * 16 + q) * 16;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) *(u32x4*)(dst + m * 64) = out[m];
+  }
+}
+
+// One (item, tile block) unit.  GW > 0: each wave covers exactly GW groups
+// (K = GW * KS * 128, a compile-time shape), fully unrolled so the prefetch
+// ring, the load offsets and the LDS offsets are static.  GW = 0: any K.
+template <int FMT, int MODE, int WPB, int KS, int RT, int D, int GW>
+__device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it, int tblock, const u32x2* lut,
+                                            char* xs, f32x4* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int K = MODE == MODE_GATEUP ? a.d : a.f;
+  const int G = K / kGroup;
+  constexpr int BB = block_bytes_c<FMT>();
+  const int64_t row_bytes = (int64_t)G * BB;
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
+
+  constexpr int TPB = WPB / KS;  // tiles per block
+  const int tile = tblock * TPB + wave / KS;
+  const int ks = wave % KS;
+  const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
+  const bool active = tile < n_tiles;
+  const int gpk = GW > 0 ? GW : (G + KS - 1) / KS;
+  const int gb = ks * gpk, ge = min(G, gb + gpk);
+
+  // rows of the RT tiles, already advanced to the wave's first group
+  const uint8_t* rows[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t off;
+    if (MODE == MODE_GATEUP)  // r even: gate rows, r odd: up rows, of features tile*16 .. +16 (RT == 2)
+      off = (r & 1) * gu_bytes + ((int64_t)tile * 16 + i16) * row_bytes;
+    else
+      off = 2 * gu_bytes + (((int64_t)tile * RT + r) * 16 + i16) * row_bytes;
+    rows[r] = bank + off + (int64_t)gb * BB;
+  }
+
+  // weight prefetch starts before the activations are staged
+  u32x3 ring[D][RT];
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (GW > 0 ? j < GW : gb + j < ge)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * BB, q);
+  }
+
+  __syncthreads();  // the previous unit is done with the staging buffer
+  stage_rows<FMT, MODE>(a, it, xs, K);
+  __syncthreads();
+
+  f32x4 acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // rows past the item's tokens read its last row; their results are dropped
+  const char* arow = xs + min(i16, it.n - 1) * stage_stride(K) + q * 16 + gb * 256;
+
+  auto step = [&](int i, u32x3 (&cur)[RT]) {
+    u32x4 A[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) A[m] = *(const u32x4*)(arow + i * 256 + m * 64);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      u32x4 W[4];
+      const float s = decode_block_x3<FMT>(cur[r], lut, lane, W);
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
+      acc[r] += s * tmp;
+    }
+  };
+
+  if (active) {
+    if (GW > 0) {
+#pragma unroll
+      for (int i = 0; i < (GW > 0 ? GW : 1); ++i) {
+        u32x3 cur[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) cur[r] = ring[i % D][r];
+        if (i + D < GW)
+#pragma unroll
+          for (int r = 0; r < RT; ++r) ring[i % D][r] = load_block_x3<FMT>(rows[r] + (i + D) * BB, q);
+        step(i, cur);
+      }
+    } else {
+      const int n = ge - gb;
+      for (int i0 = 0; i0 < n; i0 += D) {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          const int i = i0 + j;
+          if (i >= n) break;
+          u32x3 cur[RT];
+#pragma unroll
+          for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
+          if (i + D < n)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + (int64_t)(i + D) * BB, q);
+          step(i, cur);
+        }
+      }
+    }
+  }
+
+  if (KS > 1) {
+    const int tl = wave / KS;
+    if (ks > 0) {
+#pragma unroll
+      for (int r = 0; r < RT; ++r) red[((tl * (KS - 1) + ks - 1) * RT + r) * 64 + lane] = acc[r];
+    }
+    __syncthreads();
+    if (ks == 0) {
+#pragma unroll
+      for (int w = 1; w < KS; ++w)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] += red[((tl * (KS - 1) + w - 1) * RT + r) * 64 + lane];
+    }
+    __syncthreads();  // red is reused by the block's next unit
+    if (ks > 0) return;
+  }
+  if (!active) return;
+
+  // lane holds positions it.pos + 4q + j, column i16 of each tile; the
+  // operands encode 2t, hence the 0.5
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ti = 4 * q + j;
+    if (ti >= it.n) continue;
+    const int64_t p = it.pos + ti;
+    if (MODE == MODE_GATEUP) {
+      const float g = 0.5f * acc[0][j], u = 0.5f * acc[1][j];
+      const float hv = g / (1.f + __expf(-g)) * u;
+      a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
+    } else {
+      int64_t slot;
+      float wgt;
+      if (p < a.Tk) {
+        slot = a.perm[p];
+        wgt = a.topk_w[slot];
+      } else {
+        slot = p;
+        wgt = 1.f;
+      }
+      wgt *= 0.5f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
+        a.slots[slot * a.d + row] = (uint16_t)f32_to_bf16(wgt * acc[r][j]);
+      }
+    }
+  }
+}
+
+// Epilogue of one tile: lane holds positions it.pos + 4q + j, column i16 of
+// each of the RT row tiles; the operands encode 2t, hence the 0.5.
+template <int MODE, int RT>
+__device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& it, int tile, int lane,
+                                              const f32x4 (&acc)[RT]) {
+  const int i16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ti = 4 * q + j;
+    if (ti >= it.n) continue;
+    const int64_t p = it.pos + ti;
+    if (MODE == MODE_GATEUP) {
+      const float g = 0.5f * acc[0][j], u = 0.5f * acc[1][j];
+      const float hv = g / (1.f + __expf(-g)) * u;
+      a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
+    } else {
+      int64_t slot;
+      float wgt;
+      if (p < a.Tk) {
+        slot = a.perm[p];
+        wgt = a.topk_w[slot];
+      } else {
+        slot = p;
+        wgt = 1.f;
+      }
+      wgt *= 0.5f;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
+        a.slots[slot * a.d + row] = (uint16_t)f32_to_bf16(wgt * acc[r][j]);
+      }
+    }
+  }
+}
+
+// Streaming unit: the item's tiles [tile0, tile_end); wave w takes tiles
+// tile0 + w, tile0 + w + WPB, ...  and streams them back to back through one
+// prefetch ring of D groups (D divides the compile-time group count G), so the
+// loads for the next tile are in flight while the current one finishes.
+template <int FMT, int MODE, int WPB, int RT, int D, int G>
+__device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const Item& it, int tile0, int tile_end,
+                                                   const u32x2* lut, char* xs) {
+  static_assert(G % D == 0 && D <= G, "the ring depth must divide the group count");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  constexpr int K = G * kGroup;
+  constexpr int BB = block_bytes_c<FMT>();
+  constexpr int64_t row_bytes = (int64_t)G * BB;
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
+  constexpr int rows_per_tile = MODE == MODE_GATEUP ? 16 : 16 * RT;
+  constexpr int64_t tile_stride = (int64_t)rows_per_tile * row_bytes * WPB;  // to the wave's next tile
+
+  const int first = tile0 + wave;
+  const int ntw = first < tile_end ? (tile_end - first + WPB - 1) / WPB : 0;
+
+  const uint8_t* rows[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int64_t off;
+    if (MODE == MODE_GATEUP)  // r even: gate rows, r odd: up rows (RT == 2)
+      off = (r & 1) * gu_bytes + ((int64_t)first * 16 + i16) * row_bytes;
+    else
+      off = 2 * gu_bytes + (((int64_t)first * RT + r) * 16 + i16) * row_bytes;
+    rows[r] = bank + off;
+  }
+
+  u32x3 ring[D][RT];
+  if (ntw > 0) {
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * BB, q);
+  }
+
+  __syncthreads();  // the previous unit is done with the staging buffer
+  stage_rows<FMT, MODE>(a, it, xs, K);
+  __syncthreads();
+
+  const char* arow = xs + min(i16, it.n - 1) * stage_stride(K) + q * 16;
+  for (int t = 0; t < ntw; ++t) {
+    const bool more = t + 1 < ntw;
+    f32x4 acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int g0 = 0; g0 < G; g0 += D) {
+      // the next D groups: the rest of this tile, else the start of the next one
+      const bool same = g0 + D < G;
+      const bool issue = same || more;
+      const uint8_t* nxt[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r) nxt[r] = same ? rows[r] + (g0 + D) * BB : rows[r] + tile_stride;
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        u32x3 cur[RT];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
+        if (issue) {
+#pragma unroll
+          for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(nxt[r] + j * BB, q);
+        }
+        u32x4 A[4];
+        const char* ap = arow + (g0 + j) * 256;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A[m] = *(const u32x4*)(ap + m * 64);
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+          u32x4 W[4];
+          const float s = decode_block_x3<FMT>(cur[r], lut, lane, W);
+          f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
+          acc[r] += s * tmp;
+        }
+      }
+    }
+    tile_epilogue<MODE, RT>(a, it, first + WPB * t, lane, acc);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) rows[r] += tile_stride;
+  }
+}
+
+template <int MODE, int WPB, int RT, int D, int G>
+__global__ __launch_bounds__(64 * WPB) void expert_stream_kernel(ExpertArgs a, int tiles_per_unit,
+                                                                   int units_per_item) {
+  extern __shared__ __align__(16) char smem[];
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  char* xs = smem + lut_bytes;
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
+  const int64_t units = (int64_t)(*a.n_items) * units_per_item;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const Item it = a.items[u / units_per_item];
+    const int tile0 = (int)(u % units_per_item) * tiles_per_unit;
+    const int tile_end = min(n_tiles, tile0 + tiles_per_unit);
+    if (a.formats[it.bank] == kPTQ1)
+      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
+    else
+      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
+  }
+}
+
+// Persistent blocks over units (item, tile block).
+// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][staged rows][KS reduction]
+template <int MODE, int WPB, int KS, int RT, int D, int GW>
+__global__ __launch_bounds__(64 * WPB) void expert_dec_kernel(ExpertArgs a, int tblocks_per_item) {
+  extern __shared__ __align__(16) char smem[];
+  const int K = MODE == MODE_GATEUP ? a.d : a.f;
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  char* xs = smem + lut_bytes;
+  f32x4* red = (f32x4*)(xs + a.nmax * stage_stride(K));
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  const int64_t units = (int64_t)(*a.n_items) * tblocks_per_item;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const Item it = a.items[u / tblocks_per_item];
+    const int tb = (int)(u % tblocks_per_item);
+    if (a.formats[it.bank] == kPTQ1)
+      expert_unit<kPTQ1, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red);
+    else
+      expert_unit<kPQ2, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red);
+  }
+}
+
+static int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <int MODE, int WPB, int KS, int RT, int D, int GW>
+static hipError_t launch_dec(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  const int K = MODE == MODE_GATEUP ? a.d : a.f;
+  const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
+  constexpr int TPB = WPB / KS;
+  const int tbpi = (n_tiles + TPB - 1) / TPB;
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
+                     (KS > 1 ? (size_t)TPB * (KS - 1) * RT * 64 * 16 : 0);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = expert_dec_kernel<MODE, WPB, KS, RT, D, GW>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WPB, lds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t grid = std::min<int64_t>((int64_t)cu_count() * per_cu, max_items * tbpi);
+  kern<<<dim3((unsigned)grid), 64 * WPB, lds, stream>>>(a, tbpi);
+  return hipGetLastError();
+}
+
+// Expected number of work items (the exact count is only known on the device):
+// touched routed experts plus extra 16-token chunks, plus the shared experts.
+// (A low estimate: splitting work too finely costs less than idle blocks.)
+static double expected_items(const ExpertArgs& a) {
+  const double slots = (double)a.T * a.k;
+  const double touched = a.E * (1.0 - std::exp(-slots / a.E));
+  return std::max(touched, slots / kChunk) + (double)a.S * ((a.T + kChunk - 1) / kChunk);
+}
+
+template <int MODE, int WPB, int RT, int D, int G>
+static hipError_t launch_stream(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  constexpr int K = G * kGroup;
+  const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = expert_stream_kernel<MODE, WPB, RT, D, G>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WPB, lds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t blocks = (int64_t)cu_count() * per_cu;
+  // tiles per wave per unit: balance ceil(units / blocks) rounds of (tpw + 1)
+  // tile-times (one tile-time for the unit's staging bubble)
+  const double items = std::min<double>((double)max_items, expected_items(a));
+  const int max_tpw = (n_tiles + WPB - 1) / WPB;
+  int best_tpw = 1;
+  double best = 1e30;
+  for (int tpw = 1; tpw <= max_tpw; ++tpw) {
+    const int tpu = tpw * WPB;
+    const double units = items * ((n_tiles + tpu - 1) / tpu);
+    const double cost = std::ceil(units / blocks) * (tpw + 1);
+    if (cost < best) {
+      best = cost;
+      best_tpw = tpw;
+    }
+  }
+  const int tpu = best_tpw * WPB;
+  const int upi = (n_tiles + tpu - 1) / tpu;
+  const int64_t grid = std::min<int64_t>(blocks, max_items * upi);
+  kern<<<dim3((unsigned)grid), 64 * WPB, lds, stream>>>(a, tpu, upi);
+  return hipGetLastError();
+}
+
+// Shapes with a compile-time group count stream; others take the generic loop.
+//   gate/up: K = d;  down: K = f.  Few tokens: K split over KS waves per tile.
+static hipError_t launch_gateup(const ExpertArgs& a, int64_t mi, bool small, hipStream_t s) {
+  const int G = a.d / kGroup;
+  if (small) {
+    switch (G) {
+      case 24: return launch_dec<MODE_GATEUP, 8, 4, 2, 6, 6>(a, mi, s);
+      case 16: return launch_dec<MODE_GATEUP, 8, 4, 2, 4, 4>(a, mi, s);
+      case 2: return launch_dec<MODE_GATEUP, 8, 2, 2, 1, 1>(a, mi, s);
+      default: return launch_dec<MODE_GATEUP, 8, 4, 2, 4, 0>(a, mi, s);
+    }
+  }
+  switch (G) {
+    case 24: return launch_stream<MODE_GATEUP, 8, 2, 8, 24>(a, mi, s);
+    case 16: return launch_stream<MODE_GATEUP, 8, 2, 8, 16>(a, mi, s);
+    case 2: return launch_stream<MODE_GATEUP, 8, 2, 2, 2>(a, mi, s);
+    default: return launch_dec<MODE_GATEUP, 8, 1, 2, 8, 0>(a, mi, s);
+  }
+}
+
+static hipError_t launch_down(const ExpertArgs& a, int64_t mi, bool small, hipStream_t s) {
+  const int G = a.f / kGroup;
+  if (small) {
+    switch (G) {
+      case 8: return launch_dec<MODE_DOWN, 8, 2, 2, 4, 4>(a, mi, s);
+      case 6: return launch_dec<MODE_DOWN, 8, 2, 2, 3, 3>(a, mi, s);
+      case 4: return launch_dec<MODE_DOWN, 8, 2, 2, 2, 2>(a, mi, s);
+      case 1: return launch_dec<MODE_DOWN, 8, 1, 2, 1, 1>(a, mi, s);
+      default: return launch_dec<MODE_DOWN, 8, 2, 2, 4, 0>(a, mi, s);
+    }
+  }
+  switch (G) {
+    case 8: return launch_stream<MODE_DOWN, 8, 4, 4, 8>(a, mi, s);
+    case 6: return launch_stream<MODE_DOWN, 8, 4, 3, 6>(a, mi, s);
+    case 4: return launch_stream<MODE_DOWN, 8, 4, 4, 4>(a, mi, s);
+    case 1: return launch_stream<MODE_DOWN, 8, 4, 1, 1>(a, mi, s);
+    default: return launch_dec<MODE_DOWN, 8, 1, 4, 4, 0>(a, mi, s);
+  }
+}
+
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream, void** ev) {
+  if (max_items <= 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  const bool small = a.T <= 4;
+  if (ev) e = hipEventRecord((hipEvent_t)ev[4], stream);
+  if (e == hipSuccess) e = launch_gateup(a, max_items, small, stream);
+  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[5], stream);
+  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[6], stream);
+  if (e == hipSuccess) e = launch_down(a, max_items, small, stream);
+  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[7], stream);
+  return e;
+}
+
+}  // namespace moe

@@ -72,6 +72,8 @@ struct ExpertArgs {
   const uint16_t* x;   // bf16 [T x d]
   uint16_t* h;         // bf16 [(Tk + S*T) x f]
   uint16_t* slots;     // bf16 [(Tk + S*T) x d]
+  int nmax;            // most tokens any work item holds (<= kChunk)
+  int fmt_mask;        // 1: some bank is PQ2_0, 2: some bank is PTQ1_0
 };
 
 hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
@@ -79,6 +81,7 @@ hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, 
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream);
-hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream);
+// stage_events: NULL or the caller's events; [4..7] bracket gate/up and down.
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream, void** stage_events);
 
 }  // namespace moe

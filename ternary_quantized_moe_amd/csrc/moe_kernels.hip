@@ -38,12 +38,24 @@ __global__ __launch_bounds__(64) void unpack_device_kernel(const uint8_t* __rest
     __syncthreads();
   }
   const int r = lane & 15, q = lane >> 4;
-  const int64_t b = (int64_t)blockIdx.x * 16 + r;
-  if (b >= n_blocks) return;
+  const int64_t b = (int64_t)blockIdx.x * 16 + min<int64_t>(r, n_blocks - 1 - (int64_t)blockIdx.x * 16);
   const uint8_t* blk = src + b * block_bytes_c<FMT>();
+  const uint8_t* end = src + n_blocks * block_bytes_c<FMT>();
+  // the same 12-byte read the expert kernels make, byte by byte where it would
+  // pass the end of the container (this entry point promises no slack)
+  const uint8_t* p = blk + (FMT == kPQ2 ? 8 : 6) * q;
+  u32x3 v;
+  if (p + 12 <= end) {
+    v = load_block_x3<FMT>(blk, q);
+  } else {
+    uint32_t w[3] = {0u, 0u, 0u};
+    for (int i = 0; i < 12; ++i)
+      if (p + i < end) w[i >> 2] |= (uint32_t)p[i] << (8 * (i & 3));
+    v = u32x3{w[0], w[1], w[2]};
+  }
   u32x4 W[4];
-  float s = load_decode_block<FMT>(blk, lut, lane % kLutCopies, q, W);
-  (void)s;
+  (void)decode_block_x3<FMT>(v, lut, lane, W);  // all lanes take part in the cross-lane read
+  if ((int64_t)blockIdx.x * 16 + r >= n_blocks) return;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
 #pragma unroll
@@ -364,182 +376,6 @@ hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t strea
   scan_kernel<<<1, 1024, 0, stream>>>(a, nb);
   scatter_kernel<<<(unsigned)((a.T * a.k + 255) / 256), 256, 0, stream>>>(a);
   return hipGetLastError();
-}
-
-// ============================================================ grouped experts
-// Work item = (bank, up to 16 tokens).  Lane l feeds token l%16 as the A
-// operand (activations, held in registers for the wave's K range) and weight
-// row l%16 of each 16-row tile as the B operand (decoded in registers); the KS
-// waves of a block split K and reduce through LDS.
-constexpr int MODE_GATEUP = 0;
-constexpr int MODE_DOWN = 1;
-
-template <int FMT, int MODE, int NG, int KS, int RT>
-__device__ __forceinline__ void expert_tile(const ExpertArgs& a, const Item& it, int tile,
-                                            const u32x2* lut, f32x4 (*red)[RT][64]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, q = lane >> 4;
-  const int K = MODE == MODE_GATEUP ? a.d : a.f;
-  const int G = K / kGroup;
-  const int BB = block_bytes_c<FMT>();
-  const int64_t row_bytes = (int64_t)G * BB;
-  const uint8_t* bank = a.banks + a.offsets[it.bank];
-  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;  // one gate or up matrix
-
-  // activation row of this lane's token
-  const uint16_t* arow = nullptr;
-  if (i16 < it.n) {
-    const int64_t p = it.pos + i16;
-    if (MODE == MODE_GATEUP) {
-      const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
-      arow = a.x + tok * a.d;
-    } else {
-      arow = a.h + p * a.f;
-    }
-  }
-
-  const int g0 = wave * NG;
-  u32x4 A[NG][4];
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int g = g0 + gi;
-    if (arow && g < G) {
-      if (FMT == kPQ2)
-        load_act_pq2(arow, g, q, A[gi]);
-      else
-        load_act_ptq1(arow, g, q, A[gi]);
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) A[gi][m] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  // weight rows of the RT tiles
-  const uint8_t* rows[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) {
-    if (MODE == MODE_GATEUP) {
-      // r = 0: gate rows, r = 1: up rows (same features)
-      const int64_t row = (int64_t)tile * 16 + i16;
-      rows[r] = bank + (r == 0 ? 0 : gu_bytes) + row * row_bytes;
-    } else {
-      const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
-      rows[r] = bank + 2 * gu_bytes + row * row_bytes;
-    }
-  }
-
-  f32x4 acc[RT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int copy = lane % kLutCopies;
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int g = g0 + gi;
-    if (g >= G) break;
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      u32x4 W[4];
-      const float s = load_decode_block<FMT>(rows[r] + (int64_t)g * BB, lut, copy, q, W);
-      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 4; ++m) tmp = mfma16(A[gi][m], W[m], tmp);
-      acc[r] += s * tmp;
-    }
-  }
-
-  if (KS > 1) {
-    if (wave > 0) {
-#pragma unroll
-      for (int r = 0; r < RT; ++r) red[wave - 1][r][lane] = acc[r];
-    }
-    __syncthreads();
-    if (wave > 0) return;
-#pragma unroll
-    for (int w = 0; w < KS - 1; ++w)
-#pragma unroll
-      for (int r = 0; r < RT; ++r) acc[r] += red[w][r][lane];
-  }
-
-  // lane holds tokens 4q + j of the item, column i16 of each tile
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int ti = 4 * q + j;
-    if (ti >= it.n) continue;
-    const int64_t p = it.pos + ti;
-    if (MODE == MODE_GATEUP) {
-      const float g = acc[0][j], u = acc[1][j];
-      const float hv = g / (1.f + __expf(-g)) * u;
-      a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
-    } else {
-      int64_t slot;
-      float wgt;
-      if (p < a.Tk) {
-        slot = a.perm[p];
-        wgt = a.topk_w[slot];
-      } else {
-        slot = p;
-        wgt = 1.f;
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
-        const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
-        a.slots[slot * a.d + row] = (uint16_t)f32_to_bf16(wgt * acc[r][j]);
-      }
-    }
-  }
-}
-
-template <int MODE, int NG, int KS, int RT>
-__global__ __launch_bounds__(64 * KS) void expert_kernel(ExpertArgs a) {
-  __shared__ u32x2 lut[256 * kLutCopies];
-  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][RT][64];
-  if ((int)blockIdx.y >= *a.n_items) return;
-  const Item it = a.items[blockIdx.y];
-  const int fmt = a.formats[it.bank];
-  if (fmt == kPTQ1) {
-    ptq1_lut_fill(lut, threadIdx.x, 64 * KS);
-    __syncthreads();
-    expert_tile<kPTQ1, MODE, NG, KS, RT>(a, it, blockIdx.x, lut, red);
-  } else {
-    expert_tile<kPQ2, MODE, NG, KS, RT>(a, it, blockIdx.x, lut, red);
-  }
-}
-
-template <int MODE, int NG, int RT>
-static void launch_ng(const ExpertArgs& a, dim3 grid, int ks, hipStream_t stream) {
-  switch (ks) {
-    case 1: expert_kernel<MODE, NG, 1, RT><<<grid, 64, 0, stream>>>(a); break;
-    case 2: expert_kernel<MODE, NG, 2, RT><<<grid, 128, 0, stream>>>(a); break;
-    case 3: expert_kernel<MODE, NG, 3, RT><<<grid, 192, 0, stream>>>(a); break;
-    case 4: expert_kernel<MODE, NG, 4, RT><<<grid, 256, 0, stream>>>(a); break;
-    case 5: expert_kernel<MODE, NG, 5, RT><<<grid, 320, 0, stream>>>(a); break;
-    case 6: expert_kernel<MODE, NG, 6, RT><<<grid, 384, 0, stream>>>(a); break;
-    case 7: expert_kernel<MODE, NG, 7, RT><<<grid, 448, 0, stream>>>(a); break;
-    default: expert_kernel<MODE, NG, 8, RT><<<grid, 512, 0, stream>>>(a); break;
-  }
-}
-
-// NG groups per wave (the smallest supported NG >= G/8), KS = ceil(G / NG) waves.
-template <int MODE, int RT>
-static hipError_t launch_expert_mode(const ExpertArgs& a, int64_t max_items, int tiles, int G,
-                                     hipStream_t stream) {
-  dim3 grid((unsigned)tiles, (unsigned)max_items);
-  const int need = (G + 7) / 8;
-  if (need <= 1) launch_ng<MODE, 1, RT>(a, grid, G, stream);
-  else if (need <= 2) launch_ng<MODE, 2, RT>(a, grid, (G + 1) / 2, stream);
-  else if (need <= 3) launch_ng<MODE, 3, RT>(a, grid, (G + 2) / 3, stream);
-  else if (need <= 4) launch_ng<MODE, 4, RT>(a, grid, (G + 3) / 4, stream);
-  else if (need <= 6) launch_ng<MODE, 6, RT>(a, grid, (G + 5) / 6, stream);
-  else if (need <= 8) launch_ng<MODE, 8, RT>(a, grid, (G + 7) / 8, stream);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
-  if (max_items <= 0) return hipSuccess;
-  hipError_t e = launch_expert_mode<MODE_GATEUP, 2>(a, max_items, a.f / 16, a.d / kGroup, stream);
-  if (e != hipSuccess) return e;
-  return launch_expert_mode<MODE_DOWN, 2>(a, max_items, a.d / 32, a.f / kGroup, stream);
 }
 
 }  // namespace moe

@@ -8,6 +8,8 @@ import numpy as np
 
 from .binding import pack, packed_bytes
 
+BANK_SLACK = 16  # readable bytes the library needs after the last bank (MOE_BANK_SLACK)
+
 
 def pack_expert(fmt: int, trits, scales) -> np.ndarray:
     """[gate, up, down] trits and fp16-bit scales -> one bank's container bytes."""
@@ -16,11 +18,12 @@ def pack_expert(fmt: int, trits, scales) -> np.ndarray:
 
 def build_banks(source, n_banks: int, formats: np.ndarray, d_model: int, d_ff: int, threads: int = 0):
     """Pack every bank back to back.  source(e) -> ([gate, up, down] trits,
-    [gate, up, down] fp16 scale bits).  Returns (data uint8, offsets int64)."""
+    [gate, up, down] fp16 scale bits).  Returns (data uint8, offsets int64); data
+    ends with BANK_SLACK zero bytes."""
     sizes = [3 * packed_bytes(int(formats[e]), d_model * d_ff) for e in range(n_banks)]
     offsets = np.zeros(n_banks, dtype=np.int64)
     offsets[1:] = np.cumsum(sizes)[:-1]
-    data = np.empty(int(sum(sizes)), dtype=np.uint8)
+    data = np.zeros(int(sum(sizes)) + BANK_SLACK, dtype=np.uint8)
 
     def one(e):
         trits, scales = source(e)

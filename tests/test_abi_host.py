@@ -116,7 +116,7 @@ def _fake_banks(d=256, f=128, E=8, S=0, fmts=None, offsets=None, nbytes=None):
     size = 3 * d * f // 128 * 34
     offsets = np.arange(E + S, dtype=np.int64) * size if offsets is None else np.asarray(offsets, np.int64)
     keep = (fmts, offsets)
-    c = binding.ExpertBanksC(d, f, E, S, 0x1000, nbytes if nbytes is not None else size * (E + S), 0x2000,
+    c = binding.ExpertBanksC(d, f, E, S, 0x1000, nbytes if nbytes is not None else size * (E + S) + 16, 0x2000,
                              0x3000, offsets.ctypes.data, fmts.ctypes.data)
     return c, keep
 
@@ -146,6 +146,8 @@ def test_forward_validation_happens_before_launch():
     assert "bank 7" in L.moe_last_error().decode()
     c4, keep4 = _fake_banks(nbytes=100)
     assert _forward_rc(c4) == -6
+    c6, keep6 = _fake_banks(nbytes=8 * 3 * 256 * 128 // 128 * 34 + 15)  # one byte short of the slack
+    assert _forward_rc(c6) == -6 and "slack" in L.moe_last_error().decode()
     c5, keep5 = _fake_banks(offsets=np.arange(8) * 2)
     assert _forward_rc(c5) == -1                      # offsets not multiples of 4
     assert L.moe_workspace_bytes(ctypes.byref(c), 16, 2, 16) > 0
