@@ -172,7 +172,8 @@ int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t 
 /* Measurement hook.  With events != NULL (n_events >= 2 * MOE_N_STAGES
  * hipEvent_t handles created by the caller), every later moe_ternary_forward
  * call on this thread records events[2s] before and events[2s+1] after stage s
- * on the call's stream; NULL (or n_events = 0) turns recording off.  Stages:
+ * on the call's stream (a NULL entry skips that record); NULL events (or
+ * n_events = 0) turn recording off.  Stages:
  * 0 router/correction projection, 1 routing (top-k, ranking, scan, scatter),
  * 2 gate/up experts, 3 down experts, 4 combine.  The library keeps the pointer
  * until it is replaced; the caller keeps the events alive meanwhile. */

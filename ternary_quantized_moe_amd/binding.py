@@ -254,14 +254,20 @@ class StageTimer:
     recorded on the call's stream.  `ms()` synchronises and returns the mean
     duration per stage over the recorded steps."""
 
-    def __init__(self, n_steps: int):
+    def __init__(self, n_steps: int, stages=None):
+        """stages: indices of the stages to time (default: all); the others
+        record nothing, which keeps the timed stream free of extra markers."""
         import torch
-        self._ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * N_STAGES)] for _ in range(n_steps)]
+        self.stages = list(range(N_STAGES)) if stages is None else list(stages)
+        self._ev = [[torch.cuda.Event(enable_timing=True) if (i // 2) in self.stages else None
+                     for i in range(2 * N_STAGES)] for _ in range(n_steps)]
         for evs in self._ev:          # torch creates the HIP event on first record
             for e in evs:
-                e.record()
+                if e is not None:
+                    e.record()
         torch.cuda.synchronize()
-        self._arr = [(ctypes.c_void_p * (2 * N_STAGES))(*[e.cuda_event for e in evs]) for evs in self._ev]
+        self._arr = [(ctypes.c_void_p * (2 * N_STAGES))(*[e.cuda_event if e is not None else None for e in evs])
+                     for evs in self._ev]
         self._i = 0
 
     def step(self):
@@ -279,8 +285,7 @@ class StageTimer:
     def ms(self):
         import torch
         torch.cuda.synchronize()
-        out = np.zeros(N_STAGES)
-        for evs in self._ev[: self._i]:
-            for s in range(N_STAGES):
-                out[s] += evs[2 * s].elapsed_time(evs[2 * s + 1])
+        out = np.full(N_STAGES, np.nan)
+        for s in self.stages:
+            out[s] = sum(evs[2 * s].elapsed_time(evs[2 * s + 1]) for evs in self._ev[: self._i])
         return out / max(self._i, 1)

@@ -22,7 +22,8 @@ thread_local void** g_stage_events = nullptr;
 // Record the stage's start (end=false) or end event if measurement is on.
 hipError_t stage_mark(int stage, bool end, hipStream_t st) {
   if (!g_stage_events) return hipSuccess;
-  return hipEventRecord((hipEvent_t)g_stage_events[2 * stage + (end ? 1 : 0)], st);
+  hipEvent_t ev = (hipEvent_t)g_stage_events[2 * stage + (end ? 1 : 0)];
+  return ev ? hipEventRecord(ev, st) : hipSuccess;
 }
 
 int32_t fail(int32_t code, const char* fmt, ...) {

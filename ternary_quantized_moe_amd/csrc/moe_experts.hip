@@ -322,6 +322,9 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
           for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
           acc[r] += s * tmp;
         }
+        // keep each step's loads and decode in place: hoisting the ring's
+        // refills would double the registers the ring needs
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     tile_epilogue<MODE, RT>(a, it, first + WPB * t, lane, acc);
@@ -330,9 +333,11 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
   }
 }
 
-template <int MODE, int WPB, int RT, int D, int G>
-__global__ __launch_bounds__(64 * WPB) void expert_stream_kernel(ExpertArgs a, int tiles_per_unit,
-                                                                   int units_per_item) {
+// FS: container formats the kernel handles (1: PQ2_0, 2: PTQ1_0, 3: both), so a
+// single-format layer does not pay for the other decoder's registers.
+template <int MODE, int WPB, int RT, int D, int G, int FS, int WPE>
+__global__ __launch_bounds__(64 * WPB) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) {
   extern __shared__ __align__(16) char smem[];
   const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
   u32x2* lut = (u32x2*)smem;
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(64 * WPB) void expert_stream_kernel(ExpertArgs a, i
     const Item it = a.items[u / units_per_item];
     const int tile0 = (int)(u % units_per_item) * tiles_per_unit;
     const int tile_end = min(n_tiles, tile0 + tiles_per_unit);
-    if (a.formats[it.bank] == kPTQ1)
+    if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
       expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
     else
       expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
@@ -411,13 +416,13 @@ static double expected_items(const ExpertArgs& a) {
   return std::max(touched, slots / kChunk) + (double)a.S * ((a.T + kChunk - 1) / kChunk);
 }
 
-template <int MODE, int WPB, int RT, int D, int G>
-static hipError_t launch_stream(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+template <int MODE, int WPB, int RT, int D, int G, int FS, int WPE>
+static hipError_t launch_stream_fs(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
   constexpr int K = G * kGroup;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kern = expert_stream_kernel<MODE, WPB, RT, D, G>;
+  auto kern = expert_stream_kernel<MODE, WPB, RT, D, G, FS, WPE>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WPB, lds);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
@@ -442,6 +447,15 @@ static hipError_t launch_stream(const ExpertArgs& a, int64_t max_items, hipStrea
   const int64_t grid = std::min<int64_t>(blocks, max_items * upi);
   kern<<<dim3((unsigned)grid), 64 * WPB, lds, stream>>>(a, tpu, upi);
   return hipGetLastError();
+}
+
+// WPE: waves per SIMD the kernel is built for (1: up to 512 registers per
+// wave, so the prefetch ring can hold a whole tile of loads).
+template <int MODE, int WPB, int RT, int D, int G, int WPE = 2>
+static hipError_t launch_stream(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  if (a.fmt_mask == 1) return launch_stream_fs<MODE, WPB, RT, D, G, 1, WPE>(a, max_items, stream);
+  if (a.fmt_mask == 2) return launch_stream_fs<MODE, WPB, RT, D, G, 2, WPE>(a, max_items, stream);
+  return launch_stream_fs<MODE, WPB, RT, D, G, 3, WPE>(a, max_items, stream);
 }
 
 // Shapes with a compile-time group count stream; others take the generic loop.
@@ -488,12 +502,13 @@ hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t st
   if (max_items <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   const bool small = a.T <= 4;
-  if (ev) e = hipEventRecord((hipEvent_t)ev[4], stream);
+  auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], stream) : hipSuccess; };
+  e = mark(4);
   if (e == hipSuccess) e = launch_gateup(a, max_items, small, stream);
-  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[5], stream);
-  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[6], stream);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess) e = launch_down(a, max_items, small, stream);
-  if (e == hipSuccess && ev) e = hipEventRecord((hipEvent_t)ev[7], stream);
+  if (e == hipSuccess) e = mark(7);
   return e;
 }
 

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -114,110 +116,149 @@ __device__ __forceinline__ void split_sum_f16x8(u32x4 w, u32x4 v, u32x4& hi, u32
   }
 }
 
-template <int EPI, int KS>
+// Block = one 16-row tile x up to MT*16 tokens; its KS waves split K in
+// 32-wide steps and reduce through LDS.  Each weight k-step is split into bf16
+// hi/lo once and reused for all MT token tiles.
+template <int EPI, int KS, int MT>
 __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
-  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][64];
+  __shared__ f32x4 red[KS > 1 ? KS - 1 : 1][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
-  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const int64_t t0 = (int64_t)blockIdx.y * 16 * MT;
   const int n0 = blockIdx.x * 16;
   const int N = a.N0 + a.N1;
-  const int64_t t = t0 + i16;
   const int n = n0 + i16;
 
   const int nsteps = (a.K + 31) / 32;
   const int spw = (nsteps + KS - 1) / KS;
   const int s_begin = wave * spw, s_end = min(nsteps, s_begin + spw);
 
-  const uint16_t* arow = t < a.T ? a.act + t * a.lda : nullptr;
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = t0 + 16 * m + i16;
+    arow[m] = t < a.T ? a.act + t * a.lda : nullptr;
+  }
   const uint16_t* wrow = nullptr;
   const uint16_t* wrowb = nullptr;
-  bool summed = false;
   if (n < a.N0) {
     wrow = a.w0 + (int64_t)n * a.K;
-    if (a.w0b) {
-      wrowb = a.w0b + (int64_t)n * a.K;
-      summed = true;
-    }
+    if (a.w0b) wrowb = a.w0b + (int64_t)n * a.K;
   } else if (n < N) {
     wrow = a.w1 + (int64_t)(n - a.N0) * a.K;
   }
+  const bool summed = a.w0b != nullptr && n < a.N0;
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int s = s_begin; s < s_end; ++s) {
     const int kb = 32 * s + 8 * q;
     const bool kin = kb < a.K;
-    u32x4 av = {0u, 0u, 0u, 0u}, wv = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
-    if (arow && kin) av = *(const u32x4*)(arow + kb);
+    u32x4 wv = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
     if (wrow && kin) wv = *(const u32x4_a4*)(wrow + kb);
     if (summed && kin) wb = *(const u32x4_a4*)(wrowb + kb);
+    u32x4 av[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) av[m] = (arow[m] && kin) ? *(const u32x4*)(arow[m] + kb) : u32x4{0u, 0u, 0u, 0u};
     u32x4 hi, lo;
     if (summed)
       split_sum_f16x8(wv, wb, hi, lo);
     else
       split_f16x8(wv, hi, lo);
-    acc = mfma16(av, hi, acc);
-    acc = mfma16(av, lo, acc);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      acc[m] = mfma16(av[m], hi, acc[m]);
+      acc[m] = mfma16(av[m], lo, acc[m]);
+    }
   }
 
   if (KS > 1) {
-    if (wave > 0) red[wave - 1][lane] = acc;
+    if (wave > 0)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) red[wave - 1][m][lane] = acc[m];
     __syncthreads();
     if (wave > 0) return;
 #pragma unroll
-    for (int w = 0; w < KS - 1; ++w) acc += red[w][lane];
-  }
-
-  // lane holds tokens t0 + 4q + j, row n0 + i16
+    for (int w = 0; w < KS - 1; ++w)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t tt = t0 + 4 * q + j;
-    if (tt >= a.T || n >= N) continue;
-    if (EPI == EPI_XPROJ) {
-      if (n < a.N0)
-        a.logits[tt * a.N0 + n] = acc[j];
-      else
-        a.z[tt * a.N1 + (n - a.N0)] = (uint16_t)f32_to_bf16(acc[j]);
-    } else {
-      const int d = a.N0;
-      float v = acc[j];
-      const int64_t Tk = a.T * a.top_k;
-      for (int i = 0; i < a.top_k; ++i) v += bf16_to_f32(a.slots[(tt * a.top_k + i) * d + n]);
-      for (int sh = 0; sh < a.n_shared; ++sh) v += bf16_to_f32(a.slots[(Tk + sh * a.T + tt) * d + n]);
-      a.y[tt * d + n] = (uint16_t)f32_to_bf16(v);
+      for (int m = 0; m < MT; ++m) acc[m] += red[w][m][lane];
+  }
+  if (n >= N) return;
+
+  // lane holds tokens t0 + 16m + 4q + j, row n
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t tt = t0 + 16 * m + 4 * q + j;
+      if (tt >= a.T) continue;
+      if (EPI == EPI_XPROJ) {
+        if (n < a.N0)
+          a.logits[tt * a.N0 + n] = acc[m][j];
+        else
+          a.z[tt * a.N1 + (n - a.N0)] = (uint16_t)f32_to_bf16(acc[m][j]);
+      } else {
+        const int d = a.N0;
+        float v = acc[m][j];
+        const int64_t Tk = a.T * a.top_k;
+        for (int i = 0; i < a.top_k; ++i) v += bf16_to_f32(a.slots[(tt * a.top_k + i) * d + n]);
+        for (int sh = 0; sh < a.n_shared; ++sh) v += bf16_to_f32(a.slots[(Tk + sh * a.T + tt) * d + n]);
+        a.y[tt * d + n] = (uint16_t)f32_to_bf16(v);
+      }
     }
   }
 }
 
-hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
-  const int N = a.N0 + a.N1;
-  dim3 grid((unsigned)((N + 15) / 16), (unsigned)((a.T + 15) / 16));
-  dense_kernel<EPI_XPROJ, 8><<<grid, 512, 0, stream>>>(a);
+template <int EPI, int MT>
+static void launch_dense_mt(const DenseArgs& a, int N, hipStream_t stream) {
+  dim3 grid((unsigned)((N + 15) / 16), (unsigned)((a.T + 16 * MT - 1) / (16 * MT)));
+  const int steps = (a.K + 31) / 32;
+  // about 4 k-steps (128 inputs) per wave, at most 16 waves (8 with 4 token tiles)
+  const int ks = std::max(1, std::min(MT >= 4 ? 8 : 16, (steps + 3) / 4));
+  if (ks <= 1) dense_kernel<EPI, 1, MT><<<grid, 64, 0, stream>>>(a);
+  else if (ks <= 2) dense_kernel<EPI, 2, MT><<<grid, 128, 0, stream>>>(a);
+  else if (ks <= 4) dense_kernel<EPI, 4, MT><<<grid, 256, 0, stream>>>(a);
+  else if (ks <= 8 || MT >= 4) dense_kernel<EPI, 8, MT><<<grid, 512, 0, stream>>>(a);
+  else dense_kernel<EPI, MT >= 4 ? 8 : 16, MT><<<grid, 1024, 0, stream>>>(a);
+}
+
+// Small batches want many blocks (the projections read far more weight bytes
+// than activations), so one 16-token tile per block up to 256 tokens; larger
+// batches reuse each split weight step for four token tiles.
+template <int EPI>
+static hipError_t launch_dense(const DenseArgs& a, int N, hipStream_t stream) {
+  if (a.T <= 256)
+    launch_dense_mt<EPI, 1>(a, N, stream);
+  else
+    launch_dense_mt<EPI, 4>(a, N, stream);
   return hipGetLastError();
 }
 
+hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
+  return launch_dense<EPI_XPROJ>(a, a.N0 + a.N1, stream);
+}
+
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
-  dim3 grid((unsigned)((a.N0 + 15) / 16), (unsigned)((a.T + 15) / 16));
-  dense_kernel<EPI_COMBINE, 4><<<grid, 256, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_dense<EPI_COMBINE>(a, a.N0, stream);
 }
 
 // ============================================================ routing
 // One wave per token: k rounds of a wave-wide argmax over the E logits (larger
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
-constexpr int kMaxPerLane = kMaxExperts / 64;
 
+template <int PER>  // logits per lane: E <= 64 * PER
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   __shared__ float selv[4][kMaxExperts];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   const bool active = t < a.T;
   const int E = a.E, k = a.k;
-  float v[kMaxPerLane];
+  float v[PER];
   uint32_t avail = 0;
 #pragma unroll
-  for (int c = 0; c < kMaxPerLane; ++c) {
+  for (int c = 0; c < PER; ++c) {
     const int e = lane + 64 * c;
     v[c] = 0.f;
     if (active && e < E) {
@@ -229,7 +270,7 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
     float bv = 0.f;
     int be = 0x7fffffff;
 #pragma unroll
-    for (int c = 0; c < kMaxPerLane; ++c) {
+    for (int c = 0; c < PER; ++c) {
       if (!((avail >> c) & 1u)) continue;
       if (be == 0x7fffffff || v[c] > bv) {  // e grows with c, so ties keep the lower e
         bv = v[c];
@@ -368,13 +409,105 @@ __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
   a.perm[a.block_base[b * a.E + e] + a.slot_rank[s]] = (int)s;
 }
 
+// Grouping of a small batch (T <= kGroupMaxT) in one block, after top-k:
+// per-expert counts, offsets, ranks (ballot masks per 64-token chunk, the same
+// order rule as the multi-block path), permutation and work items.
+constexpr int kGroupMaxT = 256;
+
+__global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
+  __shared__ unsigned long long mask[kGroupMaxT / 64][kMaxExperts];
+  __shared__ int scan_buf[1024];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int E = a.E, k = a.k;
+  const int T = (int)a.T;
+  const int nchunks = (T + 63) / 64;
+  for (int i = threadIdx.x; i < nchunks * kMaxExperts; i += 1024) (&mask[0][0])[i] = 0ull;
+  __syncthreads();
+  if (wave < nchunks) {
+    const int t = 64 * wave + lane;
+    if (t < T)
+      for (int i = 0; i < k; ++i) atomicOr(&mask[wave][a.idx[(int64_t)t * k + i]], 1ull << lane);
+  }
+  __syncthreads();
+
+  const int e = threadIdx.x;
+  int total = 0;
+  if (e < E)
+    for (int c = 0; c < nchunks; ++c) total += __popcll(mask[c][e]);
+  scan_buf[e] = total;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? scan_buf[e - off] : 0;
+    __syncthreads();
+    scan_buf[e] += v;
+    __syncthreads();
+  }
+  const int off_e = scan_buf[e] - total;
+  if (e < E) {
+    a.counts[e] = total;
+    a.offsets[e] = off_e;
+  }
+  if (e == 0) a.offsets[E] = T * k;
+  __syncthreads();
+  const int chunks = e < E ? (total + kChunk - 1) / kChunk : 0;
+  scan_buf[e] = chunks;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = e >= off ? scan_buf[e - off] : 0;
+    __syncthreads();
+    scan_buf[e] += v;
+    __syncthreads();
+  }
+  const int istart = scan_buf[e] - chunks;
+  const int routed_items = scan_buf[1023];
+  for (int c = 0; c < chunks; ++c) {
+    Item it;
+    it.bank = e;
+    it.pos = off_e + c * kChunk;
+    it.n = min(kChunk, total - c * kChunk);
+    it.pad = 0;
+    a.items[istart + c] = it;
+  }
+  const int per_shared = (T + kChunk - 1) / kChunk;
+  for (int idx = e; idx < a.S * per_shared; idx += 1024) {
+    const int sh = idx / per_shared, c = idx % per_shared;
+    Item it;
+    it.bank = E + sh;
+    it.pos = T * k + sh * T + c * kChunk;
+    it.n = min(kChunk, T - c * kChunk);
+    it.pad = 0;
+    a.items[routed_items + idx] = it;
+  }
+  if (e == 0) *a.n_items = routed_items + a.S * per_shared;
+  __syncthreads();
+  scan_buf[e] = off_e;
+  __syncthreads();
+  for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
+    const int t = sl / k;
+    const int ex = a.idx[sl];
+    const int c = t >> 6, ln = t & 63;
+    int r = __popcll(mask[c][ex] & (ln == 0 ? 0ull : (~0ull >> (64 - ln))));
+    for (int cc = 0; cc < c; ++cc) r += __popcll(mask[cc][ex]);
+    a.perm[scan_buf[ex] + r] = sl;
+  }
+}
+
 hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream) {
   (void)max_items;
   const int nb = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
-  topk_kernel<<<(unsigned)((a.T + 3) / 4), 256, 0, stream>>>(a);
-  rank_kernel<<<nb, 256, 4 * a.E * sizeof(unsigned long long), stream>>>(a);
-  scan_kernel<<<1, 1024, 0, stream>>>(a, nb);
-  scatter_kernel<<<(unsigned)((a.T * a.k + 255) / 256), 256, 0, stream>>>(a);
+  const dim3 tg((unsigned)((a.T + 3) / 4));
+  if (a.E <= 64) topk_kernel<1><<<tg, 256, 0, stream>>>(a);
+  else if (a.E <= 128) topk_kernel<2><<<tg, 256, 0, stream>>>(a);
+  else if (a.E <= 256) topk_kernel<4><<<tg, 256, 0, stream>>>(a);
+  else if (a.E <= 512) topk_kernel<8><<<tg, 256, 0, stream>>>(a);
+  else topk_kernel<16><<<tg, 256, 0, stream>>>(a);
+  if (a.T <= kGroupMaxT) {
+    group_small_kernel<<<1, 1024, 0, stream>>>(a);
+  } else {
+    rank_kernel<<<nb, 256, 4 * a.E * sizeof(unsigned long long), stream>>>(a);
+    scan_kernel<<<1, 1024, 0, stream>>>(a, nb);
+    scatter_kernel<<<(unsigned)((a.T * a.k + 255) / 256), 256, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
