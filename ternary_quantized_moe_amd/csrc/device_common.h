@@ -192,6 +192,34 @@ __host__ __device__ constexpr int block_bytes_c() {
   return FMT == kPQ2 ? 34 : 28;
 }
 
+// ---------------------------------------------------------------- dense fp16 weights
+// Dense fp16 weight rows feed bf16 matrix cores as two bf16 terms (hi + lo).
+// fp16 x8 (4 dwords) -> exact bf16 hi/lo operand pairs (truncated hi).
+__device__ __forceinline__ void split_f16x8(u32x4 w, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = f16_to_f32(w[i] & 0xFFFFu), b = f16_to_f32(w[i] >> 16);
+    const uint32_t ha = __float_as_uint(a) & 0xFFFF0000u, hb = __float_as_uint(b) & 0xFFFF0000u;
+    const uint32_t la = __float_as_uint(a - __uint_as_float(ha)), lb = __float_as_uint(b - __uint_as_float(hb));
+    hi[i] = perm_b32(hb, ha, 0x07060302u);
+    lo[i] = perm_b32(lb, la, 0x07060302u);
+  }
+}
+
+// fp16 x8 from two sources summed in fp32 -> bf16 hi (round to nearest even) +
+// bf16 lo (round to nearest even); |error| <= 2^-18 |a + b|.
+__device__ __forceinline__ void split_sum_f16x8(u32x4 w, u32x4 v, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = f16_to_f32(w[i] & 0xFFFFu) + f16_to_f32(v[i] & 0xFFFFu);
+    const float b = f16_to_f32(w[i] >> 16) + f16_to_f32(v[i] >> 16);
+    const uint32_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
+    const uint32_t la = f32_to_bf16(a - bf16_to_f32(ha)), lb = f32_to_bf16(b - bf16_to_f32(hb));
+    hi[i] = ha | (hb << 16);
+    lo[i] = la | (lb << 16);
+  }
+}
+
 // ---------------------------------------------------------------- activations
 // Matrix-core A operands (bf16) for one row of activations and one group, in the
 // k-slot order of the container format.  The raw loads and the reordering are

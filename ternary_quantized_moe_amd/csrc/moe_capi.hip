@@ -11,7 +11,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/moe_ternary.h"
+#include "moe_ternary.h"
 #include "moe_internal.h"
 
 namespace {
@@ -60,7 +60,8 @@ int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t T, Tk, n_pos, nb, max_items;
-  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, h, slots;
+  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, h, slots;
+  bool large;
   int64_t route_end, total;
 };
 
@@ -70,8 +71,8 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
   p.Tk = T * k;
   p.n_pos = p.Tk + (int64_t)S * T;
   p.nb = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
-  p.max_items = p.Tk / moe::kChunk + std::min<int64_t>(E, p.Tk) +
-                (int64_t)S * ((T + moe::kChunk - 1) / moe::kChunk);
+  const int64_t C = moe::item_chunk(T);
+  p.max_items = p.Tk / C + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C - 1) / C);
   int64_t o = 0;
   p.logits = o; o += up(T * E * 4);
   p.idx = o; o += up(p.Tk * 4);
@@ -84,6 +85,10 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
   p.perm = o; o += up(p.Tk * 4);
   p.items = o; o += up(std::max<int64_t>(p.max_items, 1) * (int64_t)sizeof(moe::Item));
   p.nitems = o; o += up(4);
+  // large batches: split dense weights of the x-projection, later of the combine
+  p.large = T > moe::kGroupMaxT;
+  p.wsplit = o;
+  if (p.large) o += up(std::max(moe::dense_split_bytes(E + r, d), moe::dense_split_bytes(d, r)));
   p.route_end = o;
   p.z = o; o += up(T * (int64_t)r * 2);
   p.h = o; o += up(p.n_pos * f * 2);
@@ -308,6 +313,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.N1 = corr_A ? r : 0;
   da.logits = logits;
   da.z = at<uint16_t>(ws, p.z);
+  da.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
   hipError_t e = stage_mark(0, false, stream);
   if (e == hipSuccess) e = moe::launch_xproj(da, stream);
   if (e == hipSuccess) e = stage_mark(0, true, stream);
@@ -329,6 +335,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.perm = perm;
   ra.items = at<moe::Item>(ws, p.items);
   ra.n_items = at<int32_t>(ws, p.nitems);
+  ra.chunk = moe::item_chunk(T);
   e = stage_mark(1, false, stream);
   if (e == hipSuccess) e = moe::launch_route(ra, p.max_items, stream);
   if (e == hipSuccess) e = stage_mark(1, true, stream);
@@ -407,7 +414,8 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     ea.x = x;
     ea.h = at<uint16_t>(ws, p.h);
     ea.slots = at<uint16_t>(ws, p.slots);
-    ea.nmax = (int)std::min<int64_t>(T, moe::kChunk);
+    ea.chunk = moe::item_chunk(T);
+    ea.nmax = (int)std::min<int64_t>(T, ea.chunk);
     ea.fmt_mask = 0;
     for (int e = 0; e < E + S; ++e) ea.fmt_mask |= banks->formats_host[e] == MOE_PQ2_0 ? 1 : 2;
     hipError_t e = moe::launch_experts(ea, p.max_items, st, g_stage_events);
@@ -424,6 +432,7 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     ca.top_k = k;
     ca.n_shared = S;
     ca.y = y;
+    ca.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
     e = stage_mark(4, false, st);
     if (e == hipSuccess) e = moe::launch_combine(ca, st);
     if (e == hipSuccess) e = stage_mark(4, true, st);

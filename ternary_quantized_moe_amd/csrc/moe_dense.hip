@@ -1,0 +1,281 @@
+// Dense projections of large batches on the matrix cores:
+//   x-projection  logits = (W_r + dW_r) x (fp32) and z = A x (bf16)
+//   combine       y = B z + the token's expert slots (bf16)
+// Scion README "The idea" and "Serving notes" (router delta and the low-rank
+// correction branch on the block output).
+//
+// The fp16 weight rows are first split once per call into exact bf16 hi/lo
+// operand pairs (device_common.h), stored tile by tile in matrix-core operand
+// order, so a wave reads each operand of a 16-row tile as one contiguous 1 KB.
+// A unit of work is (64 tokens, 128 weight rows); a block of 4 waves stages the
+// tokens' activations one 128-wide group at a time into a double-buffered LDS
+// tile and each wave multiplies them with its two 16-row tiles, whose split
+// operands it streams from the workspace one group ahead.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+// Blocks of 4 waves run two to a CU, so one block's barrier and load waits
+// overlap the other's matrix work.
+constexpr int kDenseWaves = 4;
+constexpr int kDenseRows = kDenseWaves * 32;      // weight rows per unit (2 tiles per wave)
+constexpr int kDenseTok = 64;                     // tokens per unit (4 MFMA M tiles)
+constexpr int kDenseRow = 256 + 16;               // staged bytes per token row and group
+constexpr int kDenseBuf = kDenseTok * kDenseRow;  // one staged group
+constexpr int kOutStride = kDenseRows + 4;        // floats per token row of the combine tile
+constexpr size_t kDenseLds = std::max<size_t>(2 * (size_t)kDenseBuf, (size_t)kDenseTok * kOutStride * 4);
+constexpr int kDenseP = kDenseTok * 16 / (64 * kDenseWaves);  // staged 16-byte chunks per thread and group
+
+int dense_kpad(int K) { return (K + kGroup - 1) / kGroup * kGroup; }
+
+int64_t dense_split_bytes(int N, int K) { return (int64_t)(N + 15) / 16 * 16 * dense_kpad(K) * 4; }
+
+// ------------------------------------------------------------------ split
+// Split weights: 16-row tile, group g, MFMA m, hi/lo, quarter q, row i16 ->
+// 16 bytes (8 bf16 of elements g*128 + 32m + 8q .. +7 of row 16 tile + i16) at
+// ((((tile * G + g) * 4 + m) * 2 + hl) * 64 + 16 q + i16) * 16.  Elements past K
+// and rows past N are zero.
+__global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, u32x4* __restrict__ out) {
+  const int cpr = Kp / 8;
+  const int Np = (N + 15) / 16 * 16;
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= (int64_t)Np * cpr) return;
+  const int n = (int)(c / cpr), ck = (int)(c % cpr), k = ck * 8;
+  const int G = Kp / kGroup, g = ck / 16, m = (ck / 4) % 4, q = ck % 4;
+  const int64_t at = ((((int64_t)(n / 16) * G + g) * 4 + m) * 2) * 64 + 16 * q + (n % 16);
+  u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+  if (k < a.K && n < N) {
+    if (n < a.N0) {
+      const u32x4 w = *(const u32x4_a4*)(a.w0 + (int64_t)n * a.K + k);
+      if (a.w0b)
+        split_sum_f16x8(w, *(const u32x4_a4*)(a.w0b + (int64_t)n * a.K + k), hi, lo);
+      else
+        split_f16x8(w, hi, lo);
+    } else {
+      split_f16x8(*(const u32x4_a4*)(a.w1 + (int64_t)(n - a.N0) * a.K + k), hi, lo);
+    }
+  }
+  out[at] = hi;
+  out[at + 64] = lo;
+}
+
+// ------------------------------------------------------------------ GEMM
+template <int EPI, int NTT>
+__device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __restrict__ w2, int N, int Kp,
+                                           int64_t t0, int rb, char* smem) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int G = Kp / kGroup;
+  const int row0 = rb * kDenseRows + wave * 32;
+  const bool active = row0 < N;
+
+  // the wave's two row tiles (a tile past the last one repeats it; rows past N
+  // are zero and not stored); operand (g, m, hl) at + (g * 8 + m * 2 + hl) * 64
+  const u32x4* wp[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int tile = min(row0 / 16 + rt, (N - 1) / 16);
+    wp[rt] = w2 + (int64_t)tile * G * 512 + lane;
+  }
+
+  // staging roles: token row si, 16-byte chunk sc (elements 8 sc .. 8 sc + 7 of
+  // the group = MFMA sc / 4, quarter sc % 4); a wave reads 4 rows x 256 bytes
+  int si[kDenseP], sc[kDenseP];
+  const uint16_t* srow[kDenseP];
+#pragma unroll
+  for (int pp = 0; pp < kDenseP; ++pp) {
+    const int u = threadIdx.x + pp * 64 * kDenseWaves;
+    si[pp] = u >> 4;
+    sc[pp] = u & 15;
+    srow[pp] = a.act + std::min<int64_t>(t0 + si[pp], a.T - 1) * a.lda;
+  }
+  auto stage_load = [&](int g, u32x4 (&raw)[kDenseP]) {
+#pragma unroll
+    for (int pp = 0; pp < kDenseP; ++pp)
+      if (si[pp] < NTT * 16) {
+        const int k = g * kGroup + 8 * sc[pp];
+        raw[pp] = k < a.K ? *(const u32x4*)(srow[pp] + k) : u32x4{0u, 0u, 0u, 0u};
+      }
+  };
+  auto stage_store = [&](const u32x4 (&raw)[kDenseP], char* buf) {
+#pragma unroll
+    for (int pp = 0; pp < kDenseP; ++pp)
+      if (si[pp] < NTT * 16) *(u32x4*)(buf + si[pp] * kDenseRow + sc[pp] * 16) = raw[pp];
+  };
+
+  u32x4 B[2][4][2];  // [row tile][m][hi, lo] of the next group
+  if (active && G > 0) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        B[rt][m][0] = wp[rt][(m * 2) * 64];
+        B[rt][m][1] = wp[rt][(m * 2 + 1) * 64];
+      }
+  }
+  u32x4 sraw[kDenseP];
+  __syncthreads();  // the previous unit is done with the shared memory
+  stage_load(0, sraw);
+  stage_store(sraw, smem);
+  __syncthreads();
+
+  f32x4 acc[NTT][2];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int g = 0; g < G; ++g) {
+    const int gn = min(g + 1, G - 1);  // the last step refetches its own group (unused)
+    stage_load(gn, sraw);
+    if (active) {
+      const char* ab = smem + (g & 1) * kDenseBuf + i16 * kDenseRow + q * 16;
+      u32x4 A[NTT][4];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kDenseRow + m * 64);
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] = mfma16(A[tt][m], B[rt][m][hl], acc[tt][rt]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          B[rt][m][0] = wp[rt][(gn * 8 + m * 2) * 64];
+          B[rt][m][1] = wp[rt][(gn * 8 + m * 2 + 1) * 64];
+        }
+      }
+    }
+    stage_store(sraw, smem + ((g + 1) & 1) * kDenseBuf);
+    __syncthreads();
+  }
+
+  if (EPI == EPI_XPROJ) {
+    if (!active) return;
+    // lane holds tokens t0 + 16 tt + 4q + j, rows row0 + 16 rt + i16
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + 16 * tt + 4 * q + j;
+        if (t >= a.T) continue;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int r = row0 + 16 * rt + i16;
+          if (r < a.N0)
+            a.logits[t * a.N0 + r] = acc[tt][rt][j];
+          else if (r < N)
+            a.z[t * a.N1 + (r - a.N0)] = (uint16_t)f32_to_bf16(acc[tt][rt][j]);
+        }
+      }
+  } else {
+    // through shared memory, so each thread sums 8 consecutive rows of a token
+    // with 16-byte slot reads
+    float* tile = (float*)smem;
+    if (active) {
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt)
+            tile[(16 * tt + 4 * q + j) * kOutStride + wave * 32 + 16 * rt + i16] = acc[tt][rt][j];
+    }
+    __syncthreads();
+    const int d = a.N0;
+    const int64_t Tk = a.T * a.top_k;
+    for (int item = threadIdx.x; item < NTT * 16 * (kDenseRows / 8); item += 64 * kDenseWaves) {
+      const int tl = item / (kDenseRows / 8), c = item % (kDenseRows / 8);
+      const int64_t t = t0 + tl;
+      const int n0 = rb * kDenseRows + 8 * c;
+      if (t >= a.T || n0 >= d) continue;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = tile[tl * kOutStride + 8 * c + e];
+      auto add = [&](int64_t slot) {
+        const u32x4 s = *(const u32x4*)(a.slots + slot * d + n0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] += bf16_to_f32(s[e] & 0xFFFFu);
+          v[2 * e + 1] += bf16_to_f32(s[e] >> 16);
+        }
+      };
+      for (int i = 0; i < a.top_k; ++i) add(t * a.top_k + i);
+      for (int s = 0; s < a.n_shared; ++s) add(Tk + s * a.T + t);
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(v[2 * e]) | (f32_to_bf16(v[2 * e + 1]) << 16);
+      *(u32x4_a4*)(a.y + t * d + n0) = o;
+    }
+  }
+}
+
+// Persistent blocks over units l = (row block l / TB, token tile l % TB); the
+// blocks of one XCD (block index mod 8) take a contiguous range of units, so
+// they share one row block's split weights in their L2.
+template <int EPI>
+__global__ __launch_bounds__(64 * kDenseWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dense_gemm_kernel(DenseArgs a, const u32x4* w2, int N,
+                                                                        int Kp) {
+  extern __shared__ __align__(16) char smem[];
+  const int64_t TB = (a.T + kDenseTok - 1) / kDenseTok;
+  const int64_t U = TB * ((N + kDenseRows - 1) / kDenseRows);
+  const int64_t per = (U + 7) / 8;
+  for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
+    const int64_t l = (u & 7) * per + (u >> 3);
+    if (l >= U) continue;
+    const int rb = (int)(l / TB);
+    const int64_t t0 = (l % TB) * kDenseTok;
+    switch ((int)std::min<int64_t>(4, (a.T - t0 + 15) / 16)) {
+      case 1: dense_unit<EPI, 1>(a, w2, N, Kp, t0, rb, smem); break;
+      case 2: dense_unit<EPI, 2>(a, w2, N, Kp, t0, rb, smem); break;
+      case 3: dense_unit<EPI, 3>(a, w2, N, Kp, t0, rb, smem); break;
+      default: dense_unit<EPI, 4>(a, w2, N, Kp, t0, rb, smem); break;
+    }
+  }
+}
+
+static int cu_count_dense() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+template <int EPI>
+hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream) {
+  const int Kp = dense_kpad(a.K);
+  u32x4* w2 = (u32x4*)a.wsplit;
+  const int64_t chunks = (int64_t)(N + 15) / 16 * 16 * (Kp / 8);
+  if (chunks > 0) {
+    split_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(a, N, Kp, w2);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e;
+  auto kern = dense_gemm_kernel<EPI>;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kDenseWaves, kDenseLds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t U = ((a.T + kDenseTok - 1) / kDenseTok) * ((N + kDenseRows - 1) / kDenseRows);
+  const int64_t grid = std::min<int64_t>((int64_t)cu_count_dense() * per_cu, U);
+  kern<<<dim3((unsigned)grid), 64 * kDenseWaves, kDenseLds, stream>>>(a, w2, N, Kp);
+  return hipGetLastError();
+}
+
+template hipError_t launch_dense_gemm<EPI_XPROJ>(const DenseArgs&, int, hipStream_t);
+template hipError_t launch_dense_gemm<EPI_COMBINE>(const DenseArgs&, int, hipStream_t);
+
+}  // namespace moe

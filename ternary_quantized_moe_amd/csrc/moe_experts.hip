@@ -378,6 +378,434 @@ __global__ __launch_bounds__(64 * WPB) void expert_dec_kernel(ExpertArgs a, int 
   }
 }
 
+// ============================================================ large batches
+// Work unit = (item of up to 64 positions of one bank, row block).  A block of
+// WAVES waves stages the item's activations one 128-wide group at a time into a
+// double-buffered LDS tile while its waves multiply the previous group.  Each
+// wave owns 4 row tiles (gate/up: 32 features, their gate and up rows; down:
+// 64 model rows), decodes the 4 row tiles of a group once and multiplies them
+// with every token tile of the item, so one decoded weight feeds up to 4 MFMAs.
+// Blocks of 4 waves run two to a CU, so one block's barrier and load waits
+// overlap the other's matrix work.
+constexpr int kGemmWaves = 4;
+constexpr int kGemmRow = 256 + 16;                // staged bytes per token row and group
+constexpr int kGemmBuf = kGemmChunk * kGemmRow;   // one staged group
+constexpr int gemm_rows(int mode, int waves) { return waves * (mode == 0 ? 32 : 64); }  // per unit
+
+// Half of one activation quarter: elements of row `row`, group g, quarter q
+// feeding MFMAs m = 2h and 2h + 1 (PQ2_0: elements 32q + 16h .. +15; PTQ1_0: the
+// raw operands 2h, 2h + 1 of load_act_raw).
+template <int FMT>
+__device__ __forceinline__ void act_half_load(const uint16_t* row, int g, int q, int h, u32x4 (&raw)[2]) {
+  if (FMT == kPQ2) {
+    const u32x4* p = (const u32x4*)(row + g * 128 + 32 * q + 16 * h);
+    raw[0] = p[0];
+    raw[1] = p[1];
+  } else {
+    const uint16_t* p = row + g * 128 + 30 * q + 16 * h;  // 4-byte aligned
+    raw[0] = *(const u32x4_a4*)p;
+    if (h == 0) {
+      raw[1] = *(const u32x4_a4*)(p + 8);
+    } else {
+      const u32x2 w = *(const u32x2_a4*)(p + 8);
+      const uint32_t w2 = *(const uint32_t*)(p + 12);
+      const uint32_t t = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
+      raw[1] = u32x4{w.x, w.y, w2, t};
+    }
+  }
+}
+
+// MFMA operands 2h, 2h + 1 from a half quarter, stored at their staged places
+// (the same pair order as act_operands).
+template <int FMT>
+__device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_row, int q, int h) {
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    u32x4 o;
+    if (FMT == kPQ2) {
+      const uint32_t x[8] = {raw[0].x, raw[0].y, raw[0].z, raw[0].w, raw[1].x, raw[1].y, raw[1].z, raw[1].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int dl = 2 * mm + (i >> 1);
+        o[i] = perm_b32(x[dl + 4], x[dl], (i & 1) ? 0x07060302u : 0x05040100u);
+      }
+    } else {
+      o = raw[mm];
+    }
+    *(u32x4*)(dst_row + ((2 * h + mm) * 4 + q) * 16) = o;
+  }
+}
+
+// NTT: token tiles of the item (a compile-time count keeps the multiply free of
+// branches, so the independent MFMA chains of the token tiles interleave).
+template <int FMT, int MODE, int NTT, int WAVES>
+__device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
+                                          char* bufs) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int K = MODE == MODE_GATEUP ? a.d : a.f;
+  const int G = K / kGroup;
+  constexpr int BB = block_bytes_c<FMT>();
+  const int64_t row_bytes = (int64_t)G * BB;
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
+
+  // the wave's row tiles; gate/up: rt 0, 1 gate rows of features row0 + 16 rt,
+  // rt 2, 3 the up rows of the same features
+  const int row0 = rb * gemm_rows(MODE, WAVES) + wave * (MODE == MODE_GATEUP ? 32 : 64);
+  const bool active = row0 < (MODE == MODE_GATEUP ? a.f : a.d);
+  const uint8_t* wrow[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    int64_t off;
+    if (MODE == MODE_GATEUP)
+      off = (rt >> 1) * gu_bytes + (int64_t)(row0 + 16 * (rt & 1) + i16) * row_bytes;
+    else
+      off = 2 * gu_bytes + (int64_t)(row0 + 16 * rt + i16) * row_bytes;
+    wrow[rt] = bank + (active ? off : 0);
+  }
+
+  // staging roles of the thread: token row si, quarter sq, half sh of the
+  // 64 x 8 half quarters of a group
+  constexpr int P = 512 / (64 * WAVES);
+  int si[P], sq[P], sh[P];
+  bool stage_on[P];
+  const uint16_t* srow[P];
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp) {
+    const int u = threadIdx.x + pp * 64 * WAVES;
+    si[pp] = u >> 3;
+    sq[pp] = (u >> 1) & 3;
+    sh[pp] = u & 1;
+    stage_on[pp] = si[pp] < NTT * 16;
+    const int64_t p = it.pos + min(si[pp], it.n - 1);  // rows past the item repeat its last row
+    if (MODE == MODE_GATEUP) {
+      const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
+      srow[pp] = a.x + tok * a.d;
+    } else {
+      srow[pp] = a.h + p * a.f;
+    }
+  }
+
+  // weights of the next group in flight (a group step is long enough to cover
+  // the load latency)
+  u32x3 ring[4];
+  if (active) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ring[rt] = load_block_x3<FMT>(wrow[rt], q);
+  }
+  u32x4 sraw[P][2];
+  __syncthreads();  // the previous unit is done with the staging buffers
+#pragma unroll
+  for (int pp = 0; pp < P; ++pp)
+    if (stage_on[pp]) {
+      act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], sraw[pp]);
+      act_half_store<FMT>(sraw[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
+    }
+  __syncthreads();
+
+  f32x4 acc[NTT][4];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The last step fetches its own group again (in bounds, unused) and restages
+  // it into the idle buffer, so the loop body has no branch on g.
+  for (int g = 0; g < G; ++g) {
+    const int gn = min(g + 1, G - 1);
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp)
+      if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], sraw[pp]);
+    if (active) {
+      // the item's activation operands of this group, then one row tile at a
+      // time: decode it, refill its ring slot, multiply it with every token tile
+      const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
+      u32x4 A[NTT][4];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        u32x4 W[4];
+        const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+        ring[rt] = load_block_x3<FMT>(wrow[rt] + (int64_t)gn * BB, q);
+        f32x4 tmp[NTT];
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp)
+      if (stage_on[pp])
+        act_half_store<FMT>(sraw[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
+    __syncthreads();
+  }
+  if (!active) return;
+
+  // lane holds positions it.pos + 16 tt + 4q + j, column i16 of each row tile;
+  // the operands encode 2t, hence the 0.5
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int ti = 16 * tt + 4 * q + j;
+      if (ti >= it.n) continue;
+      const int64_t p = it.pos + ti;
+      if (MODE == MODE_GATEUP) {
+#pragma unroll
+        for (int ft = 0; ft < 2; ++ft) {
+          const float gv = 0.5f * acc[tt][ft][j], uv = 0.5f * acc[tt][2 + ft][j];
+          const float hv = gv / (1.f + __expf(-gv)) * uv;
+          a.h[p * a.f + row0 + 16 * ft + i16] = (uint16_t)f32_to_bf16(hv);
+        }
+      } else {
+        int64_t slot;
+        float wgt;
+        if (p < a.Tk) {
+          slot = a.perm[p];
+          wgt = a.topk_w[slot];
+        } else {
+          slot = p;
+          wgt = 1.f;
+        }
+        wgt *= 0.5f;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          a.slots[slot * a.d + row0 + 16 * rt + i16] = (uint16_t)f32_to_bf16(wgt * acc[tt][rt][j]);
+      }
+    }
+  }
+}
+
+template <int MODE, int FS, int NTT, int WAVES>
+__device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
+                                              char* bufs, bool ptq1) {
+  if (FS != 1 && ptq1)
+    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs);
+  else if (FS != 2)
+    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs);
+}
+
+// Persistent blocks over units.  Unit l = (item l / row_blocks, row block
+// l % row_blocks); the blocks of one XCD (block index mod 8, the order in which
+// workgroups are spread over the XCDs) take a contiguous range of units, so the
+// items of one expert and the row blocks of one item meet in the same L2.
+// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][2 staged groups]
+template <int MODE, int FS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void expert_gemm_kernel(ExpertArgs a, int row_blocks) {
+  extern __shared__ __align__(16) char smem[];
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  char* bufs = smem + lut_bytes;
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  const int64_t U = (int64_t)(*a.n_items) * row_blocks;
+  const int64_t per = (U + 7) / 8;
+  for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
+    const int64_t l = (u & 7) * per + (u >> 3);
+    if (l >= U) continue;
+    const Item it = a.items[l / row_blocks];
+    const int rb = (int)(l % row_blocks);
+    const bool ptq1 = FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1);
+    switch ((it.n + 15) / 16) {
+      case 1: gemm_dispatch<MODE, FS, 1, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      case 2: gemm_dispatch<MODE, FS, 2, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      case 3: gemm_dispatch<MODE, FS, 3, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      default: gemm_dispatch<MODE, FS, 4, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+    }
+  }
+}
+
+// ------------------------------------------------------------ large batches: down
+// Work unit = one item.  The block stages the item's h rows (all f inputs, in
+// the container format's k-slot order) in LDS once; each wave then takes
+// 64-row quads of the d output rows (quad w, w + WAVES, ...) and streams their
+// weights group after group through a ring that runs on from one quad into the
+// next, so after the staging the block waits on no barrier and no empty ring.
+constexpr int kDownWaves = 8;
+
+// The thread index as a value the compiler treats as new at each use, so index
+// arithmetic derived from it stays inside the persistent loop instead of being
+// hoisted to kernel entry, where it would hold registers for the whole kernel.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+template <int FMT, int NTT, int G>
+__device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs) {
+  const int tid = opaque_tid();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  constexpr int K = G * kGroup;
+  constexpr int stride = stage_stride(K);
+  constexpr int BB = block_bytes_c<FMT>();
+  constexpr int64_t row_bytes = (int64_t)G * BB;
+  constexpr int D = 1;  // groups in flight (D = 2 takes 12 more registers than the wave has)
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
+  const int nquads = a.d / 64;
+  const int nqw = wave < nquads ? (nquads - wave + kDownWaves - 1) / kDownWaves : 0;
+  constexpr int64_t quad_stride = (int64_t)64 * kDownWaves * row_bytes;
+
+  const uint8_t* rows[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt + i16) * row_bytes;
+  u32x3 ring0[4], ring1[4];
+  if (nqw > 0) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      ring0[rt] = load_block_x3<FMT>(rows[rt], q);
+      if (D == 2) ring1[rt] = load_block_x3<FMT>(rows[rt] + BB, q);
+    }
+  }
+
+  // per token row: its slot and half its gate weight (the operands encode 2t),
+  // read back through volatile pointers so the quad loop does not hold them
+  int* slot_of = (int*)(xs + kGemmChunk * stride);
+  float* wgt_of = (float*)(slot_of + kGemmChunk);
+  __syncthreads();  // the previous unit is done with the staged rows
+  if (tid < NTT * 16) {
+    const int64_t p = it.pos + min(tid, it.n - 1);
+    const bool routed = p < a.Tk;
+    const int slot = routed ? a.perm[p] : (int)p;
+    slot_of[tid] = slot;
+    wgt_of[tid] = 0.5f * (routed ? a.topk_w[slot] : 1.f);
+  }
+  {
+    // the thread's share in batches of 4, all loads of a batch in flight
+    // before its first store
+    constexpr int total = NTT * 16 * G * 8, PER = (total + 64 * kDownWaves - 1) / (64 * kDownWaves);
+    constexpr int NB = PER < 4 ? PER : 4;
+#pragma unroll
+    for (int k0 = 0; k0 < PER; k0 += NB) {
+      u32x4 raw[NB][2];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int u = tid + (k0 + k) * 64 * kDownWaves;
+        if (k0 + k < PER && u < total) {
+          const int i = u / (G * 8), rem = u % (G * 8);
+          const uint16_t* row = a.h + (int64_t)(it.pos + min(i, it.n - 1)) * a.f;  // rows past the item repeat its last
+          act_half_load<FMT>(row, rem >> 3, (rem >> 1) & 3, rem & 1, raw[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int u = tid + (k0 + k) * 64 * kDownWaves;
+        if (k0 + k < PER && u < total) {
+          const int i = u / (G * 8), rem = u % (G * 8);
+          act_half_store<FMT>(raw[k], xs + i * stride + (rem >> 3) * 256, (rem >> 1) & 3, rem & 1);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const char* ab = xs + i16 * stride + q * 16;
+  for (int t = 0; t < nqw; ++t) {
+    const bool more = t + 1 < nqw;
+    f32x4 acc[NTT][4];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](int g, u32x3 (&ring)[4]) {
+      u32x4 A[NTT][4];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * stride + g * 256 + m * 64);
+      // refill with group g + D of this quad, else of the next quad (the last
+      // quad refetches its own groups: in bounds, unused)
+      const int64_t nxt = g + D < G ? (int64_t)(g + D) * BB : (more ? quad_stride : 0) + (int64_t)(g + D - G) * BB;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        u32x4 W[4];
+        const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+        ring[rt] = load_block_x3<FMT>(rows[rt] + nxt, q);
+        f32x4 tmp[NTT];
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+      }
+    };
+#pragma unroll 1
+    for (int g = 0; g < G; g += D) {
+      step(g, ring0);
+      if (D == 2) step(g + 1, ring1);
+    }
+    // lane holds positions it.pos + 16 tt + 4q + j, column i16 of each row tile
+    const int row0 = (wave + t * kDownWaves) * 64;
+    const volatile int* vslot = slot_of;
+    const volatile float* vwgt = wgt_of;
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ti = 16 * tt + 4 * q + j;
+        if (ti >= it.n) continue;
+        const int64_t slot = vslot[ti];
+        const float wgt = vwgt[ti];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+          a.slots[slot * a.d + row0 + 16 * rt + i16] = (uint16_t)f32_to_bf16(wgt * acc[tt][rt][j]);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) rows[rt] += quad_stride;
+  }
+}
+
+template <int FS, int NTT, int G>
+__device__ __forceinline__ void down_dispatch(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
+                                              bool ptq1) {
+  if (FS != 1 && ptq1)
+    down_unit<kPTQ1, NTT, G>(a, it, lut, xs);
+  else if (FS != 2)
+    down_unit<kPQ2, NTT, G>(a, it, lut, xs);
+}
+
+// Persistent blocks over items, the blocks of one XCD taking a contiguous range
+// (so the items of one expert share its down weights in one L2).
+// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][64 staged rows][64 slots][64 weights]
+template <int FS, int G>
+__global__ __launch_bounds__(64 * kDownWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void down_resident_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  char* xs = smem + lut_bytes;
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  const int64_t U = *a.n_items;
+  const int64_t per = (U + 7) / 8;
+  for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
+    const int64_t l = (u & 7) * per + (u >> 3);
+    if (l >= U) continue;
+    const Item it = a.items[l];
+    const bool ptq1 = FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1);
+    switch ((it.n + 15) / 16) {
+      case 1: down_dispatch<FS, 1, G>(a, it, lut, xs, ptq1); break;
+      case 2: down_dispatch<FS, 2, G>(a, it, lut, xs, ptq1); break;
+      case 3: down_dispatch<FS, 3, G>(a, it, lut, xs, ptq1); break;
+      default: down_dispatch<FS, 4, G>(a, it, lut, xs, ptq1); break;
+    }
+  }
+}
+
 static int cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -458,6 +886,61 @@ static hipError_t launch_stream(const ExpertArgs& a, int64_t max_items, hipStrea
   return launch_stream_fs<MODE, WPB, RT, D, G, 3, WPE>(a, max_items, stream);
 }
 
+template <int MODE, int FS, int WAVES>
+static hipError_t launch_gemm_fs(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  const int N = MODE == MODE_GATEUP ? a.f : a.d;
+  const int row_blocks = (N + gemm_rows(MODE, WAVES) - 1) / gemm_rows(MODE, WAVES);
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + 2 * (size_t)kGemmBuf;
+  auto kern = expert_gemm_kernel<MODE, FS, WAVES>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WAVES, lds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t grid = std::min<int64_t>((int64_t)cu_count() * per_cu, max_items * row_blocks);
+  kern<<<dim3((unsigned)grid), 64 * WAVES, lds, stream>>>(a, row_blocks);
+  return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch_gemm(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
+  if (a.fmt_mask == 1) return launch_gemm_fs<MODE, 1, kGemmWaves>(a, max_items, stream);
+  if (a.fmt_mask == 2) return launch_gemm_fs<MODE, 2, kGemmWaves>(a, max_items, stream);
+  return launch_gemm_fs<MODE, 3, kGemmWaves>(a, max_items, stream);
+}
+
+template <int FS, int G>
+static hipError_t launch_down_resident_fs(const ExpertArgs& a, int64_t max_items, size_t lds, hipStream_t stream) {
+  auto kern = down_resident_kernel<FS, G>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kDownWaves, lds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int64_t grid = std::min<int64_t>((int64_t)cu_count() * per_cu, max_items);
+  kern<<<dim3((unsigned)grid), 64 * kDownWaves, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, size_t lds, hipStream_t stream) {
+  if (a.fmt_mask == 1) return launch_down_resident_fs<1, G>(a, max_items, lds, stream);
+  if (a.fmt_mask == 2) return launch_down_resident_fs<2, G>(a, max_items, lds, stream);
+  return launch_down_resident_fs<3, G>(a, max_items, lds, stream);
+}
+
+// Down projection of a large batch: LDS-resident h rows where the shape is
+// compiled in and the rows fit, else the group-staged kernel.
+static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, hipStream_t s) {
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kGemmChunk * (stage_stride(a.f) + 8);
+  if (lds <= 160 * 1024) {
+    switch (a.f / kGroup) {
+      case 8: return launch_down_resident<8>(a, mi, lds, s);
+      case 6: return launch_down_resident<6>(a, mi, lds, s);
+      case 4: return launch_down_resident<4>(a, mi, lds, s);
+      case 1: return launch_down_resident<1>(a, mi, lds, s);
+      default: break;
+    }
+  }
+  return launch_gemm<MODE_DOWN>(a, mi, s);
+}
+
 // Shapes with a compile-time group count stream; others take the generic loop.
 //   gate/up: K = d;  down: K = f.  Few tokens: K split over KS waves per tile.
 static hipError_t launch_gateup(const ExpertArgs& a, int64_t mi, bool small, hipStream_t s) {
@@ -502,12 +985,15 @@ hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t st
   if (max_items <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   const bool small = a.T <= 4;
+  const bool gemm = a.chunk == kGemmChunk;
   auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], stream) : hipSuccess; };
   e = mark(4);
-  if (e == hipSuccess) e = launch_gateup(a, max_items, small, stream);
+  if (e == hipSuccess)
+    e = gemm ? launch_gemm<MODE_GATEUP>(a, max_items, stream) : launch_gateup(a, max_items, small, stream);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess) e = launch_down(a, max_items, small, stream);
+  if (e == hipSuccess)
+    e = gemm ? launch_down_large(a, max_items, stream) : launch_down(a, max_items, small, stream);
   if (e == hipSuccess) e = mark(7);
   return e;
 }

@@ -7,12 +7,18 @@
 namespace moe {
 
 constexpr int kGroup = 128;     // weights per container group
-constexpr int kChunk = 16;      // tokens per expert work item (one MFMA M tile)
+constexpr int kChunk = 16;      // tokens per expert work item of a small batch (one MFMA M tile)
+constexpr int kGemmChunk = 64;  // tokens per expert work item of a large batch (four M tiles)
 constexpr int kRouteBlock = 256;  // tokens per ranking block
+constexpr int kGroupMaxT = 256;   // largest batch grouped by one block
 constexpr int kMaxExperts = 1024;
 
+// Small batches stream each touched expert's weights once per 16 tokens; large
+// batches multiply each decoded weight group with up to 64 tokens.
+__host__ __device__ inline int item_chunk(int64_t T) { return T > kGroupMaxT ? kGemmChunk : kChunk; }
+
 // Work item of the grouped expert kernels: bank, first position in the
-// (expert, token)-ordered slot space, number of tokens (<= kChunk).
+// (expert, token)-ordered slot space, number of tokens (<= item_chunk(T)).
 struct Item {
   int32_t bank;
   int32_t pos;
@@ -39,7 +45,12 @@ struct DenseArgs {
   int top_k;
   int n_shared;
   uint16_t* y;     // bf16 [T x N0]
+  // large batches: workspace for the split weights, dense_split_bytes(N0 + N1, K)
+  void* wsplit;
 };
+
+constexpr int EPI_XPROJ = 0;
+constexpr int EPI_COMBINE = 1;
 
 struct RouteArgs {
   const float* logits;  // [T x E]
@@ -57,6 +68,7 @@ struct RouteArgs {
   int32_t* perm;        // [T x k]
   Item* items;          // [max_items]
   int32_t* n_items;     // [1]
+  int chunk;            // tokens per work item, item_chunk(T)
 };
 
 struct ExpertArgs {
@@ -72,12 +84,16 @@ struct ExpertArgs {
   const uint16_t* x;   // bf16 [T x d]
   uint16_t* h;         // bf16 [(Tk + S*T) x f]
   uint16_t* slots;     // bf16 [(Tk + S*T) x d]
-  int nmax;            // most tokens any work item holds (<= kChunk)
+  int nmax;            // most tokens any work item holds (<= chunk)
+  int chunk;           // tokens per work item, item_chunk(T)
   int fmt_mask;        // 1: some bank is PQ2_0, 2: some bank is PTQ1_0
 };
 
 hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
                                 uint16_t* scales, hipStream_t stream);
+int64_t dense_split_bytes(int N, int K);
+template <int EPI>
+hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream);
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream);

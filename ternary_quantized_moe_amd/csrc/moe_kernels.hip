@@ -87,34 +87,6 @@ hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, 
 // out[t][n] = sum_k act[t][k] W[n][k] with fp16 weight rows split exactly into
 // two bfloat16 terms (hi + lo) so bf16 matrix cores give fp32-accurate products.
 // Block: KS waves splitting K; one 16-token x 16-row tile per block.
-constexpr int EPI_XPROJ = 0;
-constexpr int EPI_COMBINE = 1;
-
-// fp16 x8 (4 dwords) -> exact bf16 hi/lo operand pairs (truncated hi).
-__device__ __forceinline__ void split_f16x8(u32x4 w, u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = f16_to_f32(w[i] & 0xFFFFu), b = f16_to_f32(w[i] >> 16);
-    const uint32_t ha = __float_as_uint(a) & 0xFFFF0000u, hb = __float_as_uint(b) & 0xFFFF0000u;
-    const uint32_t la = __float_as_uint(a - __uint_as_float(ha)), lb = __float_as_uint(b - __uint_as_float(hb));
-    hi[i] = perm_b32(hb, ha, 0x07060302u);
-    lo[i] = perm_b32(lb, la, 0x07060302u);
-  }
-}
-
-// fp16 x8 from two sources summed in fp32 -> bf16 hi (round to nearest even) +
-// bf16 lo (round to nearest even); |error| <= 2^-18 |a + b|.
-__device__ __forceinline__ void split_sum_f16x8(u32x4 w, u32x4 v, u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float a = f16_to_f32(w[i] & 0xFFFFu) + f16_to_f32(v[i] & 0xFFFFu);
-    const float b = f16_to_f32(w[i] >> 16) + f16_to_f32(v[i] >> 16);
-    const uint32_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
-    const uint32_t la = f32_to_bf16(a - bf16_to_f32(ha)), lb = f32_to_bf16(b - bf16_to_f32(hb));
-    hi[i] = ha | (hb << 16);
-    lo[i] = la | (lb << 16);
-  }
-}
 
 // Block = one 16-row tile x up to MT*16 tokens; its KS waves split K in
 // 32-wide steps and reduce through LDS.  Each weight k-step is split into bf16
@@ -235,11 +207,14 @@ static hipError_t launch_dense(const DenseArgs& a, int N, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Large batches take the LDS-tiled matrix-core kernels (moe_dense.hip).
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
+  if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_XPROJ>(a, a.N0 + a.N1, stream);
   return launch_dense<EPI_XPROJ>(a, a.N0 + a.N1, stream);
 }
 
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
+  if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_COMBINE>(a, a.N0, stream);
   return launch_dense<EPI_COMBINE>(a, a.N0, stream);
 }
 
@@ -366,8 +341,9 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   }
   if (e == 0) a.offsets[E] = (int)(a.T * a.k);
   __syncthreads();
-  // work items: ceil(count / kChunk) per routed expert, then the shared experts
-  const int chunks = e < E ? (total + kChunk - 1) / kChunk : 0;
+  // work items: ceil(count / chunk) per routed expert, then the shared experts
+  const int C = a.chunk;
+  const int chunks = e < E ? (total + C - 1) / C : 0;
   sh[e] = chunks;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -381,19 +357,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   for (int c = 0; c < chunks; ++c) {
     Item it;
     it.bank = e;
-    it.pos = off_e + c * kChunk;
-    it.n = min(kChunk, total - c * kChunk);
+    it.pos = off_e + c * C;
+    it.n = min(C, total - c * C);
     it.pad = 0;
     a.items[istart + c] = it;
   }
-  const int per_shared = (int)((a.T + kChunk - 1) / kChunk);
+  const int per_shared = (int)((a.T + C - 1) / C);
   const int64_t Tk = a.T * a.k;
   for (int idx = e; idx < a.S * per_shared; idx += 1024) {
     const int s = idx / per_shared, c = idx % per_shared;
     Item it;
     it.bank = E + s;
-    it.pos = (int)(Tk + (int64_t)s * a.T + (int64_t)c * kChunk);
-    it.n = (int)min((int64_t)kChunk, a.T - (int64_t)c * kChunk);
+    it.pos = (int)(Tk + (int64_t)s * a.T + (int64_t)c * C);
+    it.n = (int)min((int64_t)C, a.T - (int64_t)c * C);
     it.pad = 0;
     a.items[routed_items + idx] = it;
   }
@@ -411,8 +387,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
 
 // Grouping of a small batch (T <= kGroupMaxT) in one block, after top-k:
 // per-expert counts, offsets, ranks (ballot masks per 64-token chunk, the same
-// order rule as the multi-block path), permutation and work items.
-constexpr int kGroupMaxT = 256;
+// order rule as the multi-block path), permutation and work items of kChunk
+// tokens (item_chunk(T) for such a batch).
 
 __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   __shared__ unsigned long long mask[kGroupMaxT / 64][kMaxExperts];

@@ -219,9 +219,11 @@ def test_zero_tokens_is_a_noop():
     assert y.shape[0] == 0
 
 
-def test_zero_codes_leave_only_the_correction():
+# 16 tokens take the small-batch kernels, 300 the large-batch (LDS-tiled) ones
+@pytest.mark.parametrize("T", [16, 300])
+def test_zero_codes_leave_only_the_correction(T):
     L = Layer("tiny", zero_banks=True)
-    x_bits = L.gen.tokens(16, 4)
+    x_bits = L.gen.tokens(T, 4)
     y = run_fwd(L, x_bits)
     x = omoe.bf16_to_f64(x_bits)
     ref = omoe.correction(x, omoe.f16_to_f64(L.corr_a), omoe.f16_to_f64(L.corr_b))
@@ -233,9 +235,10 @@ def test_zero_codes_leave_only_the_correction():
     assert np.array_equal(run_fwd(L2, x_bits), y)
 
 
-def test_zero_correction_equals_uncorrected_bit_exact():
+@pytest.mark.parametrize("T", [8, 300])
+def test_zero_correction_equals_uncorrected_bit_exact(T):
     L = Layer("olmoe")
-    x_bits = L.gen.tokens(8, 5)
+    x_bits = L.gen.tokens(T, 5)
     y_none = run_fwd(L, x_bits, use_corr=False)
     y_zero = run_fwd(L, x_bits, corr_b=np.zeros_like(L.corr_b))
     assert np.array_equal(y_none, y_zero)
@@ -244,9 +247,10 @@ def test_zero_correction_equals_uncorrected_bit_exact():
     assert not np.array_equal(run_fwd(L, x_bits, use_delta=False), y_corr)
 
 
-def test_doubling_down_scales_doubles_output_bit_exact():
+@pytest.mark.parametrize("T", [16, 300])
+def test_doubling_down_scales_doubles_output_bit_exact(T):
     L = Layer("tiny")
-    x_bits = L.gen.tokens(16, 6)
+    x_bits = L.gen.tokens(T, 6)
     y1 = run_fwd(L, x_bits, use_corr=False)
     L2 = Layer("tiny", key=("tiny-down-doubled",))
 
@@ -261,10 +265,11 @@ def test_doubling_down_scales_doubles_output_bit_exact():
     assert np.array_equal(f2, 2 * f1)
 
 
-def test_deterministic_and_token_independent():
+@pytest.mark.parametrize("T", [64, 300])
+def test_deterministic_and_token_independent(T):
     tq = tq_mod()
     L = Layer("olmoe")
-    x_bits = L.gen.tokens(64, 7)
+    x_bits = L.gen.tokens(T, 7)
     y1 = run_fwd(L, x_bits)
     y2 = run_fwd(L, x_bits)
     assert np.array_equal(y1, y2)
@@ -274,7 +279,7 @@ def test_deterministic_and_token_independent():
     torch.cuda.synchronize()
     for key in ("logits", "idx", "w", "counts", "offsets", "perm"):
         assert torch.equal(r1[key], r2[key]), key
-    for t in (0, 31, 63):
+    for t in (0, 31, T - 1):
         yt = run_fwd(L, x_bits[t:t + 1])
         ref = omoe.bf16_to_f64(y1[t:t + 1])
         m = np.abs(omoe.bf16_to_f64(yt) - ref).max() / np.linalg.norm(ref)
