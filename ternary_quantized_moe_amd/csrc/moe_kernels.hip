@@ -124,24 +124,33 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
   f32x4 acc[MT];
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int s = s_begin; s < s_end; ++s) {
-    const int kb = 32 * s + 8 * q;
-    const bool kin = kb < a.K;
-    u32x4 wv = {0u, 0u, 0u, 0u}, wb = {0u, 0u, 0u, 0u};
-    if (wrow && kin) wv = *(const u32x4_a4*)(wrow + kb);
-    if (summed && kin) wb = *(const u32x4_a4*)(wrowb + kb);
-    u32x4 av[MT];
+  // the wave's k-steps in batches of SB, every load of a batch issued before
+  // the first multiply (one memory round trip per batch)
+  constexpr int SB = 4;
+  for (int s0 = s_begin; s0 < s_end; s0 += SB) {
+    u32x4 wv[SB], wb[SB], av[SB][MT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) av[m] = (arow[m] && kin) ? *(const u32x4*)(arow[m] + kb) : u32x4{0u, 0u, 0u, 0u};
-    u32x4 hi, lo;
-    if (summed)
-      split_sum_f16x8(wv, wb, hi, lo);
-    else
-      split_f16x8(wv, hi, lo);
+    for (int j = 0; j < SB; ++j) {
+      const int kb = 32 * (s0 + j) + 8 * q;
+      const bool kin = s0 + j < s_end && kb < a.K;
+      wv[j] = (wrow && kin) ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      wb[j] = (summed && kin) ? *(const u32x4_a4*)(wrowb + kb) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      acc[m] = mfma16(av[m], hi, acc[m]);
-      acc[m] = mfma16(av[m], lo, acc[m]);
+      for (int m = 0; m < MT; ++m)
+        av[j][m] = (arow[m] && kin) ? *(const u32x4*)(arow[m] + kb) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      u32x4 hi, lo;
+      if (summed)
+        split_sum_f16x8(wv[j], wb[j], hi, lo);
+      else
+        split_f16x8(wv[j], hi, lo);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        acc[m] = mfma16(av[j][m], hi, acc[m]);
+        acc[m] = mfma16(av[j][m], lo, acc[m]);
+      }
     }
   }
 
@@ -174,8 +183,20 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
         const int d = a.N0;
         float v = acc[m][j];
         const int64_t Tk = a.T * a.top_k;
-        for (int i = 0; i < a.top_k; ++i) v += bf16_to_f32(a.slots[(tt * a.top_k + i) * d + n]);
-        for (int sh = 0; sh < a.n_shared; ++sh) v += bf16_to_f32(a.slots[(Tk + sh * a.T + tt) * d + n]);
+        const int ns = a.top_k + a.n_shared;
+        // the token's slots in batches of 8 loads in flight, summed in slot order
+        for (int i0 = 0; i0 < ns; i0 += 8) {
+          uint16_t sv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u;
+            const int64_t slot = i < a.top_k ? tt * a.top_k + i : Tk + (int64_t)(i - a.top_k) * a.T + tt;
+            sv[u] = i < ns ? a.slots[slot * d + n] : (uint16_t)0;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            if (i0 + u < ns) v += bf16_to_f32(sv[u]);
+        }
         a.y[tt * d + n] = (uint16_t)f32_to_bf16(v);
       }
     }
@@ -223,12 +244,11 @@ hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
 
+// One wave selects the top k of token t.  Every lane ends each round knowing
+// the round's winner, so lane i % 64 keeps the i-th selected logit in a
+// register for the softmax.  sidx: NULL, or LDS that also receives the indices.
 template <int PER>  // logits per lane: E <= 64 * PER
-__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
-  __shared__ float selv[4][kMaxExperts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  const bool active = t < a.T;
+__device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int lane, int* sidx) {
   const int E = a.E, k = a.k;
   float v[PER];
   uint32_t avail = 0;
@@ -236,12 +256,17 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   for (int c = 0; c < PER; ++c) {
     const int e = lane + 64 * c;
     v[c] = 0.f;
-    if (active && e < E) {
+    if (e < E) {
       v[c] = a.logits[t * E + e];
       avail |= 1u << c;
     }
   }
-  for (int i = 0; active && i < k; ++i) {
+  constexpr int MV = PER;  // k <= E <= 64 PER
+  float mv[MV];  // mv[c]: the (64 c + lane)-th selected logit
+#pragma unroll
+  for (int c = 0; c < MV; ++c) mv[c] = 0.f;
+  float m = 0.f;
+  for (int i = 0; i < k; ++i) {
     float bv = 0.f;
     int be = 0x7fffffff;
 #pragma unroll
@@ -264,20 +289,36 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
       }
     }
     if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
+    if (i == 0) m = bv;
+#pragma unroll
+    for (int c = 0; c < MV; ++c)
+      if (c == (i >> 6) && lane == (i & 63)) mv[c] = bv;
     if (lane == 0) {
       a.idx[t * k + i] = be;
-      selv[wave][i] = bv;
+      if (sidx) sidx[t * k + i] = be;
     }
   }
-  __syncthreads();
-  if (!active) return;
-  const float m = selv[wave][0];
+  // softmax over the selected logits
   float part = 0.f;
-  for (int i = lane; i < k; i += 64) part += __expf(selv[wave][i] - m);
+#pragma unroll
+  for (int c = 0; c < MV; ++c)
+    if (64 * c + lane < k) part += __expf(mv[c] - m);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
   const float inv = 1.f / part;
-  for (int i = lane; i < k; i += 64) a.w[t * k + i] = __expf(selv[wave][i] - m) * inv;
+#pragma unroll
+  for (int c = 0; c < MV; ++c)
+    if (64 * c + lane < k) a.w[t * k + 64 * c + lane] = __expf(mv[c] - m) * inv;
+}
+
+// One wave per token: k rounds of a wave-wide argmax over the E logits (larger
+// value first, equal values to the lower expert index; -0.0 equals +0.0), then
+// the softmax over the selected logits.
+template <int PER>
+__global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t < a.T) topk_token<PER>(a, t, lane, nullptr);
 }
 
 // Lane = token.  Each wave of the 256-token block sets bit `lane` of
@@ -385,24 +426,34 @@ __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
   a.perm[a.block_base[b * a.E + e] + a.slot_rank[s]] = (int)s;
 }
 
-// Grouping of a small batch (T <= kGroupMaxT) in one block, after top-k:
-// per-expert counts, offsets, ranks (ballot masks per 64-token chunk, the same
-// order rule as the multi-block path), permutation and work items of kChunk
-// tokens (item_chunk(T) for such a batch).
+// Grouping of a small batch (T <= kGroupMaxT) in one block: per-expert counts,
+// offsets, ranks (ballot masks per 64-token chunk, the same order rule as the
+// multi-block path), permutation and work items of kChunk tokens (item_chunk(T)
+// for such a batch).  PER = 0: after topk_kernel.  PER > 0 (T <= kFusedMaxT
+// and T k <= kFusedMaxSlots): the block's 16 waves first select the top k of
+// the tokens themselves, keeping the indices in LDS, which saves a launch.
+constexpr int kFusedMaxT = 16;  // one token per wave
+constexpr int kFusedMaxSlots = 4096;
 
+template <int PER>
 __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   __shared__ unsigned long long mask[kGroupMaxT / 64][kMaxExperts];
   __shared__ int scan_buf[1024];
+  __shared__ int sidx[PER > 0 ? kFusedMaxSlots : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.E, k = a.k;
   const int T = (int)a.T;
   const int nchunks = (T + 63) / 64;
+  constexpr int P1 = PER > 0 ? PER : 1;
+  if (PER > 0)
+    for (int t = wave; t < T; t += 16) topk_token<P1>(a, t, lane, sidx);
+  const int* ix = PER > 0 ? sidx : a.idx;
   for (int i = threadIdx.x; i < nchunks * kMaxExperts; i += 1024) (&mask[0][0])[i] = 0ull;
   __syncthreads();
   if (wave < nchunks) {
     const int t = 64 * wave + lane;
     if (t < T)
-      for (int i = 0; i < k; ++i) atomicOr(&mask[wave][a.idx[(int64_t)t * k + i]], 1ull << lane);
+      for (int i = 0; i < k; ++i) atomicOr(&mask[wave][ix[t * k + i]], 1ull << lane);
   }
   __syncthreads();
 
@@ -460,7 +511,7 @@ __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   __syncthreads();
   for (int sl = threadIdx.x; sl < T * k; sl += 1024) {
     const int t = sl / k;
-    const int ex = a.idx[sl];
+    const int ex = ix[sl];
     const int c = t >> 6, ln = t & 63;
     int r = __popcll(mask[c][ex] & (ln == 0 ? 0ull : (~0ull >> (64 - ln))));
     for (int cc = 0; cc < c; ++cc) r += __popcll(mask[cc][ex]);
@@ -471,6 +522,14 @@ __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
 hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream) {
   (void)max_items;
   const int nb = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
+  // (E > 512 would need more registers than a 1024-thread block's waves have)
+  if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxSlots && a.E <= 512) {
+    if (a.E <= 64) group_small_kernel<1><<<1, 1024, 0, stream>>>(a);
+    else if (a.E <= 128) group_small_kernel<2><<<1, 1024, 0, stream>>>(a);
+    else if (a.E <= 256) group_small_kernel<4><<<1, 1024, 0, stream>>>(a);
+    else group_small_kernel<8><<<1, 1024, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   const dim3 tg((unsigned)((a.T + 3) / 4));
   if (a.E <= 64) topk_kernel<1><<<tg, 256, 0, stream>>>(a);
   else if (a.E <= 128) topk_kernel<2><<<tg, 256, 0, stream>>>(a);
@@ -478,7 +537,7 @@ hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t strea
   else if (a.E <= 512) topk_kernel<8><<<tg, 256, 0, stream>>>(a);
   else topk_kernel<16><<<tg, 256, 0, stream>>>(a);
   if (a.T <= kGroupMaxT) {
-    group_small_kernel<<<1, 1024, 0, stream>>>(a);
+    group_small_kernel<0><<<1, 1024, 0, stream>>>(a);
   } else {
     rank_kernel<<<nb, 256, 4 * a.E * sizeof(unsigned long long), stream>>>(a);
     scan_kernel<<<1, 1024, 0, stream>>>(a, nb);
