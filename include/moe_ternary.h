@@ -107,14 +107,29 @@ int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* t
 int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n_weights, int8_t* d_trits,
                           uint16_t* d_scales, void* stream);
 
+/* Host: reorder the blocks of a [rows x cols] container (rows % 16 == 0,
+ * cols % 128 == 0) between the row-major order moe_pack writes and the
+ * tile-major order the expert kernels read.  With G = cols / 128, block
+ * (row n, group g) has row-major index n G + g and tile-major index
+ * ((n / 16) G + g) 16 + n % 16: the 16 blocks of one group of a 16-row tile are
+ * adjacent, so one wave-wide load reads 16 consecutive blocks.  Every block
+ * keeps its bytes; only their order changes.  src and dst must not overlap.
+ * Errors: MOE_E_FORMAT, MOE_E_SHAPE, MOE_E_ARG (NULL, overlap), MOE_E_SPACE. */
+int32_t moe_tile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                           int64_t dst_bytes);
+int32_t moe_untile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                             int64_t dst_bytes);
+
 /* One layer's expert banks: E routed experts, then S always-on shared experts
  * (FlashNext card, "Model Overview": top-10 routed + 1 shared).  Bank e starts
  * at byte offsets[e] of `banks` and holds three containers back to back:
- * gate [d_ff x d_model], up [d_ff x d_model], down [d_model x d_ff], row-major,
- * groups of 128 along each row, all in format formats[e].  Offsets must be
- * multiples of 4, and the buffer must extend at least MOE_BANK_SLACK bytes past
- * the end of every bank (the expert kernels read each block with one 12-byte
- * load that can run 2 bytes past the block); the slack's content is ignored. */
+ * gate [d_ff x d_model], up [d_ff x d_model], down [d_model x d_ff], groups of
+ * 128 along each row, all in format formats[e], each in the tile-major block
+ * order of moe_tile_container.  Offsets must be multiples of 16 (the kernels
+ * read each group of a 16-row tile with aligned 16-byte loads), and the buffer
+ * must extend at least MOE_BANK_SLACK bytes past the end of every bank (the
+ * expert kernels read each block with one 12-byte load that can run 2 bytes
+ * past the block); the slack's content is ignored. */
 enum { MOE_BANK_SLACK = 16 };
 typedef struct moe_expert_banks {
   int32_t d_model;              /* d: multiple of 128                              */

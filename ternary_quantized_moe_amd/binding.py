@@ -25,7 +25,7 @@ _ERRORS = {
 
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
-    "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
+    "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
 N_STAGES = 5
@@ -66,6 +66,8 @@ def lib():
             "moe_pack": (i32, [i32, vp, vp, i64, vp, i64]),
             "moe_unpack": (i32, [i32, vp, i64, vp, vp, i64]),
             "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
+            "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
+            "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
             "moe_ternary_forward": (i32, [vp, i64, vp, vp, ctypes.POINTER(ExpertBanksC), vp, vp, i32,
                                           i32, vp, vp, i64, vp]),
@@ -131,6 +133,22 @@ def unpack(fmt: int, data: np.ndarray, n_weights: int):
     scales = np.empty(max(n_weights // 128, 1), dtype=np.uint16)
     _check(lib().moe_unpack(fmt, _np_ptr(data), data.size, _np_ptr(trits), _np_ptr(scales), n_weights))
     return trits, scales[: n_weights // 128]
+
+
+def tile_container(fmt: int, data: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Row-major container -> the tile-major block order the expert kernels read."""
+    data = np.ascontiguousarray(data, dtype=np.uint8).reshape(-1)
+    out = np.empty(data.size, dtype=np.uint8)
+    _check(lib().moe_tile_container(fmt, _np_ptr(data), rows, cols, _np_ptr(out), out.size))
+    return out
+
+
+def untile_container(fmt: int, data: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """Inverse of tile_container."""
+    data = np.ascontiguousarray(data, dtype=np.uint8).reshape(-1)
+    out = np.empty(data.size, dtype=np.uint8)
+    _check(lib().moe_untile_container(fmt, _np_ptr(data), rows, cols, _np_ptr(out), out.size))
+    return out
 
 
 # ------------------------------------------------------------------ device

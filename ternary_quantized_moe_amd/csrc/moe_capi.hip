@@ -136,7 +136,8 @@ int32_t check_banks(const moe_expert_banks* b) {
                   e, fmt);
     const int64_t off = b->offsets_host[e];
     const int64_t bytes = nblocks * moe_block_bytes(fmt);
-    if (off < 0 || off % 4) return fail(MOE_E_ARG, "bank %d: offset %lld is not a non-negative multiple of 4", e, (long long)off);
+    if (off < 0 || off % 16)
+      return fail(MOE_E_ARG, "bank %d: offset %lld is not a non-negative multiple of 16", e, (long long)off);
     if (off + bytes + MOE_BANK_SLACK > b->banks_bytes)
       return fail(MOE_E_SPACE, "bank %d: bytes [%lld, %lld) plus %d bytes of slack exceed banks_bytes %lld", e,
                   (long long)off, (long long)(off + bytes), (int)MOE_BANK_SLACK, (long long)b->banks_bytes);
@@ -273,6 +274,41 @@ int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* t
   } catch (...) {
     return fail(MOE_E_ARG, "internal error in moe_unpack");
   }
+}
+
+// Block (row n, group g) of a [rows x cols] container: row-major index n G + g,
+// tile-major index ((n / 16) G + g) 16 + n % 16, with G = cols / 128.
+static int32_t retile(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                      int64_t dst_bytes, bool to_tiles) {
+  try {
+    if (!known_fmt(fmt)) return bad_fmt(fmt);
+    if (rows < 0 || rows % 16 || cols < 0 || cols % 128)
+      return fail(MOE_E_SHAPE, "a %lld x %lld container needs rows %% 16 == 0 and cols %% 128 == 0",
+                  (long long)rows, (long long)cols);
+    if (rows > 0 && cols > 0 && (!src || !dst)) return fail(MOE_E_ARG, "NULL pointer");
+    const int64_t bb = moe_block_bytes(fmt), G = cols / 128, bytes = rows * G * bb;
+    if (dst_bytes < bytes)
+      return fail(MOE_E_SPACE, "destination holds %lld bytes, %lld needed", (long long)dst_bytes, (long long)bytes);
+    if (bytes > 0 && src < dst + bytes && dst < src + bytes) return fail(MOE_E_ARG, "src and dst overlap");
+    for (int64_t n = 0; n < rows; ++n)
+      for (int64_t g = 0; g < G; ++g) {
+        const int64_t plain = n * G + g, tiled = ((n / 16) * G + g) * 16 + n % 16;
+        std::memcpy(dst + (to_tiles ? tiled : plain) * bb, src + (to_tiles ? plain : tiled) * bb, (size_t)bb);
+      }
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in the container reorder");
+  }
+}
+
+int32_t moe_tile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                           int64_t dst_bytes) {
+  return retile(fmt, src, rows, cols, dst, dst_bytes, true);
+}
+
+int32_t moe_untile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
+                             int64_t dst_bytes) {
+  return retile(fmt, src, rows, cols, dst, dst_bytes, false);
 }
 
 int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n, int8_t* d_trits, uint16_t* d_scales,

@@ -1,5 +1,11 @@
 // Grouped ternary expert kernels (gate/up + SwiGLU, down + gate weight).
 //
+// Containers are tile-major on the device (include/moe_ternary.h): the 16
+// blocks of one group of a 16-row tile are contiguous, so the block of row
+// tile_row0 + i16, group g sits at tile base + (16 g + i16) * block bytes, and
+// one load instruction of a wave (16 rows x 4 quarters) reads 16 consecutive
+// blocks.
+//
 // Work item = (bank, up to 16 consecutive positions of the (expert, token)
 // order).  A unit of work is (item, block tile): the block stages the item's
 // activation rows in LDS once (coalesced, already in matrix-core operand order)
@@ -85,10 +91,10 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
   for (int r = 0; r < RT; ++r) {
     int64_t off;
     if (MODE == MODE_GATEUP)  // r even: gate rows, r odd: up rows, of features tile*16 .. +16 (RT == 2)
-      off = (r & 1) * gu_bytes + ((int64_t)tile * 16 + i16) * row_bytes;
+      off = (r & 1) * gu_bytes + (int64_t)tile * 16 * row_bytes;
     else
-      off = 2 * gu_bytes + (((int64_t)tile * RT + r) * 16 + i16) * row_bytes;
-    rows[r] = bank + off + (int64_t)gb * BB;
+      off = 2 * gu_bytes + ((int64_t)tile * RT + r) * 16 * row_bytes;
+    rows[r] = bank + off + i16 * BB + (int64_t)gb * 16 * BB;
   }
 
   // weight prefetch starts before the activations are staged
@@ -98,7 +104,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
     for (int j = 0; j < D; ++j)
       if (GW > 0 ? j < GW : gb + j < ge)
 #pragma unroll
-        for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * BB, q);
+        for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * 16 * BB, q);
   }
 
   __syncthreads();  // the previous unit is done with the staging buffer
@@ -136,7 +142,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
         for (int r = 0; r < RT; ++r) cur[r] = ring[i % D][r];
         if (i + D < GW)
 #pragma unroll
-          for (int r = 0; r < RT; ++r) ring[i % D][r] = load_block_x3<FMT>(rows[r] + (i + D) * BB, q);
+          for (int r = 0; r < RT; ++r) ring[i % D][r] = load_block_x3<FMT>(rows[r] + (i + D) * 16 * BB, q);
         step(i, cur);
       }
     } else {
@@ -151,7 +157,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
           for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
           if (i + D < n)
 #pragma unroll
-            for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + (int64_t)(i + D) * BB, q);
+            for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + (int64_t)(i + D) * 16 * BB, q);
           step(i, cur);
         }
       }
@@ -248,7 +254,7 @@ __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& i
 // loads for the next tile are in flight while the current one finishes.
 template <int FMT, int MODE, int WPB, int RT, int D, int G>
 __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const Item& it, int tile0, int tile_end,
-                                                   const u32x2* lut, char* xs) {
+                                                   const u32x2* lut, char* xs, char* scratch) {
   static_assert(G % D == 0 && D <= G, "the ring depth must divide the group count");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
@@ -268,18 +274,26 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
   for (int r = 0; r < RT; ++r) {
     int64_t off;
     if (MODE == MODE_GATEUP)  // r even: gate rows, r odd: up rows (RT == 2)
-      off = (r & 1) * gu_bytes + ((int64_t)first * 16 + i16) * row_bytes;
+      off = (r & 1) * gu_bytes + (int64_t)first * 16 * row_bytes;
     else
-      off = 2 * gu_bytes + (((int64_t)first * RT + r) * 16 + i16) * row_bytes;
-    rows[r] = bank + off;
+      off = 2 * gu_bytes + ((int64_t)first * RT + r) * 16 * row_bytes;
+    rows[r] = bank + off;  // the tile's base: chunk of group g at + g * 16 * BB
   }
 
-  u32x3 ring[D][RT];
+  // PQ2_0 streams aligned chunks and rearranges them through LDS; PTQ1_0, whose
+  // decoder already leans on LDS for its byte table, loads its windows directly
+  constexpr bool CH = FMT == kPQ2;
+  auto fetch = [&](const uint8_t* chunk) -> u32x4 {
+    if (CH) return load_chunk<FMT>(chunk, lane);
+    const u32x3 v = load_block_x3<FMT>(chunk + i16 * BB, q);
+    return u32x4{v.x, v.y, v.z, 0u};
+  };
+  u32x4 ring[D][RT];
   if (ntw > 0) {
 #pragma unroll
     for (int j = 0; j < D; ++j)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * BB, q);
+      for (int r = 0; r < RT; ++r) ring[j][r] = fetch(rows[r] + j * 16 * BB);
   }
 
   __syncthreads();  // the previous unit is done with the staging buffer
@@ -294,21 +308,13 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
     for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int g0 = 0; g0 < G; g0 += D) {
-      // the next D groups: the rest of this tile, else the start of the next one
-      const bool same = g0 + D < G;
-      const bool issue = same || more;
-      const uint8_t* nxt[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) nxt[r] = same ? rows[r] + (g0 + D) * BB : rows[r] + tile_stride;
+      // the next D groups: the rest of this tile, else the start of the next
+      // one; after the wave's last tile, its own first groups again (in
+      // bounds, unused).  The refills are unconditional so the compiler can
+      // wait for each ring slot alone instead of for every load in flight.
+      const int64_t nxt = g0 + D < G ? (int64_t)(g0 + D) * 16 * BB : (more ? tile_stride : 0);
 #pragma unroll
       for (int j = 0; j < D; ++j) {
-        u32x3 cur[RT];
-#pragma unroll
-        for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
-        if (issue) {
-#pragma unroll
-          for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(nxt[r] + j * BB, q);
-        }
         u32x4 A[4];
         const char* ap = arow + (g0 + j) * 256;
 #pragma unroll
@@ -316,7 +322,10 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           u32x4 W[4];
-          const float s = decode_block_x3<FMT>(cur[r], lut, lane, W);
+          const u32x3 v = CH ? chunk_window<FMT>(ring[j][r], scratch + r * kChunkScratch, lane)
+                             : u32x3{ring[j][r].x, ring[j][r].y, ring[j][r].z};
+          ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
+          const float s = decode_block_x3<FMT>(v, lut, lane, W);
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
@@ -343,6 +352,7 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
   u32x2* lut = (u32x2*)smem;
   char* xs = smem + lut_bytes;
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  char* scratch = xs + a.nmax * stage_stride(G * kGroup) + (threadIdx.x >> 6) * RT * kChunkScratch;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const int64_t units = (int64_t)(*a.n_items) * units_per_item;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
@@ -350,9 +360,9 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
     const int tile0 = (int)(u % units_per_item) * tiles_per_unit;
     const int tile_end = min(n_tiles, tile0 + tiles_per_unit);
     if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
-      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
+      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch);
     else
-      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs);
+      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch);
   }
 }
 
@@ -459,9 +469,9 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   for (int rt = 0; rt < 4; ++rt) {
     int64_t off;
     if (MODE == MODE_GATEUP)
-      off = (rt >> 1) * gu_bytes + (int64_t)(row0 + 16 * (rt & 1) + i16) * row_bytes;
+      off = (rt >> 1) * gu_bytes + (int64_t)(row0 + 16 * (rt & 1)) * row_bytes + i16 * BB;
     else
-      off = 2 * gu_bytes + (int64_t)(row0 + 16 * rt + i16) * row_bytes;
+      off = 2 * gu_bytes + (int64_t)(row0 + 16 * rt) * row_bytes + i16 * BB;
     wrow[rt] = bank + (active ? off : 0);
   }
 
@@ -530,7 +540,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
       for (int rt = 0; rt < 4; ++rt) {
         u32x4 W[4];
         const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-        ring[rt] = load_block_x3<FMT>(wrow[rt] + (int64_t)gn * BB, q);
+        ring[rt] = load_block_x3<FMT>(wrow[rt] + (int64_t)gn * 16 * BB, q);
         f32x4 tmp[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -659,13 +669,13 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 
   const uint8_t* rows[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt + i16) * row_bytes;
+  for (int rt = 0; rt < 4; ++rt) rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt) * row_bytes + i16 * BB;
   u32x3 ring0[4], ring1[4];
   if (nqw > 0) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
       ring0[rt] = load_block_x3<FMT>(rows[rt], q);
-      if (D == 2) ring1[rt] = load_block_x3<FMT>(rows[rt] + BB, q);
+      if (D == 2) ring1[rt] = load_block_x3<FMT>(rows[rt] + 16 * BB, q);
     }
   }
 
@@ -726,7 +736,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
         for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * stride + g * 256 + m * 64);
       // refill with group g + D of this quad, else of the next quad (the last
       // quad refetches its own groups: in bounds, unused)
-      const int64_t nxt = g + D < G ? (int64_t)(g + D) * BB : (more ? quad_stride : 0) + (int64_t)(g + D - G) * BB;
+      const int64_t nxt = g + D < G ? (int64_t)(g + D) * 16 * BB : (more ? quad_stride : 0) + (int64_t)(g + D - G) * 16 * BB;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         u32x4 W[4];
@@ -848,7 +858,8 @@ template <int MODE, int WPB, int RT, int D, int G, int FS, int WPE>
 static hipError_t launch_stream_fs(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
   constexpr int K = G * kGroup;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K);
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
+                     (size_t)WPB * RT * kChunkScratch;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = expert_stream_kernel<MODE, WPB, RT, D, G, FS, WPE>;
   int per_cu = 0;

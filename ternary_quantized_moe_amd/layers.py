@@ -6,14 +6,20 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-from .binding import pack, packed_bytes
+from .binding import pack, packed_bytes, tile_container
 
 BANK_SLACK = 16  # readable bytes the library needs after the last bank (MOE_BANK_SLACK)
 
 
 def pack_expert(fmt: int, trits, scales) -> np.ndarray:
-    """[gate, up, down] trits and fp16-bit scales -> one bank's container bytes."""
-    return np.concatenate([pack(fmt, t, s) for t, s in zip(trits, scales)])
+    """[gate, up, down] trits ([rows, cols] int8) and fp16-bit scales -> one
+    bank's bytes: each matrix packed row-major, then put in the tile-major block
+    order the expert kernels read."""
+    out = []
+    for t, s in zip(trits, scales):
+        rows, cols = np.shape(t)
+        out.append(tile_container(fmt, pack(fmt, t, s), rows, cols))
+    return np.concatenate(out)
 
 
 def build_banks(source, n_banks: int, formats: np.ndarray, d_model: int, d_ff: int, threads: int = 0):

@@ -149,7 +149,9 @@ def test_forward_validation_happens_before_launch():
     c6, keep6 = _fake_banks(nbytes=8 * 3 * 256 * 128 // 128 * 34 + 15)  # one byte short of the slack
     assert _forward_rc(c6) == -6 and "slack" in L.moe_last_error().decode()
     c5, keep5 = _fake_banks(offsets=np.arange(8) * 2)
-    assert _forward_rc(c5) == -1                      # offsets not multiples of 4
+    assert _forward_rc(c5) == -1                      # offsets not multiples of 16
+    c7, keep7 = _fake_banks(offsets=np.arange(8) * (3 * 256 * 128 // 128 * 34) + 4, nbytes=8 * 3 * 256 * 128 // 128 * 34 + 20)
+    assert _forward_rc(c7) == -1 and "multiple of 16" in L.moe_last_error().decode()
     assert L.moe_workspace_bytes(ctypes.byref(c), 16, 2, 16) > 0
     assert L.moe_workspace_bytes(None, 16, 2, 16) == -1
 
@@ -163,3 +165,40 @@ def test_route_validation():
     assert L.moe_route(0x1000, 0, 256, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 0, None) == 0
     assert L.moe_unpack_device(99, 1, 128, 1, 1, None) == -2
     assert L.moe_unpack_device(142, 1, 100, 1, 1, None) == -3
+
+
+def _plain_to_tiles(data, rows, cols, bb):
+    """The tile-major order written as a numpy reshape: [row tile][group][row in tile]."""
+    G = cols // 128
+    return data.reshape(rows // 16, 16, G, bb).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("fmt", [PQ2_0, PTQ1_0])
+def test_tile_container_is_the_tile_major_permutation(fmt):
+    rng = np.random.default_rng(5)
+    rows, cols = 48, 384
+    t = rng.integers(-1, 2, size=(rows, cols)).astype(np.int8)
+    s = (rng.integers(0, 0x3C00, size=rows * cols // 128)).astype(np.uint16)
+    plain = tq.pack(fmt, t, s)
+    tiled = tq.tile_container(fmt, plain, rows, cols)
+    assert np.array_equal(tiled, _plain_to_tiles(plain, rows, cols, tq.block_bytes(fmt)))
+    assert np.array_equal(tq.untile_container(fmt, tiled, rows, cols), plain)
+    # every block keeps its bytes: block (n, g) of the tiled order decodes to row n, group g
+    bb, G = tq.block_bytes(fmt), cols // 128
+    n, g = 37, 2
+    blk = tiled[(((n // 16) * G + g) * 16 + n % 16) * bb:][:bb]
+    tr, sc = tq.unpack(fmt, blk, 128)
+    assert np.array_equal(tr, t[n, 128 * g:128 * (g + 1)]) and int(sc[0]) == int(s[n * G + g])
+
+
+def test_tile_container_errors():
+    L = tq.lib()
+    src = np.zeros(34 * 3 * 16, np.uint8)
+    dst = np.zeros_like(src)
+    assert L.moe_tile_container(42, src.ctypes.data, 16, 384, dst.ctypes.data, dst.size) == -2
+    assert L.moe_tile_container(PQ2_0, src.ctypes.data, 8, 384, dst.ctypes.data, dst.size) == -3
+    assert L.moe_tile_container(PQ2_0, src.ctypes.data, 16, 200, dst.ctypes.data, dst.size) == -3
+    assert L.moe_tile_container(PQ2_0, src.ctypes.data, 16, 384, dst.ctypes.data, dst.size - 1) == -6
+    assert L.moe_untile_container(PQ2_0, src.ctypes.data, 16, 384, src.ctypes.data, src.size) == -1
+    assert L.moe_tile_container(PQ2_0, None, 16, 384, dst.ctypes.data, dst.size) == -1
+    assert L.moe_tile_container(PQ2_0, src.ctypes.data, 16, 384, dst.ctypes.data, dst.size) == 0

@@ -76,11 +76,26 @@ def test_unpack_device_real_banks(name):
 
 
 def test_library_packing_equals_oracle_packing():
+    """The device banks are the oracle's containers with each matrix in the
+    tile-major block order ([row tile][group][row in tile], written here as a
+    numpy reshape)."""
+    tq = tq_mod()
     L = Layer("skewed")
+    c = L.cfg
     data, offsets = L.host_bytes()
+    shapes = [(c.d_ff, c.d_model), (c.d_ff, c.d_model), (c.d_model, c.d_ff)]
     for e in (0, 1, 250, 511, 512):
         ref = L.oracle_banks.container(e)
-        assert np.array_equal(data[offsets[e]:offsets[e] + ref.size], ref), e
+        fmt = int(L.formats[e])
+        bb = tq.block_bytes(fmt)
+        pos, mine = 0, data[offsets[e]:offsets[e] + ref.size]
+        for rows, cols in shapes:
+            n = rows * cols // 128 * bb
+            G = cols // 128
+            want = ref[pos:pos + n].reshape(rows // 16, 16, G, bb).transpose(0, 2, 1, 3).reshape(-1)
+            assert np.array_equal(mine[pos:pos + n], want), e
+            assert np.array_equal(tq.untile_container(fmt, mine[pos:pos + n], rows, cols), ref[pos:pos + n])
+            pos += n
 
 
 # ------------------------------------------------------------------ routing
