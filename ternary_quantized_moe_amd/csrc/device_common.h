@@ -199,7 +199,7 @@ __host__ __device__ constexpr int block_bytes_c() {
 // reads the chunk as BB pieces of 16 bytes (lanes past BB - 1 repeat the last
 // piece) and rearranges it through a per-wave LDS scratch into the same
 // per-lane window.
-constexpr int kChunkScratch = 16 * 34 + 32;  // bytes of scratch per chunk (PQ2_0 size + read-past slack)
+constexpr int kChunkScratch = 64 * 16;  // bytes of scratch per chunk: one 16-byte piece per lane
 
 template <int FMT>
 __device__ __forceinline__ u32x4 load_chunk(const uint8_t* chunk, int lane) {
@@ -210,7 +210,9 @@ __device__ __forceinline__ u32x4 load_chunk(const uint8_t* chunk, int lane) {
 template <int FMT>
 __device__ __forceinline__ u32x3 chunk_window(u32x4 piece, char* scratch, int lane) {
   constexpr int BB = block_bytes_c<FMT>();
-  if (lane < BB) *(u32x4*)(scratch + 16 * lane) = piece;
+  // every lane writes (lanes past BB - 1 a repeat of the last piece, past the
+  // chunk), so no branch splits the caller's loop body
+  *(u32x4*)(scratch + 16 * lane) = piece;
   // the wave's LDS operations complete in order; the fences keep the compiler
   // from moving the reads above the writes
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

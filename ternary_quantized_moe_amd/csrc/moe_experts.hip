@@ -24,6 +24,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -450,7 +451,7 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 // branches, so the independent MFMA chains of the token tiles interleave).
 template <int FMT, int MODE, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
-                                          char* bufs) {
+                                          char* bufs, char* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int K = MODE == MODE_GATEUP ? a.d : a.f;
@@ -469,11 +470,19 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   for (int rt = 0; rt < 4; ++rt) {
     int64_t off;
     if (MODE == MODE_GATEUP)
-      off = (rt >> 1) * gu_bytes + (int64_t)(row0 + 16 * (rt & 1)) * row_bytes + i16 * BB;
+      off = (rt >> 1) * gu_bytes + (int64_t)(row0 + 16 * (rt & 1)) * row_bytes;
     else
-      off = 2 * gu_bytes + (int64_t)(row0 + 16 * rt) * row_bytes + i16 * BB;
-    wrow[rt] = bank + (active ? off : 0);
+      off = 2 * gu_bytes + (int64_t)(row0 + 16 * rt) * row_bytes;
+    wrow[rt] = bank + (active ? off + i16 * BB : 0);  // the lane's row; group g at + g * 16 * BB
   }
+  // the lane's 12-byte window directly: here the LDS is busy with the
+  // activation operands, and rearranging aligned chunks through it measured no
+  // faster (the down projection below does use them)
+  constexpr bool CH = false;
+  static_assert(!CH, "the gate/up kernel reads 12-byte windows");
+  (void)scratch;
+  using RingT = u32x3;
+  auto fetch = [&](const uint8_t* p) -> RingT { return load_block_x3<FMT>(p, q); };
 
   // staging roles of the thread: token row si, quarter sq, half sh of the
   // 64 x 8 half quarters of a group
@@ -499,10 +508,10 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 
   // weights of the next group in flight (a group step is long enough to cover
   // the load latency)
-  u32x3 ring[4];
+  RingT ring[4];
   if (active) {
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) ring[rt] = load_block_x3<FMT>(wrow[rt], q);
+    for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt]);
   }
   u32x4 sraw[P][2];
   __syncthreads();  // the previous unit is done with the staging buffers
@@ -540,7 +549,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
       for (int rt = 0; rt < 4; ++rt) {
         u32x4 W[4];
         const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-        ring[rt] = load_block_x3<FMT>(wrow[rt] + (int64_t)gn * 16 * BB, q);
+        ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
         f32x4 tmp[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -599,9 +608,9 @@ template <int MODE, int FS, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                               char* bufs, bool ptq1) {
   if (FS != 1 && ptq1)
-    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs);
+    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
   else if (FS != 2)
-    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs);
+    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
 }
 
 // Persistent blocks over units.  Unit l = (item l / row_blocks, row block
@@ -651,8 +660,9 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
-template <int FMT, int NTT, int G>
-__device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs) {
+template <int FMT, int NTT, int G, bool CHK>
+__device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
+                                          char* scratch) {
   const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, q = lane >> 4;
@@ -669,13 +679,32 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 
   const uint8_t* rows[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt) * row_bytes + i16 * BB;
-  u32x3 ring0[4], ring1[4];
+  for (int rt = 0; rt < 4; ++rt)  // chunk path: the tile's base; window path: the lane's row
+    rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt) * row_bytes + (CHK && FMT == kPQ2 ? 0 : i16 * BB);
+  // CHK (kernels for PQ2_0-only layers): aligned chunk pieces rearranged
+  // through the wave's LDS scratch; otherwise the lane's 12-byte window directly
+  // (the PTQ1_0 decoder already leans on LDS, and the mixed kernel has no
+  // registers to spare)
+  constexpr bool CH = CHK && FMT == kPQ2;
+  using RingT = std::conditional_t<CH, u32x4, u32x3>;
+  auto fetch = [&](const uint8_t* chunk) -> RingT {
+    if constexpr (CH)
+      return load_chunk<FMT>(chunk, lane);
+    else
+      return load_block_x3<FMT>(chunk, q);
+  };
+  auto window = [&](const RingT& r) -> u32x3 {
+    if constexpr (CH)
+      return chunk_window<FMT>(r, scratch, lane);
+    else
+      return r;
+  };
+  RingT ring0[4], ring1[4];
   if (nqw > 0) {
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      ring0[rt] = load_block_x3<FMT>(rows[rt], q);
-      if (D == 2) ring1[rt] = load_block_x3<FMT>(rows[rt] + 16 * BB, q);
+      ring0[rt] = fetch(rows[rt]);
+      if (D == 2) ring1[rt] = fetch(rows[rt] + 16 * BB);
     }
   }
 
@@ -728,7 +757,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    auto step = [&](int g, u32x3 (&ring)[4]) {
+    auto step = [&](int g, RingT (&ring)[4]) {
       u32x4 A[NTT][4];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
@@ -740,8 +769,15 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         u32x4 W[4];
-        const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-        ring[rt] = load_block_x3<FMT>(rows[rt] + nxt, q);
+        float sc;
+        if constexpr (CH) {
+          const u32x3 v = window(ring[rt]);
+          ring[rt] = fetch(rows[rt] + nxt);
+          sc = decode_block_x3<FMT>(v, lut, lane, W);
+        } else {
+          sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+          ring[rt] = fetch(rows[rt] + nxt);
+        }
         f32x4 tmp[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -783,15 +819,17 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 template <int FS, int NTT, int G>
 __device__ __forceinline__ void down_dispatch(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                               bool ptq1) {
+  char* scratch = xs + kGemmChunk * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
   if (FS != 1 && ptq1)
-    down_unit<kPTQ1, NTT, G>(a, it, lut, xs);
+    down_unit<kPTQ1, NTT, G, false>(a, it, lut, xs, scratch);
   else if (FS != 2)
-    down_unit<kPQ2, NTT, G>(a, it, lut, xs);
+    down_unit<kPQ2, NTT, G, FS == 1>(a, it, lut, xs, scratch);
 }
 
 // Persistent blocks over items, the blocks of one XCD taking a contiguous range
 // (so the items of one expert share its down weights in one L2).
 // Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][64 staged rows][64 slots][64 weights]
+// [per-wave chunk scratch]
 template <int FS, int G>
 __global__ __launch_bounds__(64 * kDownWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void down_resident_kernel(ExpertArgs a) {
@@ -939,7 +977,8 @@ static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, s
 // Down projection of a large batch: LDS-resident h rows where the shape is
 // compiled in and the rows fit, else the group-staged kernel.
 static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, hipStream_t s) {
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kGemmChunk * (stage_stride(a.f) + 8);
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kGemmChunk * (stage_stride(a.f) + 8) +
+                     (size_t)kDownWaves * kChunkScratch;
   if (lds <= 160 * 1024) {
     switch (a.f / kGroup) {
       case 8: return launch_down_resident<8>(a, mi, lds, s);
