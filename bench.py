@@ -298,6 +298,19 @@ def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     return rec
 
 
+def calibrate_copy(mib: int, reps: int = 5):
+    """Plain device copies of known size: each reads and writes mib MiB once."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "copies": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +320,9 @@ def main():
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run plain device-to-device copies of MIB MiB (the reference kernel for "
+                         "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -314,6 +330,9 @@ def main():
               f"cross-GPU exchange, and this build runs on a single MI355X (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.sweep:
         names = [n for n in WORKLOADS if not args.only or n in args.only.split(",")]
         for name in names:
