@@ -244,6 +244,94 @@ hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
 
+// ------------------------------------------------------------ wave primitives
+// Exchanges inside rows of 16 lanes go through DPP (no LDS round trip):
+// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 1 and 2 apart, the half-row and
+// row mirrors pair the two quads of each half and the two halves of each row.
+// After the four steps every lane of a row holds the row's reduction; the four
+// rows are then combined from one lane each with readlane.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
+}
+__device__ __forceinline__ float readlane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+constexpr int kNoExpert = 0x7fffffff;
+
+// (bv, be) <- the better of (bv, be) and (ov, oe): larger value, equal values to
+// the lower index; kNoExpert marks an empty candidate.
+__device__ __forceinline__ void argmax_take(float& bv, int& be, float ov, int oe) {
+  const bool take = oe != kNoExpert && (be == kNoExpert || ov > bv || (ov == bv && oe < be));
+  if (take) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+// Wave-wide argmax: every lane returns with the same winner.
+__device__ __forceinline__ void wave_argmax(float& bv, int& be) {
+  argmax_take(bv, be, dpp_f32<kDppXor1>(bv), dpp_i32<kDppXor1>(be));
+  argmax_take(bv, be, dpp_f32<kDppXor2>(bv), dpp_i32<kDppXor2>(be));
+  argmax_take(bv, be, dpp_f32<kDppHalfMirror>(bv), dpp_i32<kDppHalfMirror>(be));
+  argmax_take(bv, be, dpp_f32<kDppMirror>(bv), dpp_i32<kDppMirror>(be));
+  float rv = readlane_f32(bv, 0);
+  int re = __builtin_amdgcn_readlane(be, 0);
+#pragma unroll
+  for (int r = 1; r < 4; ++r) argmax_take(rv, re, readlane_f32(bv, 16 * r), __builtin_amdgcn_readlane(be, 16 * r));
+  bv = rv;
+  be = re;
+}
+
+// Wave-wide sum: every lane returns the same value (rows summed in row order).
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
+}
+
+// Inclusive prefix sum over the lanes of a wave: shifts by 1, 2, 4, 8 inside
+// each row (lanes shifted in from outside the row read 0), then each row adds
+// the totals of the rows before it.
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppShr1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppShr2, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppShr4, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppShr8, 0xF, 0xF, true);
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Inclusive prefix sum over the 1024 threads of a block; *total receives the
+// block's sum.  wsum: 16 ints of shared memory.  Every thread must call it.
+__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_inclusive_scan(v, lane);
+  __syncthreads();  // wsum may still be read by a previous scan
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < 16; ++w) {
+    const int s = wsum[w];
+    before += w < wave ? s : 0;
+    all += s;
+  }
+  *total = all;
+  return v + before;
+}
+
 // One wave selects the top k of token t.  Every lane ends each round knowing
 // the round's winner, so lane i % 64 keeps the i-th selected logit in a
 // register for the softmax.  sidx: NULL, or LDS that also receives the indices.
@@ -268,26 +356,16 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int la
   float m = 0.f;
   for (int i = 0; i < k; ++i) {
     float bv = 0.f;
-    int be = 0x7fffffff;
+    int be = kNoExpert;
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
       if (!((avail >> c) & 1u)) continue;
-      if (be == 0x7fffffff || v[c] > bv) {  // e grows with c, so ties keep the lower e
+      if (be == kNoExpert || v[c] > bv) {  // e grows with c, so ties keep the lower e
         bv = v[c];
         be = lane + 64 * c;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const bool take = (oe != 0x7fffffff) &&
-                        (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (take) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    wave_argmax(bv, be);
     if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
     if (i == 0) m = bv;
 #pragma unroll
@@ -303,9 +381,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int la
 #pragma unroll
   for (int c = 0; c < MV; ++c)
     if (64 * c + lane < k) part += __expf(mv[c] - m);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-  const float inv = 1.f / part;
+  const float inv = 1.f / wave_sum(part);
 #pragma unroll
   for (int c = 0; c < MV; ++c)
     if (64 * c + lane < k) a.w[t * k + 64 * c + lane] = __expf(mv[c] - m) * inv;
@@ -354,7 +430,7 @@ __global__ __launch_bounds__(256) void rank_kernel(RouteArgs a) {
 
 // One block of 1024 threads, thread = expert.
 __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
-  __shared__ int sh[1024];
+  __shared__ int wsum[16];
   const int e = threadIdx.x;
   const int E = a.E;
   int total = 0;
@@ -366,35 +442,19 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
     }
   }
   // exclusive scan of totals
-  sh[e] = total;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? sh[e - off] : 0;
-    __syncthreads();
-    sh[e] += v;
-    __syncthreads();
-  }
-  const int off_e = sh[e] - total;
+  int unused;
+  const int off_e = block_inclusive_scan(total, wsum, &unused) - total;
   if (e < E) {
     a.counts[e] = total;
     a.offsets[e] = off_e;
     for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off_e;
   }
   if (e == 0) a.offsets[E] = (int)(a.T * a.k);
-  __syncthreads();
   // work items: ceil(count / chunk) per routed expert, then the shared experts
   const int C = a.chunk;
   const int chunks = e < E ? (total + C - 1) / C : 0;
-  sh[e] = chunks;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? sh[e - off] : 0;
-    __syncthreads();
-    sh[e] += v;
-    __syncthreads();
-  }
-  const int istart = sh[e] - chunks;
-  const int routed_items = sh[1023];
+  int routed_items;
+  const int istart = block_inclusive_scan(chunks, wsum, &routed_items) - chunks;
   for (int c = 0; c < chunks; ++c) {
     Item it;
     it.bank = e;
@@ -432,13 +492,14 @@ __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
 // for such a batch).  PER = 0: after topk_kernel.  PER > 0 (T <= kFusedMaxT
 // and T k <= kFusedMaxSlots): the block's 16 waves first select the top k of
 // the tokens themselves, keeping the indices in LDS, which saves a launch.
-constexpr int kFusedMaxT = 16;  // one token per wave
+constexpr int kFusedMaxT = 16;  // one token per wave: beyond that one CU does too much of the top-k
 constexpr int kFusedMaxSlots = 4096;
 
 template <int PER>
 __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   __shared__ unsigned long long mask[kGroupMaxT / 64][kMaxExperts];
   __shared__ int scan_buf[1024];
+  __shared__ int wsum[16];
   __shared__ int sidx[PER > 0 ? kFusedMaxSlots : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.E, k = a.k;
@@ -461,32 +522,16 @@ __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   int total = 0;
   if (e < E)
     for (int c = 0; c < nchunks; ++c) total += __popcll(mask[c][e]);
-  scan_buf[e] = total;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? scan_buf[e - off] : 0;
-    __syncthreads();
-    scan_buf[e] += v;
-    __syncthreads();
-  }
-  const int off_e = scan_buf[e] - total;
+  int unused;
+  const int off_e = block_inclusive_scan(total, wsum, &unused) - total;
   if (e < E) {
     a.counts[e] = total;
     a.offsets[e] = off_e;
   }
   if (e == 0) a.offsets[E] = T * k;
-  __syncthreads();
   const int chunks = e < E ? (total + kChunk - 1) / kChunk : 0;
-  scan_buf[e] = chunks;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = e >= off ? scan_buf[e - off] : 0;
-    __syncthreads();
-    scan_buf[e] += v;
-    __syncthreads();
-  }
-  const int istart = scan_buf[e] - chunks;
-  const int routed_items = scan_buf[1023];
+  int routed_items;
+  const int istart = block_inclusive_scan(chunks, wsum, &routed_items) - chunks;
   for (int c = 0; c < chunks; ++c) {
     Item it;
     it.bank = e;
