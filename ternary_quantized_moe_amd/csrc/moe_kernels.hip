@@ -203,6 +203,81 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
   }
 }
 
+// Combine of a small batch: a block covers 64 model rows (4 row tiles) x 16
+// tokens with 16 waves = 4 row tiles x 4 slices of K.  The slices' partial
+// sums meet in shared memory and are added in slice order; then each of 128
+// threads adds one token's slots to 8 consecutive rows with 16-byte reads, so
+// a slot row is read in 128-byte pieces.
+__global__ __launch_bounds__(1024) void combine_small_kernel(DenseArgs a) {
+  __shared__ float part[4][16][64 + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int rt = wave & 3, ks = wave >> 2;
+  const int d = a.N0, K = a.K;
+  const int n = blockIdx.x * 64 + rt * 16 + i16;  // d is a multiple of 64
+  const int64_t t0 = (int64_t)blockIdx.y * 16;
+  const uint16_t* zrow = a.act + std::min<int64_t>(t0 + i16, a.T - 1) * a.lda;
+  const uint16_t* wrow = a.w0 ? a.w0 + (int64_t)n * K : nullptr;
+  const int nsteps = (K + 31) / 32, spw = (nsteps + 3) / 4;
+  const int s_begin = ks * spw, s_end = min(nsteps, s_begin + spw);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int SB = 4;  // k-steps whose loads are in flight together
+  for (int s0 = s_begin; s0 < s_end; s0 += SB) {
+    u32x4 wv[SB], zv[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int kb = 32 * (s0 + j) + 8 * q;
+      const bool kin = wrow && s0 + j < s_end && kb < K;
+      wv[j] = kin ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      zv[j] = kin ? *(const u32x4*)(zrow + kb) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      u32x4 hi, lo;
+      split_f16x8(wv[j], hi, lo);
+      acc = mfma16(zv[j], hi, acc);
+      acc = mfma16(zv[j], lo, acc);
+    }
+  }
+  // lane holds tokens 4q + j of the tile, row rt * 16 + i16 of the block
+#pragma unroll
+  for (int j = 0; j < 4; ++j) part[ks][4 * q + j][rt * 16 + i16] = acc[j];
+  __syncthreads();
+  if (threadIdx.x >= 128) return;
+  const int tl = threadIdx.x >> 3, c = threadIdx.x & 7;
+  const int64_t t = t0 + tl;
+  if (t >= a.T) return;
+  const int n0 = blockIdx.x * 64 + 8 * c;
+  float v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    v[e] = ((part[0][tl][8 * c + e] + part[1][tl][8 * c + e]) + part[2][tl][8 * c + e]) + part[3][tl][8 * c + e];
+  const int64_t Tk = a.T * a.top_k;
+  const int ns = a.top_k + a.n_shared;
+  for (int i0 = 0; i0 < ns; i0 += 8) {  // slots in order, eight reads in flight
+    u32x4 sv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u;
+      const int64_t slot = i < a.top_k ? t * a.top_k + i : Tk + (int64_t)(i - a.top_k) * a.T + t;
+      sv[u] = i < ns ? *(const u32x4*)(a.slots + slot * d + n0) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (i0 + u >= ns) break;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] += bf16_to_f32(sv[u][e] & 0xFFFFu);
+        v[2 * e + 1] += bf16_to_f32(sv[u][e] >> 16);
+      }
+    }
+  }
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(v[2 * e]) | (f32_to_bf16(v[2 * e + 1]) << 16);
+  *(u32x4_a4*)(a.y + t * d + n0) = o;
+}
+
 template <int EPI, int MT>
 static void launch_dense_mt(const DenseArgs& a, int N, hipStream_t stream) {
   dim3 grid((unsigned)((N + 15) / 16), (unsigned)((a.T + 16 * MT - 1) / (16 * MT)));
@@ -236,7 +311,9 @@ hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
   if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_COMBINE>(a, a.N0, stream);
-  return launch_dense<EPI_COMBINE>(a, a.N0, stream);
+  const dim3 grid((unsigned)(a.N0 / 64), (unsigned)((a.T + 15) / 16));
+  combine_small_kernel<<<grid, 1024, 0, stream>>>(a);
+  return hipGetLastError();
 }
 
 // ============================================================ routing
