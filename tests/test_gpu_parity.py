@@ -199,6 +199,29 @@ def test_mixed_formats_with_shared_expert():
         assert row_metric(y.cpu().numpy().view(np.uint16), ref.y).max() <= TOL
 
 
+MANY_EXPERTS = LayerConfig("many", 22, 256, 1000, 128, 9, 0, 16, "pq2_0")
+
+
+@pytest.mark.parametrize("T", [20, 300])
+def test_many_experts(T):
+    """E = 1000 (> 512): the 16-logits-per-lane top-k, the grouping over up to
+    1024 experts, and banks spread over a large buffer."""
+    tq = tq_mod()
+    L = Layer(MANY_EXPERTS)
+    c = L.cfg
+    x_bits = L.gen.tokens(T, 8)
+    d = L.tensors(x_bits)
+    say(f"many experts T={T}")
+    r = tq.route(d["x"], d["router"], d["delta"], c.n_experts, c.top_k)
+    y = tq.forward(d["x"], d["router"], d["delta"], L.device(), d["a"], d["b"], c.top_k)
+    torch.cuda.synchronize()
+    toks = sample_tokens(T, 24)
+    idx, _ = check_routing(L, x_bits, r, toks)
+    ref = omoe.forward(x_bits[toks], L.router, L.delta, L.oracle_banks, L.corr_a, L.corr_b, c.top_k,
+                       forced_idx=idx[toks])
+    assert row_metric(y.cpu().numpy().view(np.uint16)[toks], ref.y).max() <= TOL
+
+
 def run_fwd(L, x_bits, k=None, use_delta=True, use_corr=True, corr_b=None, banks=None):
     tq = tq_mod()
     d = L.tensors(x_bits, use_delta, use_corr, corr_b)
