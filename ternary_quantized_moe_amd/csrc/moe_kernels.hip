@@ -512,10 +512,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   const int E = a.E;
   int total = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int c = a.block_cnt[(int64_t)b * E + e];
-      a.block_base[(int64_t)b * E + e] = total;
-      total += c;
+    // the expert's per-block counts, eight loads in flight at a time
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = b0 + j < nb ? a.block_cnt[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (b0 + j < nb) a.block_base[(int64_t)(b0 + j) * E + e] = total;
+        total += c[j];
+      }
     }
   }
   // exclusive scan of totals
@@ -524,7 +530,14 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   if (e < E) {
     a.counts[e] = total;
     a.offsets[e] = off_e;
-    for (int b = 0; b < nb; ++b) a.block_base[(int64_t)b * E + e] += off_e;
+    for (int b0 = 0; b0 < nb; b0 += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = b0 + j < nb ? a.block_base[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (b0 + j < nb) a.block_base[(int64_t)(b0 + j) * E + e] = v[j] + off_e;
+    }
   }
   if (e == 0) a.offsets[E] = (int)(a.T * a.k);
   // work items: ceil(count / chunk) per routed expert, then the shared experts
