@@ -60,7 +60,7 @@ int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t T, Tk, n_pos, nb, max_items;
-  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, h, slots;
+  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, xpart, h, slots;
   bool large;
   int64_t route_end, total;
 };
@@ -89,6 +89,9 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
   p.large = T > moe::kGroupMaxT;
   p.wsplit = o;
   if (p.large) o += up(std::max(moe::dense_split_bytes(E + r, d), moe::dense_split_bytes(d, r)));
+  // small batches: fp32 x-projection partials over the K slices
+  p.xpart = o;
+  if (!p.large && T > 0) o += up((int64_t)moe::xproj_split(d).splits * T * (E + r) * 4);
   p.route_end = o;
   p.z = o; o += up(T * (int64_t)r * 2);
   p.h = o; o += up(p.n_pos * f * 2);
@@ -350,6 +353,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.logits = logits;
   da.z = at<uint16_t>(ws, p.z);
   da.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
+  da.part = p.large ? nullptr : at<float>(ws, p.xpart);
   hipError_t e = stage_mark(0, false, stream);
   if (e == hipSuccess) e = moe::launch_xproj(da, stream);
   if (e == hipSuccess) e = stage_mark(0, true, stream);
@@ -372,6 +376,13 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.items = at<moe::Item>(ws, p.items);
   ra.n_items = at<int32_t>(ws, p.nitems);
   ra.chunk = moe::item_chunk(T);
+  if (!p.large) {  // the routing adds up the partials: the logits, and z for the combine
+    ra.lpart = da.part;
+    ra.lsplits = moe::xproj_split(d).splits;
+    ra.lN = da.N0 + da.N1;
+    ra.z = da.N1 > 0 ? da.z : nullptr;
+    ra.zr = da.N1;
+  }
   e = stage_mark(1, false, stream);
   if (e == hipSuccess) e = moe::launch_route(ra, p.max_items, stream);
   if (e == hipSuccess) e = stage_mark(1, true, stream);

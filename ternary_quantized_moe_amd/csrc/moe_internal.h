@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 namespace moe {
 
 constexpr int kGroup = 128;     // weights per container group
@@ -47,13 +49,32 @@ struct DenseArgs {
   uint16_t* y;     // bf16 [T x N0]
   // large batches: workspace for the split weights, dense_split_bytes(N0 + N1, K)
   void* wsplit;
+  // small batches (T <= kGroupMaxT): fp32 partial products [splits][T][N0 + N1]
+  // over the K slices of xproj_split(), added up by their consumers
+  float* part;
 };
+
+// Small-batch x-projection split: each block covers one 16-row tile, one group
+// of up to 64 tokens and one slice of 128 * kpw inputs (kpw 32-wide steps per
+// wave); at most eight slices.  The slicing depends on K alone, so a token's
+// logits come out the same whatever the batch and whether the correction rows
+// share the launch.
+struct XprojSplit {
+  int kpw, splits;
+};
+inline XprojSplit xproj_split(int K) {
+  const int steps = (K + 31) / 32;
+  XprojSplit s;
+  s.kpw = std::max(1, (steps + 31) / 32);
+  s.splits = (steps + 4 * s.kpw - 1) / (4 * s.kpw);
+  return s;
+}
 
 constexpr int EPI_XPROJ = 0;
 constexpr int EPI_COMBINE = 1;
 
 struct RouteArgs {
-  const float* logits;  // [T x E]
+  float* logits;        // [T x E]
   int64_t T;
   int E;
   int k;
@@ -69,6 +90,16 @@ struct RouteArgs {
   Item* items;          // [max_items]
   int32_t* n_items;     // [1]
   int chunk;            // tokens per work item, item_chunk(T)
+  // NULL, or the x-projection partials [lsplits][T][lN] whose first E columns
+  // sum (in slice order) to the logits; the top-k then also stores the sums
+  // into logits
+  const float* lpart;
+  int lsplits, lN;
+  // NULL, or z (bf16 [T x zr]) to receive the sums of the same partials'
+  // columns E .. E + zr - 1: blocks beyond the routing blocks of the first
+  // routing launch add them up while the routing runs
+  uint16_t* z;
+  int zr;
 };
 
 struct ExpertArgs {

@@ -203,6 +203,89 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
   }
 }
 
+// Small-batch x-projection with K split across blocks (xproj_split): block
+// (row tile, K slice, group of up to 64 tokens) has 4 waves, each taking kpw
+// 32-wide steps of the slice for all MT token tiles with every load of a batch
+// of steps in flight at once.  The waves' sums meet in shared memory in wave
+// order and the block stores one fp32 partial; the partials are added in slice
+// order by their consumers, so no block waits for another and the weight bytes
+// spread over the whole chip.
+template <int MT>
+__global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) {
+  __shared__ f32x4 red[3][MT][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int N = a.N0 + a.N1;
+  const int n = blockIdx.x * 16 + i16;
+  const int64_t t0 = (int64_t)blockIdx.z * 64;
+  const int nsteps = (a.K + 31) / 32;
+  const int s_begin = (blockIdx.y * 4 + wave) * kpw, s_end = min(nsteps, s_begin + kpw);
+
+  const uint16_t* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int64_t t = t0 + 16 * m + i16;
+    arow[m] = t < a.T ? a.act + t * a.lda : nullptr;
+  }
+  const uint16_t* wrow = nullptr;
+  const uint16_t* wrowb = nullptr;
+  if (n < a.N0) {
+    wrow = a.w0 + (int64_t)n * a.K;
+    if (a.w0b) wrowb = a.w0b + (int64_t)n * a.K;
+  } else if (n < N) {
+    wrow = a.w1 + (int64_t)(n - a.N0) * a.K;
+  }
+  const bool summed = wrowb != nullptr;
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int SB = 4;  // steps whose loads are in flight together
+  for (int s0 = s_begin; s0 < s_end; s0 += SB) {
+    u32x4 wv[SB], wb[SB], av[SB][MT];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int kb = 32 * (s0 + j) + 8 * q;
+      const bool kin = s0 + j < s_end && kb < a.K;
+      wv[j] = (wrow && kin) ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      wb[j] = (summed && kin) ? *(const u32x4_a4*)(wrowb + kb) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+        av[j][m] = (arow[m] && kin) ? *(const u32x4*)(arow[m] + kb) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      if (s0 + j >= s_end) break;
+      u32x4 hi, lo;
+      if (summed)
+        split_sum_f16x8(wv[j], wb[j], hi, lo);
+      else
+        split_f16x8(wv[j], hi, lo);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        acc[m] = mfma16(av[j][m], hi, acc[m]);
+        acc[m] = mfma16(av[j][m], lo, acc[m]);
+      }
+    }
+  }
+  if (wave > 0)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) red[wave - 1][m][lane] = acc[m];
+  __syncthreads();
+  if (wave > 0 || n >= N) return;
+  float* out = a.part + (int64_t)blockIdx.y * a.T * N;
+  // lane holds tokens t0 + 16m + 4q + j, row n
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const f32x4 v = ((acc[m] + red[0][m][lane]) + red[1][m][lane]) + red[2][m][lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + 16 * m + 4 * q + j;
+      if (t < a.T) out[t * N + n] = v[j];
+    }
+  }
+}
+
 // Combine of a small batch: a block covers 64 model rows (4 row tiles) x 16
 // tokens with 16 waves = 4 row tiles x 4 slices of K.  The slices' partial
 // sums meet in shared memory and are added in slice order; then each of 128
@@ -305,8 +388,19 @@ static hipError_t launch_dense(const DenseArgs& a, int N, hipStream_t stream) {
 
 // Large batches take the LDS-tiled matrix-core kernels (moe_dense.hip).
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
-  if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_XPROJ>(a, a.N0 + a.N1, stream);
-  return launch_dense<EPI_XPROJ>(a, a.N0 + a.N1, stream);
+  const int N = a.N0 + a.N1;
+  if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_XPROJ>(a, N, stream);
+  if (a.T <= kGroupMaxT && a.part) {
+    const XprojSplit sp = xproj_split(a.K);
+    const dim3 grid((unsigned)((N + 15) / 16), (unsigned)sp.splits, (unsigned)((a.T + 63) / 64));
+    const int mt = (int)std::min<int64_t>(4, (a.T + 15) / 16);
+    if (mt == 1) xproj_split_kernel<1><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    else if (mt == 2) xproj_split_kernel<2><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    else if (mt == 3) xproj_split_kernel<3><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    else xproj_split_kernel<4><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    return hipGetLastError();
+  }
+  return launch_dense<EPI_XPROJ>(a, N, stream);
 }
 
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
@@ -342,30 +436,49 @@ __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-constexpr int kNoExpert = 0x7fffffff;
+// Top-k candidates as 64-bit keys whose unsigned order is the selection
+// order.  High word: the fp32 logit mapped to an order-preserving integer
+// (-0.0 taken as +0.0; logits are finite); low word: the complemented expert
+// index, so of two equal logits the lower expert ranks first.  Key 0 lies
+// below every candidate and marks a used or absent one.
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  uint32_t u = __float_as_uint(v);
+  u = u == 0x80000000u ? 0u : u;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// (bv, be) <- the better of (bv, be) and (ov, oe): larger value, equal values to
-// the lower index; kNoExpert marks an empty candidate.
-__device__ __forceinline__ void argmax_take(float& bv, int& be, float ov, int oe) {
-  const bool take = oe != kNoExpert && (be == kNoExpert || ov > bv || (ov == bv && oe < be));
-  if (take) {
-    bv = ov;
-    be = oe;
-  }
+// x from another lane (DPP pattern CTRL) in the rows of ROWS; other rows keep x.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
+  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
+  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
+  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
+  return ((uint64_t)h << 32) | l;
 }
 
-// Wave-wide argmax: every lane returns with the same winner.
-__device__ __forceinline__ void wave_argmax(float& bv, int& be) {
-  argmax_take(bv, be, dpp_f32<kDppXor1>(bv), dpp_i32<kDppXor1>(be));
-  argmax_take(bv, be, dpp_f32<kDppXor2>(bv), dpp_i32<kDppXor2>(be));
-  argmax_take(bv, be, dpp_f32<kDppHalfMirror>(bv), dpp_i32<kDppHalfMirror>(be));
-  argmax_take(bv, be, dpp_f32<kDppMirror>(bv), dpp_i32<kDppMirror>(be));
-  float rv = readlane_f32(bv, 0);
-  int re = __builtin_amdgcn_readlane(be, 0);
-#pragma unroll
-  for (int r = 1; r < 4; ++r) argmax_take(rv, re, readlane_f32(bv, 16 * r), __builtin_amdgcn_readlane(be, 16 * r));
-  bv = rv;
-  be = re;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Wave-wide maximum key, returned in every lane, with compares and selects
+// only: four exchanges inside each row of 16 lanes; then lane 15 of rows 0 and
+// 2 folds into rows 1 and 3, and lane 31 (rows 0-1) into rows 2 and 3, which
+// leaves the maximum in lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
+  x = umax64(x, dpp_u64<kDppXor1, 0xF>(x));
+  x = umax64(x, dpp_u64<kDppXor2, 0xF>(x));
+  x = umax64(x, dpp_u64<kDppHalfMirror, 0xF>(x));
+  x = umax64(x, dpp_u64<kDppMirror, 0xF>(x));
+  x = umax64(x, dpp_u64<kDppRowBcast15, 0xA>(x));
+  x = umax64(x, dpp_u64<kDppRowBcast31, 0xC>(x));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // Wave-wide sum: every lane returns the same value (rows summed in row order).
@@ -409,59 +522,109 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* wsum, int* total
   return v + before;
 }
 
-// One wave selects the top k of token t.  Every lane ends each round knowing
-// the round's winner, so lane i % 64 keeps the i-th selected logit in a
-// register for the softmax.  sidx: NULL, or LDS that also receives the indices.
-template <int PER>  // logits per lane: E <= 64 * PER
+// One wave selects the top k of token t: k rounds of a wave-wide maximum over
+// the candidate keys (lane l holds experts l, l + 64, ...), each round clearing
+// the winner's key.  Lane i % 64 keeps the i-th selected key for the softmax
+// and the coalesced stores at the end.  sidx: NULL, or LDS that also receives
+// the indices.
+template <int PER>  // keys per lane: E <= 64 * PER
 __device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int lane, int* sidx) {
   const int E = a.E, k = a.k;
-  float v[PER];
-  uint32_t avail = 0;
+  float lv[PER];  // every load unconditional (clamped index) so all are in flight together
+  if (a.lpart) {
+    // the logits: the x-projection partials added in slice order, SU slices' loads at a time
+    constexpr int SU = PER >= 16 ? 4 : 8;
+    const int64_t stride = a.T * (int64_t)a.lN;
+    const float* base = a.lpart + t * a.lN;
+#pragma unroll
+    for (int c = 0; c < PER; ++c) lv[c] = 0.f;
+    for (int s0 = 0; s0 < a.lsplits; s0 += SU) {
+      float pv[SU][PER];
+#pragma unroll
+      for (int j = 0; j < SU; ++j)
+#pragma unroll
+        for (int c = 0; c < PER; ++c)
+          pv[j][c] = base[min(s0 + j, a.lsplits - 1) * stride + min(lane + 64 * c, E - 1)];
+#pragma unroll
+      for (int j = 0; j < SU; ++j)
+#pragma unroll
+        for (int c = 0; c < PER; ++c)
+          if (s0 + j < a.lsplits) lv[c] += pv[j][c];
+    }
+#pragma unroll
+    for (int c = 0; c < PER; ++c)
+      if (lane + 64 * c < E) a.logits[t * E + lane + 64 * c] = lv[c];
+  } else {
+#pragma unroll
+    for (int c = 0; c < PER; ++c) lv[c] = a.logits[t * E + min(lane + 64 * c, E - 1)];
+  }
+  uint64_t key[PER], sel[PER];  // sel[c] in lane l: the (64 c + l)-th selected key (k <= E)
 #pragma unroll
   for (int c = 0; c < PER; ++c) {
     const int e = lane + 64 * c;
-    v[c] = 0.f;
-    if (e < E) {
-      v[c] = a.logits[t * E + e];
-      avail |= 1u << c;
-    }
+    key[c] = e < E ? route_key(lv[c], e) : 0ull;
+    sel[c] = 0ull;
   }
-  constexpr int MV = PER;  // k <= E <= 64 PER
-  float mv[MV];  // mv[c]: the (64 c + lane)-th selected logit
-#pragma unroll
-  for (int c = 0; c < MV; ++c) mv[c] = 0.f;
   float m = 0.f;
   for (int i = 0; i < k; ++i) {
-    float bv = 0.f;
-    int be = kNoExpert;
+    uint64_t best = key[0];
+#pragma unroll
+    for (int c = 1; c < PER; ++c) best = umax64(best, key[c]);
+    const uint64_t w = wave_max_key(best);
+    const int we = key_expert(w);
+    if (i == 0) m = key_value(w);
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
-      if (!((avail >> c) & 1u)) continue;
-      if (be == kNoExpert || v[c] > bv) {  // e grows with c, so ties keep the lower e
-        bv = v[c];
-        be = lane + 64 * c;
-      }
-    }
-    wave_argmax(bv, be);
-    if ((be & 63) == lane) avail &= ~(1u << (be >> 6));
-    if (i == 0) m = bv;
-#pragma unroll
-    for (int c = 0; c < MV; ++c)
-      if (c == (i >> 6) && lane == (i & 63)) mv[c] = bv;
-    if (lane == 0) {
-      a.idx[t * k + i] = be;
-      if (sidx) sidx[t * k + i] = be;
+      key[c] = we == lane + 64 * c ? 0ull : key[c];
+      sel[c] = i == lane + 64 * c ? w : sel[c];
     }
   }
   // softmax over the selected logits
-  float part = 0.f;
+  float ev[PER], part = 0.f;
 #pragma unroll
-  for (int c = 0; c < MV; ++c)
-    if (64 * c + lane < k) part += __expf(mv[c] - m);
+  for (int c = 0; c < PER; ++c) {
+    ev[c] = 64 * c + lane < k ? __expf(key_value(sel[c]) - m) : 0.f;
+    part += ev[c];
+  }
   const float inv = 1.f / wave_sum(part);
 #pragma unroll
-  for (int c = 0; c < MV; ++c)
-    if (64 * c + lane < k) a.w[t * k + 64 * c + lane] = __expf(mv[c] - m) * inv;
+  for (int c = 0; c < PER; ++c) {
+    const int i = 64 * c + lane;
+    if (i < k) {
+      const int e = key_expert(sel[c]);
+      a.idx[t * k + i] = e;
+      if (sidx) sidx[t * k + i] = e;
+      a.w[t * k + i] = ev[c] * inv;
+    }
+  }
+}
+
+// z = bf16 of the x-projection partials' columns E .. E + zr - 1, added in
+// slice order.  Fold block b of nb takes elements b * blockDim + thread, then
+// every nb * blockDim-th.
+__device__ __forceinline__ void fold_z(const RouteArgs& a, int b, int nb) {
+  const int n = (int)a.T * a.zr;
+  const int64_t stride = a.T * (int64_t)a.lN;
+  for (int i = b * (int)blockDim.x + (int)threadIdx.x; i < n; i += nb * (int)blockDim.x) {
+    const int t = i / a.zr, c = i - t * a.zr;
+    const float* p = a.lpart + (int64_t)t * a.lN + a.E + c;
+    float v = 0.f;
+    for (int s0 = 0; s0 < a.lsplits; s0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = p[min(s0 + j, a.lsplits - 1) * stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < a.lsplits) v += pv[j];
+    }
+    a.z[i] = (uint16_t)f32_to_bf16(v);
+  }
+}
+
+// Blocks of the first routing launch beyond its routing blocks: fold z.
+inline int fold_blocks(const RouteArgs& a, int threads) {
+  if (!a.z || !a.lpart || a.zr <= 0) return 0;
+  return (int)std::min<int64_t>(256, (a.T * a.zr + threads - 1) / threads);
 }
 
 // One wave per token: k rounds of a wave-wide argmax over the E logits (larger
@@ -470,6 +633,11 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int la
 template <int PER>
 __global__ __launch_bounds__(256) void topk_kernel(RouteArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntk = (int)((a.T + 3) / 4);
+  if ((int)blockIdx.x >= ntk) {
+    fold_z(a, (int)blockIdx.x - ntk, (int)gridDim.x - ntk);
+    return;
+  }
   const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t < a.T) topk_token<PER>(a, t, lane, nullptr);
 }
@@ -591,6 +759,10 @@ __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
   __shared__ int scan_buf[1024];
   __shared__ int wsum[16];
   __shared__ int sidx[PER > 0 ? kFusedMaxSlots : 1];
+  if (blockIdx.x > 0) {  // fused launch: fold blocks
+    fold_z(a, (int)blockIdx.x - 1, (int)gridDim.x - 1);
+    return;
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int E = a.E, k = a.k;
   const int T = (int)a.T;
@@ -659,13 +831,14 @@ hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t strea
   const int nb = (int)((a.T + kRouteBlock - 1) / kRouteBlock);
   // (E > 512 would need more registers than a 1024-thread block's waves have)
   if (a.T <= kFusedMaxT && a.T * a.k <= kFusedMaxSlots && a.E <= 512) {
-    if (a.E <= 64) group_small_kernel<1><<<1, 1024, 0, stream>>>(a);
-    else if (a.E <= 128) group_small_kernel<2><<<1, 1024, 0, stream>>>(a);
-    else if (a.E <= 256) group_small_kernel<4><<<1, 1024, 0, stream>>>(a);
-    else group_small_kernel<8><<<1, 1024, 0, stream>>>(a);
+    const unsigned g = 1u + (unsigned)fold_blocks(a, 1024);
+    if (a.E <= 64) group_small_kernel<1><<<g, 1024, 0, stream>>>(a);
+    else if (a.E <= 128) group_small_kernel<2><<<g, 1024, 0, stream>>>(a);
+    else if (a.E <= 256) group_small_kernel<4><<<g, 1024, 0, stream>>>(a);
+    else group_small_kernel<8><<<g, 1024, 0, stream>>>(a);
     return hipGetLastError();
   }
-  const dim3 tg((unsigned)((a.T + 3) / 4));
+  const dim3 tg((unsigned)((a.T + 3) / 4 + fold_blocks(a, 256)));
   if (a.E <= 64) topk_kernel<1><<<tg, 256, 0, stream>>>(a);
   else if (a.E <= 128) topk_kernel<2><<<tg, 256, 0, stream>>>(a);
   else if (a.E <= 256) topk_kernel<4><<<tg, 256, 0, stream>>>(a);
