@@ -323,7 +323,7 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           u32x4 W[4];
-          const u32x3 v = CH ? chunk_window<FMT>(ring[j][r], scratch + r * kChunkScratch, lane)
+          const u32x3 v = CH ? chunk_window<FMT>(ring[j][r], scratch, lane)
                              : u32x3{ring[j][r].x, ring[j][r].y, ring[j][r].z};
           ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
           const float s = decode_block_x3<FMT>(v, lut, lane, W);
@@ -353,7 +353,9 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
   u32x2* lut = (u32x2*)smem;
   char* xs = smem + lut_bytes;
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
-  char* scratch = xs + a.nmax * stage_stride(G * kGroup) + (threadIdx.x >> 6) * RT * kChunkScratch;
+  // one chunk scratch per wave: its LDS operations complete in order, so row tile
+  // r + 1 writes only after tile r's window has been read
+  char* scratch = xs + a.nmax * stage_stride(G * kGroup) + (threadIdx.x >> 6) * kChunkScratch;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const int64_t units = (int64_t)(*a.n_items) * units_per_item;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
@@ -886,6 +888,8 @@ static hipError_t launch_dec(const ExpertArgs& a, int64_t max_items, hipStream_t
 // Expected number of work items (the exact count is only known on the device):
 // touched routed experts plus extra 16-token chunks, plus the shared experts.
 // (A low estimate: splitting work too finely costs less than idle blocks.)
+constexpr double kCoResidentGain = 1.4;  // streaming blocks sharing a CU, measured
+
 static double expected_items(const ExpertArgs& a) {
   const double slots = (double)a.T * a.k;
   const double touched = a.E * (1.0 - std::exp(-slots / a.E));
@@ -897,15 +901,18 @@ static hipError_t launch_stream_fs(const ExpertArgs& a, int64_t max_items, hipSt
   constexpr int K = G * kGroup;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
-                     (size_t)WPB * RT * kChunkScratch;
+                     (size_t)WPB * kChunkScratch;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = expert_stream_kernel<MODE, WPB, RT, D, G, FS, WPE>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WPB, lds);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
-  const int64_t blocks = (int64_t)cu_count() * per_cu;
-  // tiles per wave per unit: balance ceil(units / blocks) rounds of (tpw + 1)
-  // tile-times (one tile-time for the unit's staging bubble)
+  const int cus = cu_count();
+  const int64_t blocks = (int64_t)cus * per_cu;
+  // tiles per wave per unit: the busiest CU takes ceil(units / CUs) units of
+  // (tpw + 1) tile-times each (one for the unit's staging bubble); units that
+  // share a CU overlap each other's bubbles and load waits, measured as 1.4x
+  // the throughput of one block alone
   const double items = std::min<double>((double)max_items, expected_items(a));
   const int max_tpw = (n_tiles + WPB - 1) / WPB;
   int best_tpw = 1;
@@ -913,7 +920,8 @@ static hipError_t launch_stream_fs(const ExpertArgs& a, int64_t max_items, hipSt
   for (int tpw = 1; tpw <= max_tpw; ++tpw) {
     const int tpu = tpw * WPB;
     const double units = items * ((n_tiles + tpu - 1) / tpu);
-    const double cost = std::ceil(units / blocks) * (tpw + 1);
+    const double on_cu = std::ceil(units / cus);
+    const double cost = on_cu * (tpw + 1) / (per_cu >= 2 && on_cu >= 2 ? kCoResidentGain : 1.0);
     if (cost < best) {
       best = cost;
       best_tpw = tpw;
@@ -1005,7 +1013,9 @@ static hipError_t launch_gateup(const ExpertArgs& a, int64_t mi, bool small, hip
   }
   switch (G) {
     case 24: return launch_stream<MODE_GATEUP, 8, 2, 8, 24>(a, mi, s);
-    case 16: return launch_stream<MODE_GATEUP, 8, 2, 8, 16>(a, mi, s);
+    case 16:  // PQ2_0-only layers: two blocks per CU at 128 registers (no byte table)
+      if (a.fmt_mask == 1) return launch_stream_fs<MODE_GATEUP, 8, 2, 4, 16, 1, 4>(a, mi, s);
+      return launch_stream<MODE_GATEUP, 8, 2, 8, 16>(a, mi, s);
     case 2: return launch_stream<MODE_GATEUP, 8, 2, 2, 2>(a, mi, s);
     default: return launch_dec<MODE_GATEUP, 8, 1, 2, 8, 0>(a, mi, s);
   }
@@ -1023,8 +1033,12 @@ static hipError_t launch_down(const ExpertArgs& a, int64_t mi, bool small, hipSt
     }
   }
   switch (G) {
-    case 8: return launch_stream<MODE_DOWN, 8, 4, 4, 8>(a, mi, s);
-    case 6: return launch_stream<MODE_DOWN, 8, 4, 3, 6>(a, mi, s);
+    case 8:  // PQ2_0-only layers: two row tiles per wave, two blocks per CU
+      if (a.fmt_mask == 1) return launch_stream_fs<MODE_DOWN, 8, 2, 4, 8, 1, 4>(a, mi, s);
+      return launch_stream<MODE_DOWN, 8, 4, 4, 8>(a, mi, s);
+    case 6:
+      if (a.fmt_mask == 1) return launch_stream_fs<MODE_DOWN, 8, 2, 3, 6, 1, 4>(a, mi, s);
+      return launch_stream<MODE_DOWN, 8, 4, 3, 6>(a, mi, s);
     case 4: return launch_stream<MODE_DOWN, 8, 4, 4, 4>(a, mi, s);
     case 1: return launch_stream<MODE_DOWN, 8, 4, 1, 1>(a, mi, s);
     default: return launch_dec<MODE_DOWN, 8, 1, 4, 4, 0>(a, mi, s);
