@@ -168,6 +168,22 @@ __device__ __forceinline__ u32x3 load_block_x3(const uint8_t* blk, int q) {
   return *(const u32x3_a2*)(blk + (FMT == kPQ2 ? 8 : 6) * q);
 }
 
+// The same window from one 12-byte load at 4-byte alignment (windows start
+// 2-byte aligned): when the window starts at 2 mod 4 the load begins 2 bytes
+// early and the window's last 2 bytes, which no decoder uses, are dropped.
+// Such loads stream about 1.4x faster than the 2-byte-aligned ones; the small-
+// batch PQ2_0 reads take them (elsewhere the per-load address arithmetic cost
+// more than it saved).
+typedef u32x3 __attribute__((aligned(4))) u32x3_a4;
+template <int FMT>
+__device__ __forceinline__ u32x3 load_block_x3_a4(const uint8_t* blk, int q) {
+  const uint8_t* p = blk + (FMT == kPQ2 ? 8 : 6) * q;
+  const int mis = (int)((uintptr_t)p & 2);  // pointer arithmetic keeps the global address space
+  const u32x3 v = *(const u32x3_a4*)(p - mis);
+  const uint32_t sh = (uint32_t)mis * 8;
+  return u32x3{__builtin_amdgcn_alignbit(v.y, v.x, sh), __builtin_amdgcn_alignbit(v.z, v.y, sh), v.z >> sh};
+}
+
 // Decode one lane's quarter of a block fetched with load_block_x3 into the
 // B operands; returns the group scale.  The operands encode 2t, so results
 // carry a factor 2 that the caller removes once.

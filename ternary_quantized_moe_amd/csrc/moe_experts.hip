@@ -98,6 +98,9 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
     rows[r] = bank + off + i16 * BB + (int64_t)gb * 16 * BB;
   }
 
+  auto fetch = [&](const uint8_t* blk) -> u32x3 {
+    return FMT == kPQ2 ? load_block_x3_a4<FMT>(blk, q) : load_block_x3<FMT>(blk, q);
+  };
   // weight prefetch starts before the activations are staged
   u32x3 ring[D][RT];
   if (active) {
@@ -105,7 +108,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
     for (int j = 0; j < D; ++j)
       if (GW > 0 ? j < GW : gb + j < ge)
 #pragma unroll
-        for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + j * 16 * BB, q);
+        for (int r = 0; r < RT; ++r) ring[j][r] = fetch(rows[r] + j * 16 * BB);
   }
 
   __syncthreads();  // the previous unit is done with the staging buffer
@@ -143,7 +146,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
         for (int r = 0; r < RT; ++r) cur[r] = ring[i % D][r];
         if (i + D < GW)
 #pragma unroll
-          for (int r = 0; r < RT; ++r) ring[i % D][r] = load_block_x3<FMT>(rows[r] + (i + D) * 16 * BB, q);
+          for (int r = 0; r < RT; ++r) ring[i % D][r] = fetch(rows[r] + (i + D) * 16 * BB);
         step(i, cur);
       }
     } else {
@@ -158,7 +161,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
           for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
           if (i + D < n)
 #pragma unroll
-            for (int r = 0; r < RT; ++r) ring[j][r] = load_block_x3<FMT>(rows[r] + (int64_t)(i + D) * 16 * BB, q);
+            for (int r = 0; r < RT; ++r) ring[j][r] = fetch(rows[r] + (int64_t)(i + D) * 16 * BB);
           step(i, cur);
         }
       }
@@ -798,8 +801,12 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     }
     // lane holds positions it.pos + 16 tt + 4q + j, column i16 of each row tile
     const int row0 = (wave + t * kDownWaves) * 64;
-    const volatile int* vslot = slot_of;
-    const volatile float* vwgt = wgt_of;
+    // (LDS-qualified: through generic pointers these reads become flat loads,
+    // whose waits also wait for every weight load in flight)
+    typedef const volatile int __attribute__((address_space(3))) lds_int;
+    typedef const volatile float __attribute__((address_space(3))) lds_float;
+    lds_int* vslot = (lds_int*)slot_of;
+    lds_float* vwgt = (lds_float*)wgt_of;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
