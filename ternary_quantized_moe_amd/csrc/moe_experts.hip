@@ -41,6 +41,23 @@ constexpr int MODE_DOWN = 1;
 // LDS banks.
 __host__ __device__ constexpr int stage_stride(int K) { return 2 * K + 16; }
 
+// Per-item table of the down projection, after the staged rows: each token
+// row's slot and half its gate weight (the operands encode 2t).  It is filled
+// with the staging, so a tile epilogue reads shared memory instead of making
+// two dependent global loads (position -> slot -> gate weight) per tile.
+__host__ __device__ constexpr int slot_table_bytes(int nmax) { return (8 * nmax + 15) / 16 * 16; }
+
+__device__ __forceinline__ void stage_slots(const ExpertArgs& a, const Item& it, int* slot_of, float* wgt_of) {
+  const int i = threadIdx.x;
+  if (i < it.n) {
+    const int64_t p = it.pos + i;
+    const bool routed = p < a.Tk;
+    const int slot = routed ? a.perm[p] : (int)p;
+    slot_of[i] = slot;
+    wgt_of[i] = 0.5f * (routed ? a.topk_w[slot] : 1.f);
+  }
+}
+
 template <int FMT, int MODE>
 __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Item& it, char* xs, int K) {
   const int G = K / kGroup;
@@ -68,7 +85,7 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Item& it, 
 // ring, the load offsets and the LDS offsets are static.  GW = 0: any K.
 template <int FMT, int MODE, int WPB, int KS, int RT, int D, int GW>
 __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it, int tblock, const u32x2* lut,
-                                            char* xs, f32x4* red) {
+                                            char* xs, f32x4* red, int* slot_of, float* wgt_of) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int K = MODE == MODE_GATEUP ? a.d : a.f;
@@ -113,6 +130,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
 
   __syncthreads();  // the previous unit is done with the staging buffer
   stage_rows<FMT, MODE>(a, it, xs, K);
+  if (MODE == MODE_DOWN) stage_slots(a, it, slot_of, wgt_of);
   __syncthreads();
 
   f32x4 acc[RT];
@@ -198,16 +216,8 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
       const float hv = g / (1.f + __expf(-g)) * u;
       a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
     } else {
-      int64_t slot;
-      float wgt;
-      if (p < a.Tk) {
-        slot = a.perm[p];
-        wgt = a.topk_w[slot];
-      } else {
-        slot = p;
-        wgt = 1.f;
-      }
-      wgt *= 0.5f;
+      const int64_t slot = slot_of[ti];
+      const float wgt = wgt_of[ti];
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
@@ -221,7 +231,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
 // each of the RT row tiles; the operands encode 2t, hence the 0.5.
 template <int MODE, int RT>
 __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& it, int tile, int lane,
-                                              const f32x4 (&acc)[RT]) {
+                                              const f32x4 (&acc)[RT], const int* slot_of, const float* wgt_of) {
   const int i16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -233,16 +243,8 @@ __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& i
       const float hv = g / (1.f + __expf(-g)) * u;
       a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
     } else {
-      int64_t slot;
-      float wgt;
-      if (p < a.Tk) {
-        slot = a.perm[p];
-        wgt = a.topk_w[slot];
-      } else {
-        slot = p;
-        wgt = 1.f;
-      }
-      wgt *= 0.5f;
+      const int64_t slot = slot_of[ti];
+      const float wgt = wgt_of[ti];
 #pragma unroll
       for (int r = 0; r < RT; ++r) {
         const int64_t row = ((int64_t)tile * RT + r) * 16 + i16;
@@ -258,7 +260,8 @@ __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& i
 // loads for the next tile are in flight while the current one finishes.
 template <int FMT, int MODE, int WPB, int RT, int D, int G>
 __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const Item& it, int tile0, int tile_end,
-                                                   const u32x2* lut, char* xs, char* scratch) {
+                                                   const u32x2* lut, char* xs, char* scratch, int* slot_of,
+                                                   float* wgt_of) {
   static_assert(G % D == 0 && D <= G, "the ring depth must divide the group count");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
@@ -302,6 +305,7 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
 
   __syncthreads();  // the previous unit is done with the staging buffer
   stage_rows<FMT, MODE>(a, it, xs, K);
+  if (MODE == MODE_DOWN) stage_slots(a, it, slot_of, wgt_of);
   __syncthreads();
 
   const char* arow = xs + min(i16, it.n - 1) * stage_stride(K) + q * 16;
@@ -340,7 +344,7 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    tile_epilogue<MODE, RT>(a, it, first + WPB * t, lane, acc);
+    tile_epilogue<MODE, RT>(a, it, first + WPB * t, lane, acc, slot_of, wgt_of);
 #pragma unroll
     for (int r = 0; r < RT; ++r) rows[r] += tile_stride;
   }
@@ -358,7 +362,9 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
   // one chunk scratch per wave: its LDS operations complete in order, so row tile
   // r + 1 writes only after tile r's window has been read
-  char* scratch = xs + a.nmax * stage_stride(G * kGroup) + (threadIdx.x >> 6) * kChunkScratch;
+  int* slot_of = (int*)(xs + a.nmax * stage_stride(G * kGroup));
+  float* wgt_of = (float*)(slot_of + a.nmax);
+  char* scratch = xs + a.nmax * stage_stride(G * kGroup) + slot_table_bytes(a.nmax) + (threadIdx.x >> 6) * kChunkScratch;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const int64_t units = (int64_t)(*a.n_items) * units_per_item;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
@@ -366,14 +372,14 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
     const int tile0 = (int)(u % units_per_item) * tiles_per_unit;
     const int tile_end = min(n_tiles, tile0 + tiles_per_unit);
     if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
-      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch);
+      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
     else
-      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch);
+      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
   }
 }
 
 // Persistent blocks over units (item, tile block).
-// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][staged rows][KS reduction]
+// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][staged rows][slot table][KS reduction]
 template <int MODE, int WPB, int KS, int RT, int D, int GW>
 __global__ __launch_bounds__(64 * WPB) void expert_dec_kernel(ExpertArgs a, int tblocks_per_item) {
   extern __shared__ __align__(16) char smem[];
@@ -381,16 +387,18 @@ __global__ __launch_bounds__(64 * WPB) void expert_dec_kernel(ExpertArgs a, int 
   const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
   u32x2* lut = (u32x2*)smem;
   char* xs = smem + lut_bytes;
-  f32x4* red = (f32x4*)(xs + a.nmax * stage_stride(K));
+  int* slot_of = (int*)(xs + a.nmax * stage_stride(K));
+  float* wgt_of = (float*)(slot_of + a.nmax);
+  f32x4* red = (f32x4*)(xs + a.nmax * stage_stride(K) + slot_table_bytes(a.nmax));
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
   const int64_t units = (int64_t)(*a.n_items) * tblocks_per_item;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const Item it = a.items[u / tblocks_per_item];
     const int tb = (int)(u % tblocks_per_item);
     if (a.formats[it.bank] == kPTQ1)
-      expert_unit<kPTQ1, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red);
+      expert_unit<kPTQ1, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red, slot_of, wgt_of);
     else
-      expert_unit<kPQ2, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red);
+      expert_unit<kPQ2, MODE, WPB, KS, RT, D, GW>(a, it, tb, lut, xs, red, slot_of, wgt_of);
   }
 }
 
@@ -881,7 +889,7 @@ static hipError_t launch_dec(const ExpertArgs& a, int64_t max_items, hipStream_t
   constexpr int TPB = WPB / KS;
   const int tbpi = (n_tiles + TPB - 1) / TPB;
   const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
-                     (KS > 1 ? (size_t)TPB * (KS - 1) * RT * 64 * 16 : 0);
+                     slot_table_bytes(a.nmax) + (KS > 1 ? (size_t)TPB * (KS - 1) * RT * 64 * 16 : 0);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = expert_dec_kernel<MODE, WPB, KS, RT, D, GW>;
   int per_cu = 0;
@@ -908,7 +916,7 @@ static hipError_t launch_stream_fs(const ExpertArgs& a, int64_t max_items, hipSt
   constexpr int K = G * kGroup;
   const int n_tiles = MODE == MODE_GATEUP ? a.f / 16 : a.d / (16 * RT);
   const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
-                     (size_t)WPB * kChunkScratch;
+                     slot_table_bytes(a.nmax) + (size_t)WPB * kChunkScratch;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = expert_stream_kernel<MODE, WPB, RT, D, G, FS, WPE>;
   int per_cu = 0;
