@@ -286,18 +286,20 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
   }
 }
 
-// Combine of a small batch: a block covers 64 model rows (4 row tiles) x 16
-// tokens with 16 waves = 4 row tiles x 4 slices of K.  The slices' partial
-// sums meet in shared memory and are added in slice order; then each of 128
-// threads adds one token's slots to 8 consecutive rows with 16-byte reads, so
-// a slot row is read in 128-byte pieces.
-__global__ __launch_bounds__(1024) void combine_small_kernel(DenseArgs a) {
-  __shared__ float part[4][16][64 + 4];
+// Combine of a small batch: a block covers RTB 16-row tiles of the model rows
+// x 16 tokens with 4 RTB waves = RTB row tiles x 4 slices of K.  The slices'
+// partial sums meet in shared memory and are added in slice order; then each
+// of 32 RTB threads adds one token's slots to 8 consecutive rows with 16-byte
+// reads, in slot order.
+template <int RTB>
+__global__ __launch_bounds__(256 * RTB) void combine_small_kernel(DenseArgs a) {
+  constexpr int R = 16 * RTB;  // model rows per block
+  __shared__ float part[4][16][R + 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
-  const int rt = wave & 3, ks = wave >> 2;
+  const int rt = wave % RTB, ks = wave / RTB;
   const int d = a.N0, K = a.K;
-  const int n = blockIdx.x * 64 + rt * 16 + i16;  // d is a multiple of 64
+  const int n = blockIdx.x * R + rt * 16 + i16;  // d is a multiple of 128
   const int64_t t0 = (int64_t)blockIdx.y * 16;
   const uint16_t* zrow = a.act + std::min<int64_t>(t0 + i16, a.T - 1) * a.lda;
   const uint16_t* wrow = a.w0 ? a.w0 + (int64_t)n * K : nullptr;
@@ -326,11 +328,12 @@ __global__ __launch_bounds__(1024) void combine_small_kernel(DenseArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) part[ks][4 * q + j][rt * 16 + i16] = acc[j];
   __syncthreads();
-  if (threadIdx.x >= 128) return;
-  const int tl = threadIdx.x >> 3, c = threadIdx.x & 7;
+  constexpr int CPT = R / 8;  // 8-row groups per token
+  if (threadIdx.x >= 16 * CPT) return;
+  const int tl = threadIdx.x / CPT, c = threadIdx.x % CPT;
   const int64_t t = t0 + tl;
   if (t >= a.T) return;
-  const int n0 = blockIdx.x * 64 + 8 * c;
+  const int n0 = blockIdx.x * R + 8 * c;
   float v[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -405,8 +408,13 @@ hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
 
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
   if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_COMBINE>(a, a.N0, stream);
-  const dim3 grid((unsigned)(a.N0 / 64), (unsigned)((a.T + 15) / 16));
-  combine_small_kernel<<<grid, 1024, 0, stream>>>(a);
+  // blocks of 16 rows up to 32 tokens, of 32 rows beyond (measured: fewer
+  // weight bytes per CU win until the token tiles multiply the blocks)
+  const unsigned tt = (unsigned)((a.T + 15) / 16);
+  if (a.T <= 32)
+    combine_small_kernel<1><<<dim3((unsigned)(a.N0 / 16), tt), 256, 0, stream>>>(a);
+  else
+    combine_small_kernel<2><<<dim3((unsigned)(a.N0 / 32), tt), 512, 0, stream>>>(a);
   return hipGetLastError();
 }
 
