@@ -258,7 +258,10 @@ __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& i
 // tile0 + w, tile0 + w + WPB, ...  and streams them back to back through one
 // prefetch ring of D groups (D divides the compile-time group count G), so the
 // loads for the next tile are in flight while the current one finishes.
-template <int FMT, int MODE, int WPB, int RT, int D, int G>
+// PIPE: each step adds the previous step's product to the accumulators, so
+// the add does not wait for the MFMAs just issued (5 more registers per row
+// tile: the kernels built for two waves per SIMD have them, the others not).
+template <int FMT, int MODE, int WPB, int RT, int D, int G, bool PIPE>
 __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const Item& it, int tile0, int tile_end,
                                                    const u32x2* lut, char* xs, char* scratch, int* slot_of,
                                                    float* wgt_of) {
@@ -311,9 +314,14 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
   const char* arow = xs + min(i16, it.n - 1) * stage_stride(K) + q * 16;
   for (int t = 0; t < ntw; ++t) {
     const bool more = t + 1 < ntw;
-    f32x4 acc[RT];
+    f32x4 acc[RT], ptmp[RT];
+    float ps[RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < RT; ++r) {
+      acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ptmp[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ps[r] = 0.f;
+    }
 #pragma unroll 1
     for (int g0 = 0; g0 < G; g0 += D) {
       // the next D groups: the rest of this tile, else the start of the next
@@ -337,13 +345,22 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
-          acc[r] += s * tmp;
+          if (PIPE) {
+            acc[r] += ps[r] * ptmp[r];
+            ptmp[r] = tmp;
+            ps[r] = s;
+          } else {
+            acc[r] += s * tmp;
+          }
         }
         // keep each step's loads and decode in place: hoisting the ring's
         // refills would double the registers the ring needs
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if (PIPE)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) acc[r] += ps[r] * ptmp[r];
     tile_epilogue<MODE, RT>(a, it, first + WPB * t, lane, acc, slot_of, wgt_of);
 #pragma unroll
     for (int r = 0; r < RT; ++r) rows[r] += tile_stride;
@@ -372,9 +389,9 @@ void expert_stream_kernel(ExpertArgs a, int tiles_per_unit, int units_per_item) 
     const int tile0 = (int)(u % units_per_item) * tiles_per_unit;
     const int tile_end = min(n_tiles, tile0 + tiles_per_unit);
     if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
-      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
+      expert_stream_unit<kPTQ1, MODE, WPB, RT, D, G, (WPE <= 2)>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
     else
-      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
+      expert_stream_unit<kPQ2, MODE, WPB, RT, D, G, (WPE <= 2)>(a, it, tile0, tile_end, lut, xs, scratch, slot_of, wgt_of);
   }
 }
 
