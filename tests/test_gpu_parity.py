@@ -199,6 +199,33 @@ def test_mixed_formats_with_shared_expert():
         assert row_metric(y.cpu().numpy().view(np.uint16), ref.y).max() <= TOL
 
 
+# Ragged shapes: d = 1152 (9 groups; the small-batch x-projection's last K slice
+# is partial), E + r = 68 (a ragged last row tile), f = 384 (3 down groups),
+# mixed formats with a shared expert; T = 37 and 64 take the 32-row combine
+# blocks, the separate top-k launch and its z-fold blocks; T = 300 the prefill
+# kernels, including the mixed-format down GEMM.
+RAGGED = LayerConfig("ragged", 23, 1152, 44, 384, 3, 1, 24, "mixed")
+
+
+@pytest.mark.parametrize("T", [1, 13, 37, 64, 300])
+def test_ragged_shapes(T):
+    tq = tq_mod()
+    L = Layer(RAGGED)
+    c = L.cfg
+    x_bits = L.gen.tokens(T, 3)
+    d = L.tensors(x_bits)
+    say(f"ragged T={T}")
+    r = tq.route(d["x"], d["router"], d["delta"], c.n_experts, c.top_k)
+    y = tq.forward(d["x"], d["router"], d["delta"], L.device(), d["a"], d["b"], c.top_k)
+    torch.cuda.synchronize()
+    idx, _ = check_routing(L, x_bits, r, np.arange(T))
+    ref = omoe.forward(x_bits, L.router, L.delta, L.oracle_banks, L.corr_a, L.corr_b, c.top_k,
+                       forced_idx=idx)
+    m = row_metric(y.cpu().numpy().view(np.uint16), ref.y)
+    say(f"  max row metric {m.max():.3e}")
+    assert m.max() <= TOL
+
+
 MANY_EXPERTS = LayerConfig("many", 22, 256, 1000, 128, 9, 0, 16, "pq2_0")
 
 
