@@ -119,19 +119,22 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
         B[rt][m][1] = wp[rt][(m * 2 + 1) * 64];
       }
   }
-  u32x4 sraw[kDenseP];
+  u32x4 s0[kDenseP], s1[kDenseP];  // staged loads of the next two groups
   __syncthreads();  // the previous unit is done with the shared memory
-  stage_load(0, sraw);
-  stage_store(sraw, smem);
+  stage_load(0, s0);
+  stage_store(s0, smem);
+  stage_load(min(1, G - 1), s1);
   __syncthreads();
 
   f32x4 acc[NTT][2];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int g = 0; g < G; ++g) {
-    const int gn = min(g + 1, G - 1);  // the last step refetches its own group (unused)
-    stage_load(gn, sraw);
+  // step g: issue the loads of group g + 2, multiply group g, store group g + 1
+  // (loaded one step earlier); the last steps refetch the last group (unused)
+  auto step = [&](int g, u32x4 (&issue)[kDenseP], const u32x4 (&ready)[kDenseP]) {
+    const int gn = min(g + 1, G - 1);
+    stage_load(min(g + 2, G - 1), issue);
     if (active) {
       const char* ab = smem + (g & 1) * kDenseBuf + i16 * kDenseRow + q * 16;
       u32x4 A[NTT][4];
@@ -154,8 +157,12 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
         }
       }
     }
-    stage_store(sraw, smem + ((g + 1) & 1) * kDenseBuf);
+    stage_store(ready, smem + ((g + 1) & 1) * kDenseBuf);
     __syncthreads();
+  };
+  for (int g = 0; g < G; g += 2) {
+    step(g, s0, s1);
+    if (g + 1 < G) step(g + 1, s1, s0);
   }
 
   if (EPI == EPI_XPROJ) {

@@ -479,7 +479,10 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 
 // NTT: token tiles of the item (a compile-time count keeps the multiply free of
 // branches, so the independent MFMA chains of the token tiles interleave).
-template <int FMT, int MODE, int NTT, int WAVES>
+// SD: groups of activations in flight (1: loaded in the step before they are
+// staged; 2: two steps before, so a load has two group steps to land, which
+// only the PQ2_0-only gate/up kernel has the registers for).
+template <int FMT, int MODE, int NTT, int WAVES, int SD>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                           char* bufs, char* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -543,13 +546,14 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt]);
   }
-  u32x4 sraw[P][2];
+  u32x4 s0[P][2], s1[P][SD == 2 ? 2 : 1];  // staged loads in flight (SD = 1: s0 only)
   __syncthreads();  // the previous unit is done with the staging buffers
 #pragma unroll
   for (int pp = 0; pp < P; ++pp)
     if (stage_on[pp]) {
-      act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], sraw[pp]);
-      act_half_store<FMT>(sraw[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
+      act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], s0[pp]);
+      act_half_store<FMT>(s0[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
+      if constexpr (SD == 2) act_half_load<FMT>(srow[pp], min(1, G - 1), sq[pp], sh[pp], s1[pp]);
     }
   __syncthreads();
 
@@ -559,43 +563,93 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The last step fetches its own group again (in bounds, unused) and restages
-  // it into the idle buffer, so the loop body has no branch on g.
-  for (int g = 0; g < G; ++g) {
-    const int gn = min(g + 1, G - 1);
+  // the item's activation operands of group g, then one row tile at a time:
+  // decode it, refill its ring slot with group gn, multiply it with every token tile
+  auto multiply = [&](int g, int gn) {
+    if (!active) return;
+    const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
+    u32x4 A[NTT][4];
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      u32x4 W[4];
+      const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+      ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
+      f32x4 tmp[NTT];
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+    }
+  };
+  auto load = [&](int g, u32x4 (&raw)[P][2]) {
 #pragma unroll
     for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], sraw[pp]);
-    if (active) {
-      // the item's activation operands of this group, then one row tile at a
-      // time: decode it, refill its ring slot, multiply it with every token tile
-      const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
-      u32x4 A[NTT][4];
+      if (stage_on[pp]) act_half_load<FMT>(srow[pp], g, sq[pp], sh[pp], raw[pp]);
+  };
+  auto store = [&](int g, const u32x4 (&raw)[P][2]) {  // into the buffer of group g
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        u32x4 W[4];
-        const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-        ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
-        f32x4 tmp[NTT];
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+    for (int pp = 0; pp < P; ++pp)
+      if (stage_on[pp]) act_half_store<FMT>(raw[pp], bufs + (g & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
+  };
+  // The last steps fetch the last group again (in bounds, unused) and restage
+  // it into the idle buffer, so the loop bodies have no branch on g.
+  if constexpr (SD == 2) {
+    // step g: issue group g + 2, multiply group g, stage group g + 1 (issued a step ago)
+    for (int g = 0; g < G; g += 2) {
+      load(min(g + 2, G - 1), s0);
+      multiply(g, min(g + 1, G - 1));
+      store(g + 1, s1);
+      __syncthreads();
+      if (g + 1 < G) {
+        load(min(g + 3, G - 1), s1);
+        multiply(g + 1, min(g + 2, G - 1));
+        store(g + 2, s0);
+        __syncthreads();
       }
     }
+  } else {
+    for (int g = 0; g < G; ++g) {
+      const int gn = min(g + 1, G - 1);
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp])
-        act_half_store<FMT>(sraw[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
-    __syncthreads();
+      for (int pp = 0; pp < P; ++pp)
+        if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
+      if (active) {  // the multiply written out (as a lambda call it spills here)
+        const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
+        u32x4 A[NTT][4];
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+          for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          u32x4 W[4];
+          const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+          ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
+          f32x4 tmp[NTT];
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
+#pragma unroll
+          for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+        }
+      }
+#pragma unroll
+      for (int pp = 0; pp < P; ++pp)
+        if (stage_on[pp])
+          act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
+      __syncthreads();
+    }
   }
   if (!active) return;
 
@@ -638,9 +692,9 @@ template <int MODE, int FS, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                               char* bufs, bool ptq1) {
   if (FS != 1 && ptq1)
-    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPTQ1, MODE, NTT, WAVES, 1>(a, it, rb, lut, bufs, nullptr);
   else if (FS != 2)
-    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPQ2, MODE, NTT, WAVES, (FS == 1 && MODE == MODE_GATEUP) ? 2 : 1>(a, it, rb, lut, bufs, nullptr);
 }
 
 // Persistent blocks over units.  Unit l = (item l / row_blocks, row block
