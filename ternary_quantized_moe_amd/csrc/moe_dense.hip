@@ -40,15 +40,16 @@ int64_t dense_split_bytes(int N, int K) { return (int64_t)(N + 15) / 16 * 16 * d
 // Split weights: 16-row tile, group g, MFMA m, hi/lo, quarter q, row i16 ->
 // 16 bytes (8 bf16 of elements g*128 + 32m + 8q .. +7 of row 16 tile + i16) at
 // ((((tile * G + g) * 4 + m) * 2 + hl) * 64 + 16 q + i16) * 16.  Elements past K
-// and rows past N are zero.
+// and rows past N are zero.  Block (tile, g) reads its 16 rows x 128 elements
+// with 256-byte row pieces and writes its 8 KB of operands as one contiguous run
+// after rearranging them in shared memory.
 __global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, u32x4* __restrict__ out) {
-  const int cpr = Kp / 8;
-  const int Np = (N + 15) / 16 * 16;
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= (int64_t)Np * cpr) return;
-  const int n = (int)(c / cpr), ck = (int)(c % cpr), k = ck * 8;
-  const int G = Kp / kGroup, g = ck / 16, m = (ck / 4) % 4, q = ck % 4;
-  const int64_t at = ((((int64_t)(n / 16) * G + g) * 4 + m) * 2) * 64 + 16 * q + (n % 16);
+  __shared__ u32x4 tile_ops[512];
+  const int G = Kp / kGroup;
+  const int tile = blockIdx.x / G, g = blockIdx.x % G;
+  const int t = threadIdx.x;
+  const int i16 = t >> 4, c = t & 15;  // row of the tile, 8-element chunk of the group
+  const int n = tile * 16 + i16, k = g * kGroup + 8 * c;
   u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
   if (k < a.K && n < N) {
     if (n < a.N0) {
@@ -61,8 +62,13 @@ __global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, 
       split_f16x8(*(const u32x4_a4*)(a.w1 + (int64_t)(n - a.N0) * a.K + k), hi, lo);
     }
   }
-  out[at] = hi;
-  out[at + 64] = lo;
+  const int m = c >> 2, q = c & 3;
+  tile_ops[(m * 2) * 64 + 16 * q + i16] = hi;
+  tile_ops[(m * 2 + 1) * 64 + 16 * q + i16] = lo;
+  __syncthreads();
+  u32x4* dst = out + (int64_t)blockIdx.x * 512;
+  dst[t] = tile_ops[t];
+  dst[t + 256] = tile_ops[t + 256];
 }
 
 // ------------------------------------------------------------------ GEMM
@@ -265,9 +271,9 @@ template <int EPI>
 hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream) {
   const int Kp = dense_kpad(a.K);
   u32x4* w2 = (u32x4*)a.wsplit;
-  const int64_t chunks = (int64_t)(N + 15) / 16 * 16 * (Kp / 8);
-  if (chunks > 0) {
-    split_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(a, N, Kp, w2);
+  const int64_t blocks = (int64_t)(N + 15) / 16 * (Kp / kGroup);  // (tile, group) pairs
+  if (blocks > 0) {
+    split_kernel<<<(unsigned)blocks, 256, 0, stream>>>(a, N, Kp, w2);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
