@@ -325,10 +325,11 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
 #pragma unroll 1
     for (int g0 = 0; g0 < G; g0 += D) {
       // the next D groups: the rest of this tile, else the start of the next
-      // one; after the wave's last tile, its own first groups again (in
-      // bounds, unused).  The refills are unconditional so the compiler can
-      // wait for each ring slot alone instead of for every load in flight.
-      const int64_t nxt = g0 + D < G ? (int64_t)(g0 + D) * 16 * BB : (more ? tile_stride : 0);
+      // one; after the wave's last tile, the groups of this step again (in
+      // bounds and unused; just read, so they come from the caches, not HBM).
+      // The refills are unconditional so the compiler can wait for each ring
+      // slot alone instead of for every load in flight.
+      const int64_t nxt = g0 + D < G ? (int64_t)(g0 + D) * 16 * BB : (more ? tile_stride : (int64_t)g0 * 16 * BB);
 #pragma unroll
       for (int j = 0; j < D; ++j) {
         u32x4 A[4];
