@@ -107,6 +107,32 @@ int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* t
 int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n_weights, int8_t* d_trits,
                           uint16_t* d_scales, void* stream);
 
+/* Quantizer rules for a group of 128 weights (project README, "What the
+ * experiments established": the ternary Lloyd quantizer over groups of 128
+ * that the released experts use beats one-shot absmean; Scion-35B-A3B
+ * discussion thread, its list of findings). */
+enum { MOE_QUANT_ABSMEAN = 0, MOE_QUANT_LLOYD = 1 };
+
+/* Device: quantize n_weights bfloat16 weights (d_w, device memory, row-major,
+ * groups of 128 along each row) into a container at d_dst (device memory,
+ * moe_packed_bytes(fmt, n_weights) bytes, groups in the order of the input).
+ *   MOE_QUANT_ABSMEAN  s = mean |w|; t = sign(w) where 2|w| > s, else 0.
+ *   MOE_QUANT_LLOYD    from the absmean codes, alternate s = mean |w| over the
+ *                      weights with t != 0 and t = sign(w) where 2|w| > s until
+ *                      the codes repeat, at most 32 rounds; s is then the mean
+ *                      |w| over the final nonzero codes (0 if there are none).
+ * Every comparison and sum is fp32, each group sum a balanced tree over adjacent
+ * pairs (weights 2m and 2m+1 first); the scale is rounded to binary16, nearest
+ * even, saturating at 65504.  Weights must be finite (otherwise the codes and
+ * scales of their groups are unspecified).  The result is a pure function of
+ * the input bits.  d_w must be 16-byte and d_dst 4-byte aligned; the buffers
+ * must not overlap.  Ordered on `stream`; nothing is allocated.
+ * Errors: MOE_E_FORMAT, MOE_E_ARG (unknown method, NULL, misaligned),
+ * MOE_E_SHAPE (n_weights negative, not a multiple of 128, or too large for one
+ * launch: above 2^31 - 1 blocks of 16 groups), MOE_E_DEVICE. */
+int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, int64_t n_weights,
+                            uint8_t* d_dst, void* stream);
+
 /* Host: reorder the blocks of a [rows x cols] container (rows % 16 == 0,
  * cols % 128 == 0) between the row-major order moe_pack writes and the
  * tile-major order the expert kernels read.  With G = cols / 128, block

@@ -25,6 +25,7 @@ _ERRORS = {
 
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
+    "moe_quantize_device",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -66,6 +67,7 @@ def lib():
             "moe_pack": (i32, [i32, vp, vp, i64, vp, i64]),
             "moe_unpack": (i32, [i32, vp, i64, vp, vp, i64]),
             "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
+            "moe_quantize_device": (i32, [i32, i32, vp, i64, vp, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -159,6 +161,26 @@ def unpack_device(fmt: int, d_src, n_weights: int, stream=None):
     _check(lib().moe_unpack_device(fmt, _dev_ptr(d_src), n_weights, _dev_ptr(trits), _dev_ptr(scales),
                                    _stream(stream)))
     return trits, scales[: n_weights // 128]
+
+
+QUANT_ABSMEAN = 0
+QUANT_LLOYD = 1
+
+
+def quantize_device(fmt: int, method: int, d_w, out=None, stream=None):
+    """bfloat16 weights (a contiguous device tensor, size a multiple of 128;
+    bf16 or int16 bit patterns) -> container bytes (uint8 device tensor)."""
+    import torch
+    n = d_w.numel()
+    nbytes = lib().moe_packed_bytes(fmt, n)
+    if nbytes < 0:
+        _check(lib().moe_quantize_device(fmt, method, None, n, None, _stream(stream)))
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=d_w.device)
+    elif out.numel() < nbytes:
+        raise MoeError(-6, f"out holds {out.numel()} bytes, {nbytes} needed")
+    _check(lib().moe_quantize_device(fmt, method, _dev_ptr(d_w), n, _dev_ptr(out), _stream(stream)))
+    return out[:nbytes]
 
 
 class ExpertBanks:

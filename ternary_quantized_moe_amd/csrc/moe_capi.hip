@@ -326,6 +326,26 @@ int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n, int8_t* 
   return ok();
 }
 
+int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, int64_t n, uint8_t* d_dst,
+                            void* stream) {
+  if (!known_fmt(fmt)) return bad_fmt(fmt);
+  if (method != MOE_QUANT_ABSMEAN && method != MOE_QUANT_LLOYD)
+    return fail(MOE_E_ARG, "unknown quantizer method %d; valid are 0 (absmean) and 1 (Lloyd)", (int)method);
+  if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
+  if (n / 128 > moe::quantize_max_groups())
+    return fail(MOE_E_SHAPE, "weight count %lld exceeds one launch", (long long)n);
+  if (n == 0) return ok();
+  if (!d_w || !d_dst) return fail(MOE_E_ARG, "NULL pointer");
+  if ((uintptr_t)d_w % 16) return fail(MOE_E_ARG, "d_w must be 16-byte aligned");
+  if ((uintptr_t)d_dst % 4) return fail(MOE_E_ARG, "d_dst must be 4-byte aligned");
+  const uintptr_t w0 = (uintptr_t)d_w, w1 = w0 + (uintptr_t)n * 2;
+  const uintptr_t d0 = (uintptr_t)d_dst, d1 = d0 + (uintptr_t)(n / 128 * (fmt == MOE_PQ2_0 ? 34 : 28));
+  if (w0 < d1 && d0 < w1) return fail(MOE_E_ARG, "d_w and d_dst overlap");
+  hipError_t e = moe::launch_quantize(fmt, method, d_w, n / 128, d_dst, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "moe_quantize_device launch");
+  return ok();
+}
+
 int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k) {
   if (n_tokens < 0 || n_experts < 1 || top_k < 1) return -1;
   return make_plan(n_tokens, d_model, n_experts, 0, 128, top_k, 0).route_end;

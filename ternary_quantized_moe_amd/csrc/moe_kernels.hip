@@ -21,6 +21,7 @@
 
 #include "device_common.h"
 #include "moe_internal.h"
+#include "wave_ops.h"
 
 namespace moe {
 
@@ -422,27 +423,6 @@ hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
 // One wave per token: k rounds of a wave-wide argmax over the E logits (larger
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
-
-// ------------------------------------------------------------ wave primitives
-// Exchanges inside rows of 16 lanes go through DPP (no LDS round trip):
-// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes 1 and 2 apart, the half-row and
-// row mirrors pair the two quads of each half and the two halves of each row.
-// After the four steps every lane of a row holds the row's reduction; the four
-// rows are then combined from one lane each with readlane.
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
-
-template <int CTRL>
-__device__ __forceinline__ int dpp_i32(int v) {
-  return __builtin_amdgcn_update_dpp(v, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
-}
-__device__ __forceinline__ float readlane_f32(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
 
 // Top-k candidates as 64-bit keys whose unsigned order is the selection
 // order.  High word: the fp32 logit mapped to an order-preserving integer

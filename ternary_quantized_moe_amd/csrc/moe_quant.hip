@@ -1,0 +1,194 @@
+// Ternary quantizer for gfx950: bfloat16 weights -> PQ2_0 or PTQ1_0 containers.
+//
+// A group of 128 weights becomes ternary codes t and one scale s (project
+// README, "What the experiments established": the deployed ternary Lloyd
+// quantizer over groups of 128 beats one-shot absmean; Scion-35B-A3B discussion
+// thread, its list of findings; container layouts from the 35B-A3B card and the
+// FlashNext card, "Weight Representation").  Two rules:
+//   absmean  s = mean |w|;  t = sign(w) where 2|w| > s, else 0
+//   Lloyd    from the absmean codes, alternate  s = mean |w| over the weights
+//            with t != 0  and  t = sign(w) where 2|w| > s, until the codes
+//            repeat (at most 32 rounds); the stored scale belongs to the final
+//            codes.
+// Every decision is taken in fp32 and every group sum is a balanced tree over
+// adjacent pairs (weights 2m and 2m+1 first), so the containers are fixed bit
+// for bit.  The scale is rounded to binary16 (nearest even), saturating at the
+// largest finite value; a group of zeros gets scale 0.
+//
+// Layout: a row of 16 lanes holds one group, lane i weights 8i..8i+7 (one
+// 16-byte load), so a wave takes four consecutive groups.  A sum takes three
+// levels inside the lane and four DPP exchanges inside the row, after which
+// every lane of the row holds it.  The Lloyd loop runs until no group of the
+// wave changes: a group that has converged is a fixed point of the iteration,
+// so the rounds it runs after that leave it as it is.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+#include "moe_ternary.h"
+#include "wave_ops.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kQuantThreads = 256;            // four waves, 16 groups per block
+constexpr int kQuantGroupsPerBlock = kQuantThreads / 16;
+constexpr int kQuantMaxRounds = 32;
+constexpr uint32_t kF16MaxFinite = 0x7BFFu;
+
+// Sum over the 16 lanes of each row, returned to every lane of the row.
+__device__ __forceinline__ float row_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+__device__ __forceinline__ int row_sum_i32(int v) {
+  v += dpp_i32<kDppXor1>(v);
+  v += dpp_i32<kDppXor2>(v);
+  v += dpp_i32<kDppHalfMirror>(v);
+  v += dpp_i32<kDppMirror>(v);
+  return v;
+}
+
+// Adjacent-pair tree over a lane's eight values.
+__device__ __forceinline__ float tree8(const float (&v)[8]) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+// Bit j set where 2 a_j > s (a nonzero code).
+__device__ __forceinline__ uint32_t nonzero_mask(const float (&a)[8], float s) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) m |= (2.0f * a[j] > s ? 1u : 0u) << j;
+  return m;
+}
+
+// fp32 mean of a over the nonzero codes of the group (0 if there are none).
+__device__ __forceinline__ float mean_of_nonzero(const float (&a)[8], uint32_t nz) {
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (nz >> j) & 1u ? a[j] : 0.0f;
+  const float total = row_sum(tree8(v));
+  const int count = row_sum_i32(__popc(nz));
+  return count > 0 ? total / (float)count : 0.0f;
+}
+
+// Eight bits -> the even bits of a 16-bit word (bit j -> bit 2j).
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+  x = (x | (x << 4)) & 0x0F0Fu;
+  x = (x | (x << 2)) & 0x3333u;
+  x = (x | (x << 1)) & 0x5555u;
+  return x;
+}
+
+// Five (or four) 2-bit base-3 digits, least significant first -> sum d_i 3^i.
+__device__ __forceinline__ uint32_t base3_byte(uint64_t digits, int n) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 4; i >= 0; --i)
+    if (i < n) v = v * 3u + (uint32_t)((digits >> (2 * i)) & 3u);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int src_lane) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
+}
+
+template <int FMT, int METHOD>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __restrict__ w, int64_t groups,
+                                                                 uint8_t* __restrict__ dst) {
+  const int lane = threadIdx.x & 63, i = lane & 15, row0 = lane & 48;
+  const int64_t g = (int64_t)blockIdx.x * kQuantGroupsPerBlock + (threadIdx.x >> 4);
+  const bool valid = g < groups;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (valid) v = w[g * 16 + i];
+
+  // |w| in fp32 and the sign bits, weight 8i + j in slot j
+  float a[8];
+  uint32_t neg = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    a[2 * k] = fabsf(__uint_as_float(v[k] << 16));
+    a[2 * k + 1] = fabsf(__uint_as_float(v[k] & 0xFFFF0000u));
+    neg |= ((v[k] >> 15) & 1u) << (2 * k);
+    neg |= (v[k] >> 31) << (2 * k + 1);
+  }
+
+  float s = row_sum(tree8(a)) / 128.0f;
+  uint32_t nz = nonzero_mask(a, s);
+  if (METHOD == MOE_QUANT_LLOYD) {
+    bool fixed = false;
+    for (int r = 0; r < kQuantMaxRounds; ++r) {
+      s = mean_of_nonzero(a, nz);
+      const uint32_t next = nonzero_mask(a, s);
+      const bool changed = __ballot(next != nz) != 0;  // wave-uniform
+      nz = next;
+      if (!changed) {
+        fixed = true;
+        break;
+      }
+    }
+    if (!fixed) s = mean_of_nonzero(a, nz);
+  }
+
+  uint32_t sbits = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
+  if (sbits == 0x7C00u) sbits = kF16MaxFinite;  // s >= 0: +Inf is the only overflow
+
+  if (FMT == kPQ2) {
+    // 2-bit codes: 01 = +1, 11 = -1; lane i writes bytes 2i and 2i+1
+    const uint32_t codes = spread8(nz) | (spread8(nz & neg) << 1);
+    if (valid) {
+      uint8_t* blk = dst + g * 34;
+      *(uint16_t*)(blk + 2 * i) = (uint16_t)codes;
+      if (i == 0) *(uint16_t*)(blk + 32) = (uint16_t)sbits;
+    }
+  } else {
+    // base-3 digits d = t mod 3 as 2-bit fields: 1 -> 01, -1 -> 10
+    const uint32_t digits = spread8(nz & ~neg) | (spread8(nz & neg) << 1);
+    // Lane i < 6 writes bytes 4i..4i+3 = weights 20i..20i+19, which start at
+    // slot o = 20i mod 8 of lane L = 20i / 8 and end inside lane L + 2.
+    // Lane 6 writes the two tail bytes (weights 120..127, all in lane 15) and
+    // the scale.
+    const int L = i < 6 ? (5 * i) >> 1 : 15;
+    const int o = i < 6 ? (i & 1) * 4 : 0;
+    const uint64_t d0 = lane_value(digits, row0 + L);
+    const uint64_t d1 = lane_value(digits, row0 + min(L + 1, 15));
+    const uint64_t d2 = lane_value(digits, row0 + min(L + 2, 15));
+    const uint64_t d = (d0 | (d1 << 16) | (d2 << 32)) >> (2 * o);
+    uint32_t word;
+    if (i < 6) {
+      word = base3_byte(d, 5) | (base3_byte(d >> 10, 5) << 8) | (base3_byte(d >> 20, 5) << 16) |
+             (base3_byte(d >> 30, 5) << 24);
+    } else {
+      word = base3_byte(d0, 4) | (base3_byte(d0 >> 8, 4) << 8) | (sbits << 16);
+    }
+    if (valid && i < 7) *(uint32_t*)(dst + g * 28 + 4 * i) = word;
+  }
+}
+
+template <int FMT>
+hipError_t launch_quantize_fmt(int method, const u32x4* w, int64_t groups, uint8_t* dst, hipStream_t stream) {
+  const int64_t blocks = (groups + kQuantGroupsPerBlock - 1) / kQuantGroupsPerBlock;
+  if (method == MOE_QUANT_LLOYD)
+    quantize_kernel<FMT, MOE_QUANT_LLOYD><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst);
+  else
+    quantize_kernel<FMT, MOE_QUANT_ABSMEAN><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t quantize_max_groups() { return (int64_t)0x7FFFFFFF * kQuantGroupsPerBlock; }
+
+hipError_t launch_quantize(int fmt, int method, const uint16_t* w, int64_t groups, uint8_t* dst,
+                           hipStream_t stream) {
+  const u32x4* wv = (const u32x4*)w;
+  return fmt == MOE_PQ2_0 ? launch_quantize_fmt<kPQ2>(method, wv, groups, dst, stream)
+                          : launch_quantize_fmt<kPTQ1>(method, wv, groups, dst, stream);
+}
+
+}  // namespace moe
