@@ -42,6 +42,19 @@ WORKLOADS = {
     "skewed-p16384": ("skewed", 16384, "prefill"),
 }
 DEFAULT_WORKLOAD = "olmoe-b64"
+# the ternary quantizer (bfloat16 weights -> containers) on every expert bank of a
+# layer: name -> (layer config, container id, rule 0 absmean / 1 Lloyd)
+QUANT_WORKLOADS = {
+    "quant-lloyd-a3b35": ("a3b35", 142, 1),
+    "quant-absmean-a3b35": ("a3b35", 142, 0),
+    "quant-lloyd-flashnext": ("flashnext", 143, 1),
+}
+QUANT_METRIC = "ternary quantizer weights/s (bf16 -> PQ2_0 / PTQ1_0, absmean or Lloyd g128)"
+# VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# algorithmic lane operations per weight: the absmean step (|w|, the group sum,
+# the code compare) and each Lloyd round (code compare, masked sum, count)
+QUANT_OPS_ABSMEAN, QUANT_OPS_ROUND = 3, 3
 DESCR = {
     "olmoe": "OLMoE-shaped MoE block (d=2048, 64 PQ2_0 experts, ffn 1024, top-8, rank-512 correction)",
     "a3b35": "35B-A3B-class MoE block (d=2048, 128 PQ2_0 experts, ffn 768, top-8, rank-512 correction)",
@@ -52,18 +65,23 @@ DESCR = {
 }
 
 
-def kernel_source_hash() -> str:
-    """Hash of the sources the expert (gate/up, down) kernels are compiled from."""
+EXPERT_SOURCES = ("device_common.h", "moe_experts.hip", "moe_internal.h")
+QUANT_SOURCES = ("device_common.h", "moe_quant.hip", "wave_ops.h")
+
+
+def kernel_source_hash(names=EXPERT_SOURCES) -> str:
+    """Hash of the sources a kernel is compiled from (by default the expert
+    gate/up and down kernels)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ternary_quantized_moe_amd", "csrc")
-    for name in ("device_common.h", "moe_experts.hip", "moe_internal.h"):
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, sources=EXPERT_SOURCES):
     """Measured HBM traffic of the dominant kernel (profiles/traffic.json), or
     None when absent or taken on a different kernel source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -71,7 +89,7 @@ def load_traffic(workload: str):
         rec = json.load(open(path)).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("src_sha") != kernel_source_hash():
+    if not rec or rec.get("src_sha") != kernel_source_hash(sources):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -305,6 +323,118 @@ def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     return rec
 
 
+# --------------------------------------------------------------------------- quantizer
+def quant_shape(workload: str):
+    from synthetic import CONFIGS
+    cname, fmt, method = QUANT_WORKLOADS[workload]
+    c = CONFIGS[cname]
+    return c, fmt, method, c.n_banks * 3 * c.d_ff, c.d_model
+
+
+def quant_cpu_baseline(fmt, method, d_w, out, rounds, budget_groups=65536):
+    """The oracle quantizer, as it stands, on the first groups of the input; its
+    containers and rounds are compared with the device's for the same groups."""
+    import numpy as np
+    from oracle import codec, quant
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    G = min(budget_groups if method == 1 else 16 * budget_groups, d_w.numel() // 128)
+    w = d_w.view(-1)[:G * 128].cpu().numpy().view(np.uint16)
+    reps, dt = 0, 0.0
+    while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
+        t0 = time.perf_counter()
+        t, sb, _, r = quant.quantize_groups(w, method)
+        data = codec.pack(fmt, t, sb)
+        dt += time.perf_counter() - t0
+        reps += 1
+    bb = codec.block_bytes(fmt)
+    got = out[:G * bb].cpu().numpy().reshape(G, bb)
+    bad = int(np.count_nonzero(np.any(got != data.reshape(G, bb), axis=1)))
+    bad_rounds = int(np.count_nonzero(rounds[:G].cpu().numpy() != r))
+    base = {"value": reps * G * 128 / dt, "unit": "weights/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {G} of {d_w.numel() // 128} groups, {reps} pass(es), {dt:.1f} s"}
+    return base, {"groups_checked": G, "groups_differing": bad, "rounds_differing": bad_rounds}
+
+
+def run_quant(workload: str, steps: int, warmup: int, with_cpu: bool = True):
+    import torch
+    import ternary_quantized_moe_amd as tq
+    from synthetic.weights import weights_bf16_device
+
+    c, fmt, method, rows, cols = quant_shape(workload)
+    n = rows * cols
+    groups = n // 128
+    bb = 34 if fmt == 142 else 28
+    t0 = time.time()
+    d_w = weights_bf16_device(rows, cols, seed=0).view(-1)
+    out = torch.empty(groups * bb, dtype=torch.uint8, device="cuda:0")
+    rounds = torch.empty(groups, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    for _ in range(warmup):
+        tq.quantize_device(fmt, method, d_w, out=out)
+    torch.cuda.synchronize()
+    # one kernel launch per step, bracketed by events on the launch stream
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        tq.quantize_device(fmt, method, d_w, out=out, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    # the rounds per group (untimed; the same input gives the same rounds)
+    tq.quantize_device(fmt, method, d_w, out=out, rounds=rounds)
+    mean_rounds = float(rounds.to(torch.float64).mean().item())
+    alg_bytes = 2 * n + groups * bb
+    alg_ops = n * (QUANT_OPS_ABSMEAN + QUANT_OPS_ROUND * mean_rounds)
+    hbm = alg_bytes / launch_s / 1e9
+    ops = alg_ops / launch_s / 1e12
+    src = QUANT_SOURCES
+    if method == 0:
+        roof = {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, src)}
+    else:
+        roof = {"bound": "alu", "achieved": round(ops, 2), "peak": round(ALU_PEAK_TOPS, 2), "unit": "TOP/s",
+                "frac": round(ops / ALU_PEAK_TOPS, 4), "traffic": load_traffic(workload, src),
+                "hbm_GBs": round(hbm, 1), "hbm_frac": round(hbm / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": "quantize_kernel", "alg_bytes_per_launch": int(alg_bytes),
+                 "alg_ops_per_launch": int(alg_ops), "mean_lloyd_rounds": round(mean_rounds, 4),
+                 "avg_launch_us": round(launch_s * 1e6, 2)})
+    rule = "Lloyd" if method == 1 else "absmean"
+    rec = {
+        "metric": QUANT_METRIC,
+        "value": round(steps * n / elapsed, 1),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{rule} ternary quantizer into {'PQ2_0' if fmt == 142 else 'PTQ1_0'} over every "
+                               f"expert bank of the {DESCR[c.name]}: {n} bfloat16 weights ({groups} groups)",
+                   "name": workload, "weights": n, "parallelism": "single-gpu", "setup_s": round(setup_s, 1)},
+        "roofline": roof,
+    }
+    if with_cpu:
+        print(f"{workload}: timed, {launch_s * 1e3:.3f} ms per launch; oracle on the host next",
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"], rec["parity"] = quant_cpu_baseline(fmt, method, d_w, out, rounds)
+    del d_w, out, rounds
+    torch.cuda.empty_cache()
+    return rec
+
+
 def calibrate_copy(mib: int, reps: int = 5):
     """Plain device copies of known size: each reads and writes mib MiB once."""
     import torch
@@ -323,7 +453,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS))
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -352,7 +482,10 @@ def main():
                   + " ".join(f"{k}={v * 1e3:.1f}" for k, v in rec["stages_ms"].items())
                   + f", parity {rec['parity_max_row_err']:.1e}", file=sys.stderr, flush=True)
         return
-    rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    if args.workload in QUANT_WORKLOADS:
+        rec = run_quant(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    else:
+        rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     print(json.dumps(rec), flush=True)
 
 

@@ -125,13 +125,17 @@ enum { MOE_QUANT_ABSMEAN = 0, MOE_QUANT_LLOYD = 1 };
  * pairs (weights 2m and 2m+1 first); the scale is rounded to binary16, nearest
  * even, saturating at 65504.  Weights must be finite (otherwise the codes and
  * scales of their groups are unspecified).  The result is a pure function of
- * the input bits.  d_w must be 16-byte and d_dst 4-byte aligned; the buffers
- * must not overlap.  Ordered on `stream`; nothing is allocated.
- * Errors: MOE_E_FORMAT, MOE_E_ARG (unknown method, NULL, misaligned),
- * MOE_E_SHAPE (n_weights negative, not a multiple of 128, or too large for one
- * launch: above 2^31 - 1 blocks of 16 groups), MOE_E_DEVICE. */
+ * the input bits.  d_rounds (device memory, n_weights/128 bytes, or NULL)
+ * receives per group the Lloyd rounds taken, the round that repeats the codes
+ * included (32 if none does); 0 for absmean.  d_w must be 16-byte and d_dst
+ * 4-byte aligned; the buffers must not overlap.  Ordered on `stream`; nothing
+ * is allocated.
+ * Errors: MOE_E_FORMAT, MOE_E_ARG (unknown method, NULL d_w or d_dst,
+ * misaligned, overlapping), MOE_E_SHAPE (n_weights negative, not a multiple of
+ * 128, or too large for one launch: above 2^31 - 1 blocks of 16 groups),
+ * MOE_E_DEVICE. */
 int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, int64_t n_weights,
-                            uint8_t* d_dst, void* stream);
+                            uint8_t* d_dst, uint8_t* d_rounds, void* stream);
 
 /* Host: reorder the blocks of a [rows x cols] container (rows % 16 == 0,
  * cols % 128 == 0) between the row-major order moe_pack writes and the

@@ -67,7 +67,7 @@ def lib():
             "moe_pack": (i32, [i32, vp, vp, i64, vp, i64]),
             "moe_unpack": (i32, [i32, vp, i64, vp, vp, i64]),
             "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
-            "moe_quantize_device": (i32, [i32, i32, vp, i64, vp, vp]),
+            "moe_quantize_device": (i32, [i32, i32, vp, i64, vp, vp, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -167,19 +167,24 @@ QUANT_ABSMEAN = 0
 QUANT_LLOYD = 1
 
 
-def quantize_device(fmt: int, method: int, d_w, out=None, stream=None):
+def quantize_device(fmt: int, method: int, d_w, out=None, rounds=None, stream=None):
     """bfloat16 weights (a contiguous device tensor, size a multiple of 128;
-    bf16 or int16 bit patterns) -> container bytes (uint8 device tensor)."""
+    bf16 or int16 bit patterns) -> container bytes (uint8 device tensor).
+    rounds: None, or a uint8 device tensor of n/128 entries that receives the
+    Lloyd rounds per group."""
     import torch
     n = d_w.numel()
     nbytes = lib().moe_packed_bytes(fmt, n)
     if nbytes < 0:
-        _check(lib().moe_quantize_device(fmt, method, None, n, None, _stream(stream)))
+        _check(lib().moe_quantize_device(fmt, method, None, n, None, None, _stream(stream)))
     if out is None:
         out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=d_w.device)
     elif out.numel() < nbytes:
         raise MoeError(-6, f"out holds {out.numel()} bytes, {nbytes} needed")
-    _check(lib().moe_quantize_device(fmt, method, _dev_ptr(d_w), n, _dev_ptr(out), _stream(stream)))
+    if rounds is not None and rounds.numel() < n // 128:
+        raise MoeError(-6, f"rounds holds {rounds.numel()} entries, {n // 128} needed")
+    _check(lib().moe_quantize_device(fmt, method, _dev_ptr(d_w), n, _dev_ptr(out), _dev_ptr(rounds),
+                                     _stream(stream)))
     return out[:nbytes]
 
 

@@ -327,7 +327,7 @@ int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n, int8_t* 
 }
 
 int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, int64_t n, uint8_t* d_dst,
-                            void* stream) {
+                            uint8_t* d_rounds, void* stream) {
   if (!known_fmt(fmt)) return bad_fmt(fmt);
   if (method != MOE_QUANT_ABSMEAN && method != MOE_QUANT_LLOYD)
     return fail(MOE_E_ARG, "unknown quantizer method %d; valid are 0 (absmean) and 1 (Lloyd)", (int)method);
@@ -341,7 +341,11 @@ int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, in
   const uintptr_t w0 = (uintptr_t)d_w, w1 = w0 + (uintptr_t)n * 2;
   const uintptr_t d0 = (uintptr_t)d_dst, d1 = d0 + (uintptr_t)(n / 128 * (fmt == MOE_PQ2_0 ? 34 : 28));
   if (w0 < d1 && d0 < w1) return fail(MOE_E_ARG, "d_w and d_dst overlap");
-  hipError_t e = moe::launch_quantize(fmt, method, d_w, n / 128, d_dst, (hipStream_t)stream);
+  if (d_rounds) {
+    const uintptr_t r0 = (uintptr_t)d_rounds, r1 = r0 + (uintptr_t)(n / 128);
+    if ((r0 < w1 && w0 < r1) || (r0 < d1 && d0 < r1)) return fail(MOE_E_ARG, "d_rounds overlaps d_w or d_dst");
+  }
+  hipError_t e = moe::launch_quantize(fmt, method, d_w, n / 128, d_dst, d_rounds, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "moe_quantize_device launch");
   return ok();
 }

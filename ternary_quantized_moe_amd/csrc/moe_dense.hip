@@ -256,17 +256,6 @@ void dense_gemm_kernel(DenseArgs a, const u32x4* w2, int N,
   }
 }
 
-static int cu_count_dense() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int EPI>
 hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream) {
   const int Kp = dense_kpad(a.K);
@@ -283,7 +272,7 @@ hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream) {
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kDenseWaves, kDenseLds);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
   const int64_t U = ((a.T + kDenseTok - 1) / kDenseTok) * ((N + kDenseRows - 1) / kDenseRows);
-  const int64_t grid = std::min<int64_t>((int64_t)cu_count_dense() * per_cu, U);
+  const int64_t grid = std::min<int64_t>((int64_t)cu_count() * per_cu, U);
   kern<<<dim3((unsigned)grid), 64 * kDenseWaves, kDenseLds, stream>>>(a, w2, N, Kp);
   return hipGetLastError();
 }

@@ -943,17 +943,6 @@ void down_resident_kernel(ExpertArgs a) {
   }
 }
 
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-  }
-  return n;
-}
-
 template <int MODE, int WPB, int KS, int RT, int D, int GW>
 static hipError_t launch_dec(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
   const int K = MODE == MODE_GATEUP ? a.d : a.f;

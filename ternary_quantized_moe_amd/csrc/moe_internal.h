@@ -122,11 +122,14 @@ struct ExpertArgs {
 
 hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
                                 uint16_t* scales, hipStream_t stream);
+// Compute units of the current device (256 if the query fails).
+int cu_count();
 // Quantizer: groups of 128 bfloat16 weights (w 16-byte aligned, dst 4-byte
-// aligned) -> container blocks; groups <= quantize_max_groups().
+// aligned) -> container blocks, and the Lloyd rounds per group if rounds is not
+// NULL; groups <= quantize_max_groups().
 int64_t quantize_max_groups();
 hipError_t launch_quantize(int fmt, int method, const uint16_t* w, int64_t groups, uint8_t* dst,
-                           hipStream_t stream);
+                           uint8_t* rounds, hipStream_t stream);
 int64_t dense_split_bytes(int N, int K);
 template <int EPI>
 hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream);

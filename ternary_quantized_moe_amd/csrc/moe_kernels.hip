@@ -72,6 +72,17 @@ __global__ __launch_bounds__(64) void unpack_device_kernel(const uint8_t* __rest
   if (q == 0) scales[b] = *(const uint16_t*)(blk + (FMT == kPQ2 ? 32 : 26));
 }
 
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
                                 uint16_t* scales, hipStream_t stream) {
   const int64_t nb = n_weights / kGroup;

@@ -40,17 +40,17 @@ constexpr uint32_t kF16MaxFinite = 0x7BFFu;
 
 // Sum over the 16 lanes of each row, returned to every lane of the row.
 __device__ __forceinline__ float row_sum(float v) {
-  v += dpp_f32<kDppXor1>(v);
-  v += dpp_f32<kDppXor2>(v);
-  v += dpp_f32<kDppHalfMirror>(v);
-  v += dpp_f32<kDppMirror>(v);
+  v += dpp_row_f32<kDppXor1>(v);
+  v += dpp_row_f32<kDppXor2>(v);
+  v += dpp_row_f32<kDppHalfMirror>(v);
+  v += dpp_row_f32<kDppMirror>(v);
   return v;
 }
 __device__ __forceinline__ int row_sum_i32(int v) {
-  v += dpp_i32<kDppXor1>(v);
-  v += dpp_i32<kDppXor2>(v);
-  v += dpp_i32<kDppHalfMirror>(v);
-  v += dpp_i32<kDppMirror>(v);
+  v += dpp_row_i32<kDppXor1>(v);
+  v += dpp_row_i32<kDppXor2>(v);
+  v += dpp_row_i32<kDppHalfMirror>(v);
+  v += dpp_row_i32<kDppMirror>(v);
   return v;
 }
 
@@ -59,22 +59,29 @@ __device__ __forceinline__ float tree8(const float (&v)[8]) {
   return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
-// Bit j set where 2 a_j > s (a nonzero code).
-__device__ __forceinline__ uint32_t nonzero_mask(const float (&a)[8], float s) {
+// The codes for scale s: bit j of the mask set where 2 a_j > s.  The sum of
+// the selected a_j (adjacent-pair tree) and their number over the group come
+// back in *total and *count.
+__device__ __forceinline__ uint32_t select_codes(const float (&a)[8], const float (&a2)[8], float s, float* total,
+                                                 int* count) {
   uint32_t m = 0;
+  int n = 0;
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) m |= (2.0f * a[j] > s ? 1u : 0u) << j;
+  for (int j = 0; j < 8; ++j) {
+    const bool on = a2[j] > s;
+    v[j] = on ? a[j] : 0.0f;
+    n += on ? 1 : 0;
+    m |= (on ? 1u : 0u) << j;
+  }
+  *total = row_sum(tree8(v));
+  *count = row_sum_i32(n);
   return m;
 }
 
-// fp32 mean of a over the nonzero codes of the group (0 if there are none).
-__device__ __forceinline__ float mean_of_nonzero(const float (&a)[8], uint32_t nz) {
-  float v[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (nz >> j) & 1u ? a[j] : 0.0f;
-  const float total = row_sum(tree8(v));
-  const int count = row_sum_i32(__popc(nz));
-  return count > 0 ? total / (float)count : 0.0f;
+__device__ __forceinline__ float mean_or_zero(float total, int count) {
+  const float q = total / (float)max(count, 1);
+  return count > 0 ? q : 0.0f;
 }
 
 // Eight bits -> the even bits of a 16-bit word (bit j -> bit 2j).
@@ -98,17 +105,13 @@ __device__ __forceinline__ uint32_t lane_value(uint32_t v, int src_lane) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src_lane << 2, (int)v);
 }
 
+// Quantize the group g of this lane's row; v holds lane i's eight weights of
+// it.  Rows past the last group (valid false) compute on zeros and store nothing.
 template <int FMT, int METHOD>
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __restrict__ w, int64_t groups,
-                                                                 uint8_t* __restrict__ dst) {
-  const int lane = threadIdx.x & 63, i = lane & 15, row0 = lane & 48;
-  const int64_t g = (int64_t)blockIdx.x * kQuantGroupsPerBlock + (threadIdx.x >> 4);
-  const bool valid = g < groups;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (valid) v = w[g * 16 + i];
-
-  // |w| in fp32 and the sign bits, weight 8i + j in slot j
-  float a[8];
+__device__ __forceinline__ void quantize_groups4(u32x4 v, int64_t g, bool valid, int i, int row0,
+                                                 uint8_t* __restrict__ dst, uint8_t* __restrict__ rounds) {
+  // |w| in fp32 (and 2|w|, exact) and the sign bits, weight 8i + j in slot j
+  float a[8], a2[8];
   uint32_t neg = 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -117,22 +120,34 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __
     neg |= ((v[k] >> 15) & 1u) << (2 * k);
     neg |= (v[k] >> 31) << (2 * k + 1);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a2[j] = 2.0f * a[j];
 
   float s = row_sum(tree8(a)) / 128.0f;
-  uint32_t nz = nonzero_mask(a, s);
+  float total;
+  int count;
+  uint32_t nz = select_codes(a, a2, s, &total, &count);
   if (METHOD == MOE_QUANT_LLOYD) {
-    bool fixed = false;
+    // The codes are the weights above a threshold, so two code sets of one
+    // group are nested and equal exactly when their sizes are: a round that
+    // keeps the count keeps the codes.  Each round's scale is the mean of the
+    // current codes; the loop ends with s the mean of the final codes.
+    // taken: the rounds this group needs, the one that repeats its codes
+    // included (kQuantMaxRounds if none does)
+    int taken = kQuantMaxRounds;
     for (int r = 0; r < kQuantMaxRounds; ++r) {
-      s = mean_of_nonzero(a, nz);
-      const uint32_t next = nonzero_mask(a, s);
-      const bool changed = __ballot(next != nz) != 0;  // wave-uniform
-      nz = next;
-      if (!changed) {
-        fixed = true;
-        break;
-      }
+      s = mean_or_zero(total, count);
+      int next_count;
+      nz = select_codes(a, a2, s, &total, &next_count);
+      if (next_count == count) taken = min(taken, r + 1);
+      const bool changed = __ballot(next_count != count) != 0;  // wave-uniform
+      count = next_count;
+      if (!changed) break;
     }
-    if (!fixed) s = mean_of_nonzero(a, nz);
+    s = mean_or_zero(total, count);
+    if (rounds && valid && i == 0) rounds[g] = (uint8_t)taken;
+  } else {
+    if (rounds && valid && i == 0) rounds[g] = 0;
   }
 
   uint32_t sbits = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)s);
@@ -170,13 +185,28 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __
   }
 }
 
+// One wave per four consecutive groups, one block per 16.  (A grid-stride
+// loop with the next groups loaded ahead measured slower at every grid size
+// tried: 4 to 32 blocks per CU.)
+template <int FMT, int METHOD>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __restrict__ w, int64_t groups,
+                                                                 uint8_t* __restrict__ dst, uint8_t* __restrict__ rounds) {
+  const int lane = threadIdx.x & 63, i = lane & 15, row0 = lane & 48;
+  const int64_t g = (int64_t)blockIdx.x * kQuantGroupsPerBlock + (threadIdx.x >> 4);
+  const bool valid = g < groups;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (valid) v = w[g * 16 + i];
+  quantize_groups4<FMT, METHOD>(v, g, valid, i, row0, dst, rounds);
+}
+
 template <int FMT>
-hipError_t launch_quantize_fmt(int method, const u32x4* w, int64_t groups, uint8_t* dst, hipStream_t stream) {
+hipError_t launch_quantize_fmt(int method, const u32x4* w, int64_t groups, uint8_t* dst, uint8_t* rounds,
+                               hipStream_t stream) {
   const int64_t blocks = (groups + kQuantGroupsPerBlock - 1) / kQuantGroupsPerBlock;
   if (method == MOE_QUANT_LLOYD)
-    quantize_kernel<FMT, MOE_QUANT_LLOYD><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst);
+    quantize_kernel<FMT, MOE_QUANT_LLOYD><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst, rounds);
   else
-    quantize_kernel<FMT, MOE_QUANT_ABSMEAN><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst);
+    quantize_kernel<FMT, MOE_QUANT_ABSMEAN><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst, rounds);
   return hipGetLastError();
 }
 
@@ -185,10 +215,10 @@ hipError_t launch_quantize_fmt(int method, const u32x4* w, int64_t groups, uint8
 int64_t quantize_max_groups() { return (int64_t)0x7FFFFFFF * kQuantGroupsPerBlock; }
 
 hipError_t launch_quantize(int fmt, int method, const uint16_t* w, int64_t groups, uint8_t* dst,
-                           hipStream_t stream) {
+                           uint8_t* rounds, hipStream_t stream) {
   const u32x4* wv = (const u32x4*)w;
-  return fmt == MOE_PQ2_0 ? launch_quantize_fmt<kPQ2>(method, wv, groups, dst, stream)
-                          : launch_quantize_fmt<kPTQ1>(method, wv, groups, dst, stream);
+  return fmt == MOE_PQ2_0 ? launch_quantize_fmt<kPQ2>(method, wv, groups, dst, rounds, stream)
+                          : launch_quantize_fmt<kPTQ1>(method, wv, groups, dst, rounds, stream);
 }
 
 }  // namespace moe

@@ -21,6 +21,17 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __int_as_float(dpp_i32<CTRL>(__float_as_int(v)));
 }
+// The same exchange for patterns that keep every lane inside its row and
+// every row enabled: no lane keeps its old value, so the compiler can fold the
+// move into the instruction that consumes it.
+template <int CTRL>
+__device__ __forceinline__ int dpp_row_i32(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_row_f32(float v) {
+  return __int_as_float(dpp_row_i32<CTRL>(__float_as_int(v)));
+}
 __device__ __forceinline__ float readlane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }

@@ -171,17 +171,19 @@ def test_quantize_validation():
     """Argument checks of moe_quantize_device happen on the host, before any launch."""
     L = tq.lib()
     w, out = 0x10000, 0x40000
-    assert L.moe_quantize_device(99, 0, w, 256, out, None) == -2
-    assert L.moe_quantize_device(142, 2, w, 256, out, None) == -1          # unknown method
-    assert L.moe_quantize_device(142, 0, w, 100, out, None) == -3          # not a multiple of 128
-    assert L.moe_quantize_device(143, 1, w, -128, out, None) == -3
-    assert L.moe_quantize_device(142, 0, w, 1 << 62, out, None) == -3      # beyond one launch
-    assert L.moe_quantize_device(142, 0, None, 128, out, None) == -1
-    assert L.moe_quantize_device(142, 0, w + 2, 128, out, None) == -1      # d_w not 16-byte aligned
-    assert L.moe_quantize_device(143, 0, w, 128, out + 2, None) == -1      # d_dst not 4-byte aligned
-    assert L.moe_quantize_device(142, 0, w, 256, w + 256, None) == -1      # overlap
+    assert L.moe_quantize_device(99, 0, w, 256, out, None, None) == -2
+    assert L.moe_quantize_device(142, 2, w, 256, out, None, None) == -1          # unknown method
+    assert L.moe_quantize_device(142, 0, w, 100, out, None, None) == -3          # not a multiple of 128
+    assert L.moe_quantize_device(143, 1, w, -128, out, None, None) == -3
+    assert L.moe_quantize_device(142, 0, w, 1 << 62, out, None, None) == -3      # beyond one launch
+    assert L.moe_quantize_device(142, 0, None, 128, out, None, None) == -1
+    assert L.moe_quantize_device(142, 0, w + 2, 128, out, None, None) == -1      # d_w not 16-byte aligned
+    assert L.moe_quantize_device(143, 0, w, 128, out + 2, None, None) == -1      # d_dst not 4-byte aligned
+    assert L.moe_quantize_device(142, 0, w, 256, w + 256, None, None) == -1      # overlap
     assert "overlap" in L.moe_last_error().decode()
-    assert L.moe_quantize_device(142, 0, w, 0, out, None) == 0
+    assert L.moe_quantize_device(142, 0, w, 256, out, out + 8, None) == -1       # rounds overlap dst
+    assert L.moe_quantize_device(142, 0, w, 256, out, w + 2, None) == -1         # rounds overlap w
+    assert L.moe_quantize_device(142, 0, w, 0, out, None, None) == 0
 
 
 def _plain_to_tiles(data, rows, cols, bb):

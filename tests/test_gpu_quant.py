@@ -33,11 +33,13 @@ def gpu():
 
 
 def gpu_quantize(fmt, method, w_bits):
+    """(container bytes, Lloyd rounds per group) from the device quantizer."""
     import ternary_quantized_moe_amd as tq
     d_w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).cuda()
-    out = tq.quantize_device(fmt, method, d_w)
+    rounds = torch.full((w_bits.size // 128,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = tq.quantize_device(fmt, method, d_w, rounds=rounds)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    return out.cpu().numpy(), rounds.cpu().numpy()
 
 
 def assert_same_blocks(fmt, got, want):
@@ -87,8 +89,9 @@ def special_groups():
 def test_quantize_bit_exact(fmt, method, groups):
     w = weights_bf16(groups, 128, seed=groups).reshape(-1)
     say(f"quantize fmt={fmt} method={method} groups={groups}")
-    got = gpu_quantize(fmt, method, w)
+    got, rounds = gpu_quantize(fmt, method, w)
     assert_same_blocks(fmt, got, quant.quantize(fmt, w, method))
+    assert np.array_equal(rounds, quant.quantize_groups(w, method)[3])
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -96,13 +99,14 @@ def test_quantize_bit_exact(fmt, method, groups):
 def test_quantize_special_groups(fmt, method):
     w = special_groups()
     say(f"quantize special groups fmt={fmt} method={method}")
-    got = gpu_quantize(fmt, method, w)
+    got, got_rounds = gpu_quantize(fmt, method, w)
     with np.errstate(over="ignore"):
         want = quant.quantize(fmt, w, method)
         _, _, _, rounds = quant.quantize_groups(w, method)
     if method == quant.LLOYD:
         assert rounds.max() == quant.MAX_ROUNDS  # the capped path is covered
     assert_same_blocks(fmt, got, want)
+    assert np.array_equal(got_rounds, rounds)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -115,15 +119,17 @@ def test_quantize_full_matrix_sampled(fmt, method):
     rows, cols = 128 * 3 * 768, 2048
     d_w = weights_bf16_device(rows, cols, seed=fmt + 2 * method)
     say(f"quantize full matrix fmt={fmt} method={method} rows={rows} cols={cols}")
-    out = tq.quantize_device(fmt, method, d_w)
+    n_groups = rows * cols // 128
+    rounds = torch.empty(n_groups, dtype=torch.uint8, device="cuda")
+    out = tq.quantize_device(fmt, method, d_w, rounds=rounds)
     torch.cuda.synchronize()
     bb = codec.block_bytes(fmt)
-    n_groups = rows * cols // 128
     pick = np.sort(np.random.default_rng(5).choice(n_groups, 9216, replace=False))
     w_groups = d_w.view(-1, 128).cpu().numpy().view(np.uint16)[pick]
     got = out.view(-1, bb).cpu().numpy()[pick]
     want = quant.quantize(fmt, w_groups.reshape(-1), method)
     assert_same_blocks(fmt, got.reshape(-1), want)
+    assert np.array_equal(rounds.cpu().numpy()[pick], quant.quantize_groups(w_groups.reshape(-1), method)[3])
 
 
 def test_quantize_two_calls_and_offsets():
