@@ -17,7 +17,11 @@ routing and its own expert evaluation, written from the release pages:
     Representation"; "What the experiments established" (placement rule);
   * top-k routing with an always-on shared expert: FlashNext card "Model
     Overview" (top-10 routed + 1 shared); 35B-A3B card "Model Overview";
-  * per-expert grouping of tokens (mul_mat_id): Scion README "Serving notes".
+  * per-expert grouping of tokens (mul_mat_id): Scion README "Serving notes";
+  * the ternary quantizers (absmean, Lloyd over groups of 128): project README,
+    "What the experiments established" (quant.py);
+  * the Q4_0 per-row n-gram table decode: FlashNext card, "Model Overview" and
+    "Weight Representation" (ple.py).
 
 Where the pages are silent the readings are those listed in the package's design
 notes (two's-complement 2-bit codes, little-endian base-3 digits, SwiGLU,
@@ -25,4 +29,4 @@ softmax over the selected k, ties to the lower expert index, correction input =
 block input).  Everything is evaluated in float64 from the exact bits the GPU
 receives.
 """
-from . import codec, moe  # noqa: F401
+from . import codec, moe, ple, quant  # noqa: F401
