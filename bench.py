@@ -49,6 +49,10 @@ QUANT_WORKLOADS = {
     "quant-absmean-a3b35": ("a3b35", 142, 0),
     "quant-lloyd-flashnext": ("flashnext", 143, 1),
 }
+# the Q4_0 n-gram table gather: name -> (tokens, rows per token)
+PLE_WORKLOADS = {"ple-b64": (64, 48), "ple-p4096": (4096, 48)}
+PLE_ROWS, PLE_ROW_LEN = 320_001_536, 160
+PLE_METRIC = "Q4_0 n-gram table rows gathered and decoded per second"
 QUANT_METRIC = "ternary quantizer weights/s (bf16 -> PQ2_0 / PTQ1_0, absmean or Lloyd g128)"
 # VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -67,6 +71,7 @@ DESCR = {
 
 EXPERT_SOURCES = ("device_common.h", "moe_experts.hip", "moe_internal.h")
 QUANT_SOURCES = ("device_common.h", "moe_quant.hip", "wave_ops.h")
+PLE_SOURCES = ("device_common.h", "moe_ple.hip")
 
 
 def kernel_source_hash(names=EXPERT_SOURCES) -> str:
@@ -435,6 +440,94 @@ def run_quant(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     return rec
 
 
+# --------------------------------------------------------------------------- n-gram table
+def ple_cpu_baseline(d_table, d_idx, out, budget_rows=4096):
+    """The oracle row decode, as it stands, on the first rows of the row list;
+    its rows are compared with the device's."""
+    import numpy as np
+    import torch
+    from oracle import ple
+    n = min(budget_rows, d_idx.numel())
+    rows = d_idx[:n]
+    sub = d_table[rows].cpu().numpy()                 # the sample's table rows, in list order
+    reps, dt = 0, 0.0
+    while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
+        t0 = time.perf_counter()
+        want = ple.gather(sub, n, PLE_ROW_LEN, np.arange(n))
+        dt += time.perf_counter() - t0
+        reps += 1
+    got = out[:n].cpu().numpy().astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    base = {"value": reps * n / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {d_idx.numel()} rows of the list, {reps} pass(es), {dt:.1f} s"}
+    return base, {"rows_checked": n, "rows_differing": int(np.count_nonzero(~same.all(axis=1)))}
+
+
+def run_ple(workload: str, steps: int, warmup: int, with_cpu: bool = True):
+    import torch
+    import ternary_quantized_moe_amd as tq
+    from synthetic.ple import q4_table_device, row_list_device
+
+    tokens, per_token = PLE_WORKLOADS[workload]
+    n_idx = tokens * per_token
+    t0 = time.time()
+    d_table = q4_table_device(PLE_ROWS, PLE_ROW_LEN, seed=0)
+    # P row lists, one per step in turn, so each step reads other rows
+    P = 16 if tokens <= 64 else 4
+    lists = [row_list_device(n_idx, PLE_ROWS, seed=p) for p in range(P)]
+    out = torch.empty((n_idx, PLE_ROW_LEN), dtype=torch.float32, device="cuda:0")
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    for i in range(warmup):
+        tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    row_bytes = PLE_ROW_LEN // 32 * 18
+    alg_bytes = n_idx * (8 + row_bytes + 4 * PLE_ROW_LEN)       # index, Q4_0 row, fp32 row
+    hbm = alg_bytes / launch_s / 1e9
+    rec = {
+        "metric": PLE_METRIC,
+        "value": round(steps * n_idx / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed * 1e3 / steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"gather and decode of {n_idx} rows ({tokens} tokens x {per_token} rows) of a "
+                               f"Q4_0 n-gram table of {PLE_ROWS} rows x {PLE_ROW_LEN} values "
+                               f"({PLE_ROWS * row_bytes / 1e9:.1f} GB, rows uniform at random) into fp32",
+                   "name": workload, "rows": n_idx, "row_lists": P, "parallelism": "single-gpu",
+                   "setup_s": round(setup_s, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, PLE_SOURCES),
+                     "kernel": "ple_gather_kernel", "alg_bytes_per_launch": int(alg_bytes),
+                     "avg_launch_us": round(launch_s * 1e6, 2)},
+    }
+    if with_cpu:
+        print(f"{workload}: timed, {launch_s * 1e6:.1f} us per launch; oracle on the host next",
+              file=sys.stderr, flush=True)
+        rec["cpu_baseline"], rec["parity"] = ple_cpu_baseline(d_table, lists[0], out if P == 1 else
+                                                              tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN,
+                                                                            lists[0]))
+    del d_table, lists, out
+    torch.cuda.empty_cache()
+    return rec
+
+
 def calibrate_copy(mib: int, reps: int = 5):
     """Plain device copies of known size: each reads and writes mib MiB once."""
     import torch
@@ -453,7 +546,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(PLE_WORKLOADS))
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -484,6 +578,8 @@ def main():
         return
     if args.workload in QUANT_WORKLOADS:
         rec = run_quant(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    elif args.workload in PLE_WORKLOADS:
+        rec = run_ple(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     else:
         rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     print(json.dumps(rec), flush=True)

@@ -137,6 +137,27 @@ enum { MOE_QUANT_ABSMEAN = 0, MOE_QUANT_LLOYD = 1 };
 int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, int64_t n_weights,
                             uint8_t* d_dst, uint8_t* d_rounds, void* stream);
 
+/* Device: gather rows of a Q4_0 table and decode them to fp32.  The FlashNext
+ * release keeps its n-gram table (320,001,536 rows of 160 values, 28.8 GB) as
+ * one Q4_0 tensor with groups of 32 along each row, decoded per row
+ * (Scion-FlashNext-176B-A6B card, "Model Overview" and "Weight Representation:
+ * ternary PTQ1_0 + trained corrections + Q4_0 PLE").  The format is read as
+ * ggml's Q4_0 block: 18 bytes per 32 values, a binary16 scale d (little-
+ * endian), then 16 code bytes whose low nibbles hold values 0..15 and high
+ * nibbles values 16..31; value = d * (nibble - 8).  Rows of row_len values
+ * (a multiple of 32) lie back to back, row_len / 32 * 18 bytes each.
+ *   d_table  device, n_rows rows, 2-byte aligned
+ *   d_idx    device int64 row numbers, n_idx of them, 8-byte aligned
+ *   d_out    device fp32 [n_idx x row_len], 16-byte aligned; row i = decoded
+ *            row d_idx[i] (exact: every d * (nibble - 8) is an fp32 value).
+ *            An index outside [0, n_rows) gives a row of quiet NaN and reads
+ *            nothing; duplicates are allowed.
+ * Ordered on `stream`; nothing is allocated.  Errors: MOE_E_SHAPE (row_len not
+ * a positive multiple of 32, negative counts), MOE_E_ARG (NULL, misaligned),
+ * MOE_E_DEVICE. */
+int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_len, const int64_t* d_idx,
+                            int64_t n_idx, float* d_out, void* stream);
+
 /* Host: reorder the blocks of a [rows x cols] container (rows % 16 == 0,
  * cols % 128 == 0) between the row-major order moe_pack writes and the
  * tile-major order the expert kernels read.  With G = cols / 128, block

@@ -25,7 +25,7 @@ _ERRORS = {
 
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
-    "moe_quantize_device",
+    "moe_quantize_device", "moe_ple_gather_q4_0",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -68,6 +68,7 @@ def lib():
             "moe_unpack": (i32, [i32, vp, i64, vp, vp, i64]),
             "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
             "moe_quantize_device": (i32, [i32, i32, vp, i64, vp, vp, vp]),
+            "moe_ple_gather_q4_0": (i32, [vp, i64, i32, vp, i64, vp, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -186,6 +187,20 @@ def quantize_device(fmt: int, method: int, d_w, out=None, rounds=None, stream=No
     _check(lib().moe_quantize_device(fmt, method, _dev_ptr(d_w), n, _dev_ptr(out), _dev_ptr(rounds),
                                      _stream(stream)))
     return out[:nbytes]
+
+
+def ple_gather(d_table, n_rows: int, row_len: int, d_idx, out=None, stream=None):
+    """Rows d_idx (int64 device tensor) of a Q4_0 table (uint8 device tensor of
+    n_rows rows of row_len values) -> fp32 device tensor [len(d_idx), row_len]."""
+    import torch
+    n = d_idx.numel()
+    if out is None:
+        out = torch.empty((n, row_len), dtype=torch.float32, device=d_idx.device)
+    elif out.numel() < n * row_len:
+        raise MoeError(-6, f"out holds {out.numel()} values, {n * row_len} needed")
+    _check(lib().moe_ple_gather_q4_0(_dev_ptr(d_table), n_rows, row_len, _dev_ptr(d_idx), n, _dev_ptr(out),
+                                     _stream(stream)))
+    return out
 
 
 class ExpertBanks:

@@ -350,6 +350,22 @@ int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, in
   return ok();
 }
 
+int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_len, const int64_t* d_idx,
+                            int64_t n_idx, float* d_out, void* stream) {
+  if (row_len <= 0 || row_len % 32)
+    return fail(MOE_E_SHAPE, "row length %d is not a positive multiple of 32", (int)row_len);
+  if (n_rows < 0 || n_idx < 0)
+    return fail(MOE_E_SHAPE, "negative count (rows %lld, indices %lld)", (long long)n_rows, (long long)n_idx);
+  if (n_idx == 0) return ok();
+  if (!d_idx || !d_out || (!d_table && n_rows > 0)) return fail(MOE_E_ARG, "NULL pointer");
+  if ((uintptr_t)d_table % 2) return fail(MOE_E_ARG, "d_table must be 2-byte aligned");
+  if ((uintptr_t)d_idx % 8) return fail(MOE_E_ARG, "d_idx must be 8-byte aligned");
+  if ((uintptr_t)d_out % 16) return fail(MOE_E_ARG, "d_out must be 16-byte aligned");
+  hipError_t e = moe::launch_ple_gather(d_table, n_rows, row_len, d_idx, n_idx, d_out, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "moe_ple_gather_q4_0 launch");
+  return ok();
+}
+
 int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k) {
   if (n_tokens < 0 || n_experts < 1 || top_k < 1) return -1;
   return make_plan(n_tokens, d_model, n_experts, 0, 128, top_k, 0).route_end;

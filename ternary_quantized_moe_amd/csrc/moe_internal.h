@@ -122,6 +122,10 @@ struct ExpertArgs {
 
 hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, int8_t* trits,
                                 uint16_t* scales, hipStream_t stream);
+// Q4_0 row gather: rows idx[0..n_idx) of a table of n_rows rows of row_len
+// values (row_len % 32 == 0; table 2-byte, out 16-byte aligned) -> fp32 rows.
+hipError_t launch_ple_gather(const uint8_t* table, int64_t n_rows, int row_len, const int64_t* idx, int64_t n_idx,
+                             float* out, hipStream_t stream);
 // Compute units of the current device (256 if the query fails).
 int cu_count();
 // Quantizer: groups of 128 bfloat16 weights (w 16-byte aligned, dst 4-byte

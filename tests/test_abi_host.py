@@ -186,6 +186,21 @@ def test_quantize_validation():
     assert L.moe_quantize_device(142, 0, w, 0, out, None, None) == 0
 
 
+def test_ple_gather_validation():
+    """Argument checks of moe_ple_gather_q4_0 happen on the host, before any launch."""
+    L = tq.lib()
+    t, i, o = 0x10000, 0x20000, 0x40000
+    assert L.moe_ple_gather_q4_0(t, 10, 100, i, 4, o, None) == -3          # row length not a multiple of 32
+    assert L.moe_ple_gather_q4_0(t, 10, 0, i, 4, o, None) == -3
+    assert L.moe_ple_gather_q4_0(t, -1, 64, i, 4, o, None) == -3
+    assert L.moe_ple_gather_q4_0(t, 10, 64, i, -4, o, None) == -3
+    assert L.moe_ple_gather_q4_0(t, 10, 64, None, 4, o, None) == -1
+    assert L.moe_ple_gather_q4_0(t + 1, 10, 64, i, 4, o, None) == -1      # table not 2-byte aligned
+    assert L.moe_ple_gather_q4_0(t, 10, 64, i + 4, 4, o, None) == -1      # indices not 8-byte aligned
+    assert L.moe_ple_gather_q4_0(t, 10, 64, i, 4, o + 8, None) == -1      # output not 16-byte aligned
+    assert L.moe_ple_gather_q4_0(t, 10, 64, i, 0, o, None) == 0           # nothing to do
+
+
 def _plain_to_tiles(data, rows, cols, bb):
     """The tile-major order written as a numpy reshape: [row tile][group][row in tile]."""
     G = cols // 128
