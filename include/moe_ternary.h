@@ -216,6 +216,27 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t n_tokens, const uint16_t*
                             int32_t top_k, uint16_t* y, void* workspace, int64_t workspace_bytes,
                             void* stream);
 
+/* The same forward pass with the router delta and the correction stored as
+ * ternary PQ2_0 containers, the way the 35B-A3B release ships them (Scion-
+ * 35B-A3B card, "Weight Representation" and "Shipped Components": the
+ * rank-512 corrections and the exact router deltas in the legacy q1_0_g128
+ * container, whose bytes are PQ2_0's).
+ *   router_delta_q  device PQ2_0 [E x d_model], or NULL for a zero delta
+ *   corr_A_q        device PQ2_0 [corr_rank x d_model], corr_B_q PQ2_0
+ *                   [d_model x corr_rank] (corr_rank a multiple of 128); both
+ *                   NULL with corr_rank = 0
+ * The containers are in moe_pack's row-major group order, 2-byte aligned.  A
+ * code times its group scale is an fp16 value, and the kernels expand the
+ * codes into exactly those fp16 operands, so the result equals bit for bit that
+ * of moe_ternary_forward given the fp16 matrices s * t; only 34 bytes per 128
+ * weights are read instead of 256.  Other arguments, the workspace and the
+ * errors are those of moe_ternary_forward; codes are not re-validated. */
+int32_t moe_ternary_forward_q(const uint16_t* x, int64_t n_tokens, const uint16_t* router,
+                              const uint8_t* router_delta_q, const moe_expert_banks* banks,
+                              const uint8_t* corr_A_q, const uint8_t* corr_B_q, int32_t corr_rank,
+                              int32_t top_k, uint16_t* y, void* workspace, int64_t workspace_bytes,
+                              void* stream);
+
 /* Workspace bytes moe_route needs. */
 int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts,
                                   int32_t top_k);

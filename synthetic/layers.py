@@ -29,8 +29,14 @@ import numpy as np
 PQ2_0 = 142    # format ids used by the fork for its containers
 PTQ1_0 = 143   # (Scion-35B-A3B card "Quickstart"; FlashNext card "About the Hub's quant chip")
 
-# stream kinds (fixed order: x, W_r, dW_r, codes, scales, A, B, outliers, format map, zipf)
+# stream kinds (fixed order: x, W_r, dW_r, codes, scales, A, B, outliers, format map, zipf,
+# ternary-coded dW_r, A, B)
 _K_X, _K_WR, _K_DWR, _K_CODES, _K_SCALES, _K_A, _K_B, _K_OUTL, _K_FMT, _K_ZIPF = range(10)
+_K_DWR_Q, _K_A_Q, _K_B_Q = 10, 11, 12
+# group-scale spread of the ternary-coded router delta and correction: a
+# ternary code set with P(+-1) = 0.3 each and scale |N(0, sigma)| has about the
+# magnitude of the dense N(0, 0.002) delta and N(0, 0.01) factors
+_Q_SIGMA = {_K_DWR_Q: 0.003, _K_A_Q: 0.015, _K_B_Q: 0.015}
 
 # Zipf popularity enters through a constant "massive activation" channel 0 of x
 # and router column 0 = tau * ln p_e.  tau was chosen once so the hottest expert
@@ -140,6 +146,27 @@ class LayerGen:
     def corr_b_bits(self) -> np.ndarray:
         c = self.cfg
         return f16_bits(self.rng(_K_B).normal(0.0, 0.01, size=(c.d_model, c.rank)))
+
+    # -- ternary-coded router delta and correction -----------------------------
+    def _ternary(self, kind: int, rows: int, cols: int):
+        u = self.rng(kind, 0).integers(0, 10, size=(rows, cols), dtype=np.uint8)
+        s = np.abs(self.rng(kind, 1).normal(0.0, _Q_SIGMA[kind], size=(rows, cols // 128)))
+        return _TRIT_LUT[u], f16_bits(s)
+
+    def delta_q_parts(self):
+        """(trits int8 [E, d], scale bits uint16 [E, d/128]) of a ternary-coded router delta."""
+        c = self.cfg
+        return self._ternary(_K_DWR_Q, c.n_experts, c.d_model)
+
+    def corr_a_q_parts(self):
+        """(trits [r, d], scale bits [r, d/128]) of a ternary-coded correction A."""
+        c = self.cfg
+        return self._ternary(_K_A_Q, c.rank, c.d_model)
+
+    def corr_b_q_parts(self):
+        """(trits [d, r], scale bits [d, r/128]) of a ternary-coded correction B."""
+        c = self.cfg
+        return self._ternary(_K_B_Q, c.d_model, c.rank)
 
     # -- expert banks -------------------------------------------------------
     def formats(self) -> np.ndarray:

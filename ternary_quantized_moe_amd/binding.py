@@ -25,7 +25,7 @@ _ERRORS = {
 
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
-    "moe_quantize_device", "moe_ple_gather_q4_0",
+    "moe_quantize_device", "moe_ple_gather_q4_0", "moe_ternary_forward_q",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -69,6 +69,8 @@ def lib():
             "moe_unpack_device": (i32, [i32, vp, i64, vp, vp, vp]),
             "moe_quantize_device": (i32, [i32, i32, vp, i64, vp, vp, vp]),
             "moe_ple_gather_q4_0": (i32, [vp, i64, i32, vp, i64, vp, vp]),
+            "moe_ternary_forward_q": (i32, [vp, i64, vp, vp, ctypes.POINTER(ExpertBanksC), vp, vp, i32,
+                                            i32, vp, vp, i64, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -276,6 +278,27 @@ def forward(x, router, router_delta, banks: ExpertBanks, corr_a, corr_b, top_k: 
     _check(lib().moe_ternary_forward(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta), banks.c,
                                      _dev_ptr(corr_a), _dev_ptr(corr_b), r, top_k, _dev_ptr(y), wp, wn,
                                      _stream(stream)))
+    return y
+
+
+def forward_q(x, router, router_delta_q, banks: ExpertBanks, corr_a_q, corr_b_q, corr_rank: int, top_k: int,
+              y=None, workspace=None, stream=None):
+    """forward() with the router delta and the correction given as ternary PQ2_0
+    containers (uint8 device tensors in moe_pack's row-major order, or None)."""
+    import torch
+    T = x.shape[0]
+    r = 0 if corr_a_q is None else corr_rank
+    if y is None:
+        y = torch.empty_like(x)
+    need = workspace_bytes(banks, T, top_k, r)
+    if need < 0:
+        raise MoeError(-1, "invalid arguments for the workspace size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_ternary_forward_q(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta_q), banks.c,
+                                       _dev_ptr(corr_a_q), _dev_ptr(corr_b_q), r, top_k, _dev_ptr(y), wp, wn,
+                                       _stream(stream)))
     return y
 
 

@@ -376,10 +376,13 @@ int64_t moe_workspace_bytes(const moe_expert_banks* banks, int64_t n_tokens, int
   return make_plan(n_tokens, banks->d_model, banks->n_experts, banks->n_shared, banks->d_ff, top_k, corr_rank).total;
 }
 
+// delta_q, corr_A_q: the router delta and A as ternary PQ2_0 containers (in
+// place of delta, corr_A), or NULL.
 static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, const uint16_t* router,
-                          const uint16_t* delta, const uint16_t* corr_A, int r, int k, const Plan& p,
-                          void* ws, hipStream_t stream, float* logits, int32_t* idx, float* w,
-                          int32_t* counts, int32_t* offsets, int32_t* perm) {
+                          const uint16_t* delta, const uint8_t* delta_q, const uint16_t* corr_A,
+                          const uint8_t* corr_A_q, int r, int k, const Plan& p, void* ws, hipStream_t stream,
+                          float* logits, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
+                          int32_t* perm) {
   moe::DenseArgs da{};
   da.act = x;
   da.lda = d;
@@ -387,9 +390,11 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.K = d;
   da.w0 = router;
   da.w0b = delta;
+  da.q0b = delta_q;
   da.N0 = E;
   da.w1 = corr_A;
-  da.N1 = corr_A ? r : 0;
+  da.q1 = corr_A_q;
+  da.N1 = (corr_A || corr_A_q) ? r : 0;
   da.logits = logits;
   da.z = at<uint16_t>(ws, p.z);
   da.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
@@ -443,8 +448,8 @@ int32_t moe_route(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint
     const Plan p = make_plan(T, d, E, 0, 128, k, 0);
     if (ws_bytes < p.route_end)
       return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.route_end);
-    rc = route_impl(x, T, d, E, 0, router, delta, nullptr, 0, k, p, ws, (hipStream_t)stream, logits, idx, w,
-                    counts, offsets, perm);
+    rc = route_impl(x, T, d, E, 0, router, delta, nullptr, nullptr, nullptr, 0, k, p, ws, (hipStream_t)stream,
+                    logits, idx, w, counts, offsets, perm);
     if (rc) return rc;
     return ok();
   } catch (...) {
@@ -452,20 +457,28 @@ int32_t moe_route(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint
   }
 }
 
-int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
-                            const moe_expert_banks* banks, const uint16_t* corr_A, const uint16_t* corr_B,
-                            int32_t r, int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
-  try {
+// The forward pass with the router delta and the correction either dense fp16
+// (delta, corr_A, corr_B) or ternary PQ2_0 containers (delta_q, corr_A_q,
+// corr_B_q); the caller passes one form of each.
+static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
+                            const uint8_t* delta_q, const moe_expert_banks* banks, const uint16_t* corr_A,
+                            const uint8_t* corr_A_q, const uint16_t* corr_B, const uint8_t* corr_B_q, int32_t r,
+                            int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
+  {
     int32_t rc = check_banks(banks);
     if (rc) return rc;
     const int d = banks->d_model, f = banks->d_ff, E = banks->n_experts, S = banks->n_shared;
     rc = check_dims(T, d, E, k);
     if (rc) return rc;
     if (r < 0) return fail(MOE_E_ARG, "corr_rank must be >= 0 (got %d)", r);
-    if ((corr_A == nullptr) != (corr_B == nullptr))
-      return fail(MOE_E_ARG, "corr_A and corr_B must both be given or both be NULL");
-    if (corr_A && r == 0) return fail(MOE_E_ARG, "corr_rank is 0 but corr_A/corr_B are given");
-    if (!corr_A) r = 0;
+    const bool has_A = corr_A || corr_A_q, has_B = corr_B || corr_B_q;
+    if (has_A != has_B) return fail(MOE_E_ARG, "corr_A and corr_B must both be given or both be NULL");
+    if (has_A && r == 0) return fail(MOE_E_ARG, "corr_rank is 0 but corr_A/corr_B are given");
+    if (!has_A) r = 0;
+    if (corr_A_q && r % 128)
+      return fail(MOE_E_SHAPE, "a ternary corr_B needs corr_rank to be a multiple of 128 (got %d)", r);
+    if ((uintptr_t)delta_q % 2 || (uintptr_t)corr_A_q % 2 || (uintptr_t)corr_B_q % 2)
+      return fail(MOE_E_ARG, "ternary containers must be 2-byte aligned");
     if (r % 8) return fail(MOE_E_SHAPE, "corr_rank must be a multiple of 8 (got %d)", r);
     if (r > 4096) return fail(MOE_E_SHAPE, "corr_rank above 4096 is not supported (got %d)", r);
     if (T == 0) return ok();
@@ -478,9 +491,9 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
       return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
     const hipStream_t st = (hipStream_t)stream;
 
-    rc = route_impl(x, T, d, E, S, router, delta, corr_A, r, k, p, ws, st, at<float>(ws, p.logits),
-                    at<int32_t>(ws, p.idx), at<float>(ws, p.w), at<int32_t>(ws, p.counts),
-                    at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm));
+    rc = route_impl(x, T, d, E, S, router, delta, delta_q, corr_A, corr_A_q, r, k, p, ws, st,
+                    at<float>(ws, p.logits), at<int32_t>(ws, p.idx), at<float>(ws, p.w),
+                    at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm));
     if (rc) return rc;
 
     moe::ExpertArgs ea{};
@@ -514,6 +527,7 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     ca.T = T;
     ca.K = r;
     ca.w0 = corr_B;
+    ca.q0 = corr_B_q;
     ca.N0 = d;
     ca.slots = at<uint16_t>(ws, p.slots);
     ca.top_k = k;
@@ -525,8 +539,28 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
     if (e == hipSuccess) e = stage_mark(4, true, st);
     if (e != hipSuccess) return device_fail(e, "combine launch");
     return ok();
+  }
+}
+
+int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
+                            const moe_expert_banks* banks, const uint16_t* corr_A, const uint16_t* corr_B,
+                            int32_t r, int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    return forward_impl(x, T, router, delta, nullptr, banks, corr_A, nullptr, corr_B, nullptr, r, k, y, ws,
+                        ws_bytes, stream);
   } catch (...) {
     return fail(MOE_E_ARG, "internal error in moe_ternary_forward");
+  }
+}
+
+int32_t moe_ternary_forward_q(const uint16_t* x, int64_t T, const uint16_t* router, const uint8_t* delta_q,
+                              const moe_expert_banks* banks, const uint8_t* corr_A_q, const uint8_t* corr_B_q,
+                              int32_t r, int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    return forward_impl(x, T, router, nullptr, delta_q, banks, nullptr, corr_A_q, nullptr, corr_B_q, r, k, y, ws,
+                        ws_bytes, stream);
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_ternary_forward_q");
   }
 }
 

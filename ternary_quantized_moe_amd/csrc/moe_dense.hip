@@ -17,6 +17,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "dense_rows.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -52,14 +53,18 @@ __global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, 
   const int n = tile * 16 + i16, k = g * kGroup + 8 * c;
   u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
   if (k < a.K && n < N) {
+    const int64_t rb = pq2_row_bytes(a.K);
     if (n < a.N0) {
-      const u32x4 w = *(const u32x4_a4*)(a.w0 + (int64_t)n * a.K + k);
-      if (a.w0b)
+      const u32x4 w = a.q0 ? pq2_row_f16x8(a.q0 + n * rb, k) : *(const u32x4_a4*)(a.w0 + (int64_t)n * a.K + k);
+      if (a.q0b)
+        split_sum_f16x8(w, pq2_row_f16x8(a.q0b + n * rb, k), hi, lo);
+      else if (a.w0b)
         split_sum_f16x8(w, *(const u32x4_a4*)(a.w0b + (int64_t)n * a.K + k), hi, lo);
       else
         split_f16x8(w, hi, lo);
     } else {
-      split_f16x8(*(const u32x4_a4*)(a.w1 + (int64_t)(n - a.N0) * a.K + k), hi, lo);
+      split_f16x8(a.q1 ? pq2_row_f16x8(a.q1 + (n - a.N0) * rb, k)
+                       : *(const u32x4_a4*)(a.w1 + (int64_t)(n - a.N0) * a.K + k), hi, lo);
     }
   }
   const int m = c >> 2, q = c & 3;

@@ -33,12 +33,17 @@ struct DenseArgs {
   int64_t lda;
   int64_t T;
   int K;
-  // weight rows [0, N0) = w0 (+ w0b, summed in fp32), rows [N0, N0+N1) = w1; fp16, row stride K
+  // weight rows [0, N0) = w0 (+ w0b, summed in fp32), rows [N0, N0+N1) = w1; fp16, row stride K.
+  // q0, q0b, q1: the same operands as ternary PQ2_0 rows (row-major groups,
+  // K % 128 == 0), used in place of w0, w0b, w1 when not NULL
   const uint16_t* w0;
   const uint16_t* w0b;
   int N0;
   const uint16_t* w1;
   int N1;
+  const uint8_t* q0;
+  const uint8_t* q0b;
+  const uint8_t* q1;
   // xproj epilogue
   float* logits;   // fp32 [T x N0]
   uint16_t* z;     // bf16 [T x N1]

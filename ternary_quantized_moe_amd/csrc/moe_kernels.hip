@@ -20,6 +20,7 @@
 #include <algorithm>
 
 #include "device_common.h"
+#include "dense_rows.h"
 #include "moe_internal.h"
 #include "wave_ops.h"
 
@@ -222,7 +223,8 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
 // order and the block stores one fp32 partial; the partials are added in slice
 // order by their consumers, so no block waits for another and the weight bytes
 // spread over the whole chip.
-template <int MT>
+// TQ: some rows come from ternary PQ2_0 containers (a.q0b, a.q1).
+template <int MT, bool TQ>
 __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) {
   __shared__ f32x4 red[3][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -241,13 +243,17 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
   }
   const uint16_t* wrow = nullptr;
   const uint16_t* wrowb = nullptr;
+  const uint8_t* qrow = nullptr;
+  const uint8_t* qrowb = nullptr;
   if (n < a.N0) {
     wrow = a.w0 + (int64_t)n * a.K;
-    if (a.w0b) wrowb = a.w0b + (int64_t)n * a.K;
+    if (TQ && a.q0b) qrowb = a.q0b + n * pq2_row_bytes(a.K);
+    else if (a.w0b) wrowb = a.w0b + (int64_t)n * a.K;
   } else if (n < N) {
-    wrow = a.w1 + (int64_t)(n - a.N0) * a.K;
+    if (TQ && a.q1) qrow = a.q1 + (n - a.N0) * pq2_row_bytes(a.K);
+    else wrow = a.w1 + (int64_t)(n - a.N0) * a.K;
   }
-  const bool summed = wrowb != nullptr;
+  const bool summed = wrowb != nullptr || qrowb != nullptr;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -260,7 +266,11 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
       const int kb = 32 * (s0 + j) + 8 * q;
       const bool kin = s0 + j < s_end && kb < a.K;
       wv[j] = (wrow && kin) ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
-      wb[j] = (summed && kin) ? *(const u32x4_a4*)(wrowb + kb) : u32x4{0u, 0u, 0u, 0u};
+      wb[j] = (wrowb && kin) ? *(const u32x4_a4*)(wrowb + kb) : u32x4{0u, 0u, 0u, 0u};
+      if (TQ) {
+        if (qrow && kin) wv[j] = pq2_row_f16x8(qrow, kb);
+        if (qrowb && kin) wb[j] = pq2_row_f16x8(qrowb, kb);
+      }
 #pragma unroll
       for (int m = 0; m < MT; ++m)
         av[j][m] = (arow[m] && kin) ? *(const u32x4*)(arow[m] + kb) : u32x4{0u, 0u, 0u, 0u};
@@ -303,7 +313,8 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
 // partial sums meet in shared memory and are added in slice order; then each
 // of 32 RTB threads adds one token's slots to 8 consecutive rows with 16-byte
 // reads, in slot order.
-template <int RTB>
+// TQ: B comes from a ternary PQ2_0 container (a.q0).
+template <int RTB, bool TQ>
 __global__ __launch_bounds__(256 * RTB) void combine_small_kernel(DenseArgs a) {
   constexpr int R = 16 * RTB;  // model rows per block
   __shared__ float part[4][16][R + 4];
@@ -314,7 +325,8 @@ __global__ __launch_bounds__(256 * RTB) void combine_small_kernel(DenseArgs a) {
   const int n = blockIdx.x * R + rt * 16 + i16;  // d is a multiple of 128
   const int64_t t0 = (int64_t)blockIdx.y * 16;
   const uint16_t* zrow = a.act + std::min<int64_t>(t0 + i16, a.T - 1) * a.lda;
-  const uint16_t* wrow = a.w0 ? a.w0 + (int64_t)n * K : nullptr;
+  const uint16_t* wrow = !(TQ && a.q0) && a.w0 ? a.w0 + (int64_t)n * K : nullptr;
+  const uint8_t* qrow = TQ && a.q0 ? a.q0 + n * pq2_row_bytes(K) : nullptr;
   const int nsteps = (K + 31) / 32, spw = (nsteps + 3) / 4;
   const int s_begin = ks * spw, s_end = min(nsteps, s_begin + spw);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -324,8 +336,11 @@ __global__ __launch_bounds__(256 * RTB) void combine_small_kernel(DenseArgs a) {
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
       const int kb = 32 * (s0 + j) + 8 * q;
-      const bool kin = wrow && s0 + j < s_end && kb < K;
-      wv[j] = kin ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      const bool kin = (wrow || qrow) && s0 + j < s_end && kb < K;
+      if (TQ && qrow)
+        wv[j] = kin ? pq2_row_f16x8(qrow, kb) : u32x4{0u, 0u, 0u, 0u};
+      else
+        wv[j] = kin ? *(const u32x4_a4*)(wrow + kb) : u32x4{0u, 0u, 0u, 0u};
       zv[j] = kin ? *(const u32x4*)(zrow + kb) : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -409,12 +424,20 @@ hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
     const XprojSplit sp = xproj_split(a.K);
     const dim3 grid((unsigned)((N + 15) / 16), (unsigned)sp.splits, (unsigned)((a.T + 63) / 64));
     const int mt = (int)std::min<int64_t>(4, (a.T + 15) / 16);
-    if (mt == 1) xproj_split_kernel<1><<<grid, 256, 0, stream>>>(a, sp.kpw);
-    else if (mt == 2) xproj_split_kernel<2><<<grid, 256, 0, stream>>>(a, sp.kpw);
-    else if (mt == 3) xproj_split_kernel<3><<<grid, 256, 0, stream>>>(a, sp.kpw);
-    else xproj_split_kernel<4><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    if (a.q0b || a.q1) {
+      if (mt == 1) xproj_split_kernel<1, true><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else if (mt == 2) xproj_split_kernel<2, true><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else if (mt == 3) xproj_split_kernel<3, true><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else xproj_split_kernel<4, true><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    } else {
+      if (mt == 1) xproj_split_kernel<1, false><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else if (mt == 2) xproj_split_kernel<2, false><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else if (mt == 3) xproj_split_kernel<3, false><<<grid, 256, 0, stream>>>(a, sp.kpw);
+      else xproj_split_kernel<4, false><<<grid, 256, 0, stream>>>(a, sp.kpw);
+    }
     return hipGetLastError();
   }
+  if (a.q0b || a.q1) return hipErrorInvalidValue;  // ternary rows need the split or the tiled path
   return launch_dense<EPI_XPROJ>(a, N, stream);
 }
 
@@ -423,10 +446,17 @@ hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
   // blocks of 16 rows up to 32 tokens, of 32 rows beyond (measured: fewer
   // weight bytes per CU win until the token tiles multiply the blocks)
   const unsigned tt = (unsigned)((a.T + 15) / 16);
-  if (a.T <= 32)
-    combine_small_kernel<1><<<dim3((unsigned)(a.N0 / 16), tt), 256, 0, stream>>>(a);
-  else
-    combine_small_kernel<2><<<dim3((unsigned)(a.N0 / 32), tt), 512, 0, stream>>>(a);
+  if (a.q0) {
+    if (a.T <= 32)
+      combine_small_kernel<1, true><<<dim3((unsigned)(a.N0 / 16), tt), 256, 0, stream>>>(a);
+    else
+      combine_small_kernel<2, true><<<dim3((unsigned)(a.N0 / 32), tt), 512, 0, stream>>>(a);
+  } else {
+    if (a.T <= 32)
+      combine_small_kernel<1, false><<<dim3((unsigned)(a.N0 / 16), tt), 256, 0, stream>>>(a);
+    else
+      combine_small_kernel<2, false><<<dim3((unsigned)(a.N0 / 32), tt), 512, 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

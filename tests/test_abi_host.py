@@ -156,6 +156,22 @@ def test_forward_validation_happens_before_launch():
     assert L.moe_workspace_bytes(None, 16, 2, 16) == -1
 
 
+
+def test_ternary_forward_validation():
+    """moe_ternary_forward_q checks on the host, before any launch."""
+    L = tq.lib()
+    c, keep = _fake_banks()
+
+    def rc(r=128, A=0x50000, B=0x60000, delta=None, k=2):
+        return L.moe_ternary_forward_q(0x10000, 4, 0x70000, delta, ctypes.byref(c), A, B, r, k, 0x20000, 0x40000,
+                                       1 << 40, None)
+    assert rc(r=16) == -3 and "multiple of 128" in L.moe_last_error().decode()   # B rows of 16
+    assert rc(B=None) == -1                                                        # A without B
+    assert rc(r=0) == -1                                                           # rank 0 with A, B
+    assert rc(A=0x50001) == -1 and "2-byte" in L.moe_last_error().decode()
+    assert rc(delta=0x30001, A=None, B=None, r=0) == -1
+    assert rc(k=9) == -3
+
 def test_route_validation():
     L = tq.lib()
     assert L.moe_route(0x1000, 4, 100, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
