@@ -40,6 +40,10 @@ WORKLOADS = {
     "flashnext-b1": ("flashnext", 1, "decode"), "flashnext-b8": ("flashnext", 8, "decode"),
     "flashnext-b64": ("flashnext", 64, "decode"), "flashnext-p4096": ("flashnext", 4096, "prefill"),
     "skewed-p16384": ("skewed", 16384, "prefill"),
+    # the router delta and the correction as ternary PQ2_0 containers
+    "olmoe-b1-q": ("olmoe", 1, "decode", "q"), "a3b35-b1-q": ("a3b35", 1, "decode", "q"),
+    "flashnext-b1-q": ("flashnext", 1, "decode", "q"), "flashnext-b64-q": ("flashnext", 64, "decode", "q"),
+    "a3b35-p4096-q": ("a3b35", 4096, "prefill", "q"),
 }
 DEFAULT_WORKLOAD = "olmoe-b64"
 # the ternary quantizer (bfloat16 weights -> containers) on every expert bank of a
@@ -99,6 +103,16 @@ def load_traffic(workload: str, sources=EXPERT_SOURCES):
     return rec.get("traffic_bytes_per_launch")
 
 
+def f16_expansion(trits, scale_bits):
+    """fp16 bits of s * t for trits [rows, cols] and scale bits [rows, cols/128]:
+    the scale with its sign flipped for t = -1, +0 for t = 0."""
+    import numpy as np
+    rows, cols = trits.shape
+    s = np.repeat(scale_bits.astype(np.uint32), 128, axis=1).reshape(rows, cols)
+    bits = np.where(trits < 0, s ^ 0x8000, s)
+    return np.where(trits == 0, 0, bits).astype(np.uint16)
+
+
 class Bench:
     def __init__(self, workload: str):
         import numpy as np
@@ -109,7 +123,8 @@ class Bench:
 
         self.np, self.torch, self.tq = np, torch, tq
         self.workload = workload
-        cname, self.T, self.mode = WORKLOADS[workload]
+        cname, self.T, self.mode = WORKLOADS[workload][:3]
+        self.ternary_corr = len(WORKLOADS[workload]) > 3
         self.cfg = c = CONFIGS[cname]
         self.gen = g = LayerGen(c)
         self.formats = g.formats()
@@ -126,10 +141,20 @@ class Bench:
         self.gu_bytes = np.where(self.formats == 142, 34, 28).astype(np.int64) * 2 * c.d_ff * c.d_model // 128
         self.dn_bytes = self.gu_bytes // 2
         t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
-        self.router_bits, self.delta_bits = g.router_bits(), g.delta_bits()
-        self.a_bits, self.b_bits = g.corr_a_bits(), g.corr_b_bits()
-        self.router, self.delta = t(self.router_bits), t(self.delta_bits)
-        self.corr_a, self.corr_b = t(self.a_bits), t(self.b_bits)
+        self.router_bits = g.router_bits()
+        self.router = t(self.router_bits)
+        if self.ternary_corr:
+            # PQ2_0 containers packed by the library; the oracle and the CPU
+            # baseline get their exact fp16 expansions s * t
+            parts = [g.delta_q_parts(), g.corr_a_q_parts(), g.corr_b_q_parts()]
+            self.delta, self.corr_a, self.corr_b = [
+                torch.from_numpy(tq.pack(142, tr.reshape(-1), sb.reshape(-1))).to(dev) for tr, sb in parts]
+            self.delta_bits, self.a_bits, self.b_bits = [f16_expansion(tr, sb) for tr, sb in parts]
+        else:
+            self.delta_bits = g.delta_bits()
+            self.a_bits, self.b_bits = g.corr_a_bits(), g.corr_b_bits()
+            self.delta = t(self.delta_bits)
+            self.corr_a, self.corr_b = t(self.a_bits), t(self.b_bits)
         self.P = 16 if self.mode == "decode" else 2
         self.x_bits = [g.tokens(self.T, p) for p in range(self.P)]
         self.x = [t(xb) for xb in self.x_bits]
@@ -138,7 +163,7 @@ class Bench:
         # realised routing of every activation set (untimed): touched banks, slots
         self.touched, self.idx = [], []
         for p in range(self.P):
-            r = tq.route(self.x[p], self.router, self.delta, c.n_experts, c.top_k)
+            r = tq.route(self.x[p], self.router, t(self.delta_bits), c.n_experts, c.top_k)
             counts = r["counts"].cpu().numpy()
             touched = np.nonzero(counts)[0]
             self.touched.append(np.concatenate([touched, np.arange(c.n_experts, c.n_banks)]))
@@ -151,8 +176,12 @@ class Bench:
 
     def step(self, i: int):
         c = self.cfg
-        self.tq.forward(self.x[i % self.P], self.router, self.delta, self.banks[i % self.R], self.corr_a,
-                        self.corr_b, c.top_k, y=self.y, workspace=self.ws)
+        if self.ternary_corr:
+            self.tq.forward_q(self.x[i % self.P], self.router, self.delta, self.banks[i % self.R], self.corr_a,
+                              self.corr_b, c.rank, c.top_k, y=self.y, workspace=self.ws)
+        else:
+            self.tq.forward(self.x[i % self.P], self.router, self.delta, self.banks[i % self.R], self.corr_a,
+                            self.corr_b, c.top_k, y=self.y, workspace=self.ws)
 
     # ---- parity before timing ----------------------------------------------------
     def parity(self, n_tokens: int = 4) -> float:
@@ -179,7 +208,8 @@ class Bench:
         touched = self.touched[p]
         n_pos = T * k + S * T
         expert_bytes = int((self.gu_bytes[touched] + self.dn_bytes[touched]).sum())
-        block_bytes = expert_bytes + 4 * E * d + 4 * r * d + 4 * T * d
+        dense_bytes = 34 / 128 if self.ternary_corr else 2       # per weight of the delta, A and B
+        block_bytes = int(expert_bytes + 2 * E * d + dense_bytes * (E * d + 2 * r * d) + 4 * T * d)
         gu_bytes = int(self.gu_bytes[touched].sum()) + 2 * T * d + 2 * n_pos * f
         block_flops = 2 * (n_pos * 3 * d * f + T * E * d + 2 * T * r * d)
         gu_flops = 2 * n_pos * 2 * f * d
@@ -312,7 +342,9 @@ def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{DESCR[c.name]}, {b.mode} {b.T} tokens", "name": workload,
+        "config": {"workload": f"{DESCR[c.name]}, {b.mode} {b.T} tokens"
+                               + (", router delta and correction as ternary PQ2_0 containers" if b.ternary_corr else ""),
+                   "name": workload,
                    "tokens": b.T, "mode": b.mode, "bank_replicas": b.R, "activation_sets": b.P,
                    "parallelism": "single-gpu"},
         "roofline": roof,
