@@ -21,7 +21,9 @@ routing and its own expert evaluation, written from the release pages:
   * the ternary quantizers (absmean, Lloyd over groups of 128): project README,
     "What the experiments established" (quant.py);
   * the Q4_0 per-row n-gram table decode: FlashNext card, "Model Overview" and
-    "Weight Representation" (ple.py).
+    "Weight Representation" (ple.py);
+  * the k=1 draft head (fc1, gelu, fc2): 35B-A3B card, "Shipped Components"
+    (mtp.py).
 
 Where the pages are silent the readings are those listed in the package's design
 notes (two's-complement 2-bit codes, little-endian base-3 digits, SwiGLU,
@@ -29,4 +31,4 @@ softmax over the selected k, ties to the lower expert index, correction input =
 block input).  Everything is evaluated in float64 from the exact bits the GPU
 receives.
 """
-from . import codec, moe, ple, quant  # noqa: F401
+from . import codec, moe, mtp, ple, quant  # noqa: F401
