@@ -158,6 +158,25 @@ int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, in
 int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_len, const int64_t* d_idx,
                             int64_t n_idx, float* d_out, void* stream);
 
+/* Device: the k=1 draft head that ships beside the 35B-A3B release, an fp16
+ * fc1 / gelu / fc2 head over the model's own hidden state and the next token's
+ * embedding (Scion-35B-A3B card, "Shipped Components" and "Highlights"):
+ *   x = [hidden ; emb]  (hidden first, 2h values)
+ *   y = W2 gelu(W1 x + b1) + b2,   gelu(v) = v (1 + erf(v / sqrt 2)) / 2
+ *   hidden, emb  device bf16 [n_tokens x h] (bit patterns), row-major
+ *   w1           device fp16 [m x 2h], b1 fp16 [m] or NULL (no bias)
+ *   w2           device fp16 [h x m],  b2 fp16 [h] or NULL
+ *   y            device bf16 [n_tokens x h]
+ *   workspace    device, >= moe_draft_head_workspace_bytes(...), 256-byte aligned
+ * h and m are multiples of 128 (h = 2048, m = 4096 is the card's 50 MB).
+ * Products accumulate in fp32 on matrix cores (fp16 weights as exact bf16
+ * pairs); gelu(W1 x + b1) and y are rounded to bf16.  n_tokens = 0 is a no-op.
+ * Errors: MOE_E_SHAPE, MOE_E_ARG (NULL, misaligned), MOE_E_SPACE, MOE_E_DEVICE. */
+int64_t moe_draft_head_workspace_bytes(int64_t n_tokens, int32_t hidden, int32_t inner);
+int32_t moe_draft_head(const uint16_t* hidden, const uint16_t* emb, int64_t n_tokens, int32_t h, int32_t m,
+                       const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2,
+                       uint16_t* y, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Host: reorder the blocks of a [rows x cols] container (rows % 16 == 0,
  * cols % 128 == 0) between the row-major order moe_pack writes and the
  * tile-major order the expert kernels read.  With G = cols / 128, block
@@ -262,8 +281,10 @@ int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t 
  * on the call's stream (a NULL entry skips that record); NULL events (or
  * n_events = 0) turn recording off.  Stages:
  * 0 router/correction projection, 1 routing (top-k, ranking, scan, scatter),
- * 2 gate/up experts, 3 down experts, 4 combine.  The library keeps the pointer
- * until it is replaced; the caller keeps the events alive meanwhile. */
+ * 2 gate/up experts, 3 down experts, 4 combine.  moe_draft_head records
+ * events[0], [1] around its fc1 product and [2], [3] around its fc2 product.
+ * The library keeps the pointer until it is replaced; the caller keeps the
+ * events alive meanwhile. */
 enum { MOE_N_STAGES = 5 };
 int32_t moe_set_stage_events(void** events, int32_t n_events);
 

@@ -25,7 +25,8 @@ _ERRORS = {
 
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
-    "moe_quantize_device", "moe_ple_gather_q4_0", "moe_ternary_forward_q",
+    "moe_quantize_device", "moe_ple_gather_q4_0", "moe_ternary_forward_q", "moe_draft_head_workspace_bytes",
+    "moe_draft_head",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -71,6 +72,8 @@ def lib():
             "moe_ple_gather_q4_0": (i32, [vp, i64, i32, vp, i64, vp, vp]),
             "moe_ternary_forward_q": (i32, [vp, i64, vp, vp, ctypes.POINTER(ExpertBanksC), vp, vp, i32,
                                             i32, vp, vp, i64, vp]),
+            "moe_draft_head_workspace_bytes": (i64, [i64, i32, i32]),
+            "moe_draft_head": (i32, [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -299,6 +302,25 @@ def forward_q(x, router, router_delta_q, banks: ExpertBanks, corr_a_q, corr_b_q,
     _check(lib().moe_ternary_forward_q(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta_q), banks.c,
                                        _dev_ptr(corr_a_q), _dev_ptr(corr_b_q), r, top_k, _dev_ptr(y), wp, wn,
                                        _stream(stream)))
+    return y
+
+
+def draft_head(hidden, emb, w1, b1, w2, b2, y=None, workspace=None, stream=None):
+    """The k=1 draft head: bf16 hidden and emb [T, h] (bf16 or int16 bits),
+    fp16 w1 [m, 2h], w2 [h, m], optional fp16 biases -> y [T, h]."""
+    T, h = hidden.shape
+    m = w1.shape[0]
+    if y is None:
+        import torch
+        y = torch.empty_like(hidden)
+    need = lib().moe_draft_head_workspace_bytes(T, h, m)
+    if need < 0:
+        raise MoeError(-3, f"invalid draft head shape T={T} h={h} m={m}")
+    if workspace is None:
+        workspace = alloc_workspace(need, hidden.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_draft_head(_dev_ptr(hidden), _dev_ptr(emb), T, h, m, _dev_ptr(w1), _dev_ptr(b1), _dev_ptr(w2),
+                                _dev_ptr(b2), _dev_ptr(y), wp, wn, _stream(stream)))
     return y
 
 

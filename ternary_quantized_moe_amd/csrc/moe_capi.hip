@@ -366,6 +366,32 @@ int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_
   return ok();
 }
 
+int64_t moe_draft_head_workspace_bytes(int64_t n_tokens, int32_t hidden, int32_t inner) {
+  if (n_tokens < 0 || hidden <= 0 || inner <= 0) return -1;
+  return moe::head_plan(n_tokens, hidden, inner).total;
+}
+
+int32_t moe_draft_head(const uint16_t* hidden, const uint16_t* emb, int64_t T, int32_t h, int32_t m,
+                       const uint16_t* w1, const uint16_t* b1, const uint16_t* w2, const uint16_t* b2, uint16_t* y,
+                       void* ws, int64_t ws_bytes, void* stream) {
+  if (T < 0) return fail(MOE_E_SHAPE, "negative token count %lld", (long long)T);
+  if (h <= 0 || m <= 0 || h % 128 || m % 128)
+    return fail(MOE_E_SHAPE, "hidden %d and inner %d must be positive multiples of 128", (int)h, (int)m);
+  if (T == 0) return ok();
+  if (!hidden || !emb || !w1 || !w2 || !y || !ws) return fail(MOE_E_ARG, "NULL pointer");
+  if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
+  if ((uintptr_t)w1 % 4 || (uintptr_t)w2 % 4 || (uintptr_t)hidden % 2 || (uintptr_t)emb % 2 || (uintptr_t)y % 2 ||
+      (uintptr_t)b1 % 2 || (uintptr_t)b2 % 2)
+    return fail(MOE_E_ARG, "weights must be 4-byte and vectors 2-byte aligned");
+  const int64_t need = moe::head_plan(T, h, m).total;
+  if (ws_bytes < need)
+    return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  moe::HeadArgs a{hidden, emb, T, h, m, w1, b1, w2, b2, y};
+  hipError_t e = moe::launch_head(a, (char*)ws, (hipStream_t)stream, g_stage_events);
+  if (e != hipSuccess) return device_fail(e, "moe_draft_head launch");
+  return ok();
+}
+
 int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k) {
   if (n_tokens < 0 || n_experts < 1 || top_k < 1) return -1;
   return make_plan(n_tokens, d_model, n_experts, 0, 128, top_k, 0).route_end;

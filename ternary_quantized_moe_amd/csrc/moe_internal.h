@@ -131,6 +131,27 @@ hipError_t launch_unpack_device(int fmt, const uint8_t* src, int64_t n_weights, 
 // values (row_len % 32 == 0; table 2-byte, out 16-byte aligned) -> fp32 rows.
 hipError_t launch_ple_gather(const uint8_t* table, int64_t n_rows, int row_len, const int64_t* idx, int64_t n_idx,
                              float* out, hipStream_t stream);
+// The k=1 draft head: y = W2 gelu(W1 [hidden ; emb] + b1) + b2 (bf16 in and out,
+// fp16 weights W1 [m x 2h], W2 [h x m], biases optional).
+struct HeadArgs {
+  const uint16_t* hidden;
+  const uint16_t* emb;
+  int64_t T;
+  int h, m;
+  const uint16_t* w1;
+  const uint16_t* b1;
+  const uint16_t* w2;
+  const uint16_t* b2;
+  uint16_t* y;
+};
+// Workspace regions of the draft head (byte offsets, 256-byte aligned).
+struct HeadPlan {
+  int64_t xc, g, part, wsplit, total;
+  bool large;
+};
+HeadPlan head_plan(int64_t T, int h, int m);
+// stage_events: NULL or the caller's events; [0..1] bracket fc1's product, [2..3] fc2's.
+hipError_t launch_head(const HeadArgs& a, char* ws, hipStream_t stream, void** stage_events);
 // Compute units of the current device (256 if the query fails).
 int cu_count();
 // Quantizer: groups of 128 bfloat16 weights (w 16-byte aligned, dst 4-byte

@@ -172,6 +172,26 @@ def test_ternary_forward_validation():
     assert rc(delta=0x30001, A=None, B=None, r=0) == -1
     assert rc(k=9) == -3
 
+
+def test_draft_head_validation():
+    """moe_draft_head checks on the host, before any launch."""
+    L = tq.lib()
+    args = dict(hid=0x10000, emb=0x20000, T=4, h=256, m=512, w1=0x30000, b1=None, w2=0x40000, b2=None, y=0x50000,
+                ws=0x60000, ws_bytes=1 << 40)
+
+    def rc(**kw):
+        a = dict(args, **kw)
+        return L.moe_draft_head(a["hid"], a["emb"], a["T"], a["h"], a["m"], a["w1"], a["b1"], a["w2"], a["b2"], a["y"],
+                                a["ws"], a["ws_bytes"], None)
+    assert rc(h=200) == -3 and rc(m=100) == -3 and rc(T=-1) == -3
+    assert rc(w2=None) == -1 and rc(emb=None) == -1
+    assert rc(ws=0x60010) == -1                        # workspace not 256-byte aligned
+    assert rc(w1=0x30002) == -1                        # weights not 4-byte aligned
+    assert rc(ws_bytes=1024) == -6
+    assert rc(T=0) == 0
+    assert L.moe_draft_head_workspace_bytes(4, 256, 512) > 0
+    assert L.moe_draft_head_workspace_bytes(-1, 256, 512) == -1
+
 def test_route_validation():
     L = tq.lib()
     assert L.moe_route(0x1000, 4, 100, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
