@@ -57,6 +57,9 @@ QUANT_WORKLOADS = {
 PLE_WORKLOADS = {"ple-b64": (64, 48), "ple-p4096": (4096, 48)}
 PLE_ROWS, PLE_ROW_LEN = 320_001_536, 160
 PLE_METRIC = "Q4_0 n-gram table rows gathered and decoded per second"
+# the k=1 draft head: name -> (tokens, hidden h, inner m); 2048 x 4096 is the card's 50 MB
+MTP_WORKLOADS = {"mtp-b1": (1, 2048, 4096), "mtp-b64": (64, 2048, 4096)}
+MTP_METRIC = "k=1 draft head evaluations (tokens) per second"
 QUANT_METRIC = "ternary quantizer weights/s (bf16 -> PQ2_0 / PTQ1_0, absmean or Lloyd g128)"
 # VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -76,6 +79,7 @@ DESCR = {
 EXPERT_SOURCES = ("device_common.h", "moe_experts.hip", "moe_internal.h")
 QUANT_SOURCES = ("device_common.h", "moe_quant.hip", "wave_ops.h")
 PLE_SOURCES = ("device_common.h", "moe_ple.hip")
+MTP_SOURCES = ("device_common.h", "moe_kernels.hip", "moe_internal.h", "moe_mtp.hip")
 
 
 def kernel_source_hash(names=EXPERT_SOURCES) -> str:
@@ -557,6 +561,116 @@ def run_ple(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     return rec
 
 
+# --------------------------------------------------------------------------- draft head
+def mtp_cpu_baseline(hid, emb, w, got_bits):
+    """The oracle head, as it stands, on every token of the batch; its rows are
+    compared with the device's."""
+    import numpy as np
+    from oracle import moe as omoe, mtp
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    reps, dt = 0, 0.0
+    while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
+        t0 = time.perf_counter()
+        ref = mtp.head(hid, emb, *w)
+        dt += time.perf_counter() - t0
+        reps += 1
+    got = omoe.bf16_to_f64(got_bits)
+    err = float((np.abs(got - ref).max(axis=1) / np.linalg.norm(ref, axis=1)).max())
+    T = hid.shape[0]
+    return ({"value": reps * T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+             "sample": f"all {T} tokens, {reps} pass(es), {dt:.1f} s"}, err)
+
+
+def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
+    import numpy as np
+    import torch
+    import ternary_quantized_moe_amd as tq
+    from synthetic.mtp import head_inputs, head_weights
+
+    T, h, m = MTP_WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    t0 = time.time()
+    w = head_weights(h, m, 0)
+    # R copies of the weights, so each step reads them from HBM (over the 256 MB Infinity Cache)
+    per_copy = 2 * (m * 2 * h + h * m)
+    R = max(1, math.ceil(1.0e9 / per_copy))
+    copies = [[t(a) for a in w] for _ in range(R)]
+    P = 16
+    inputs = [head_inputs(T, h, p) for p in range(P)]
+    dev_in = [(t(a), t(b)) for a, b in inputs]
+    y = torch.empty((T, h), dtype=torch.int16, device=dev)
+    ws = tq.alloc_workspace(tq.lib().moe_draft_head_workspace_bytes(T, h, m), dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step(i):
+        w1, b1, w2, b2 = copies[i % R]
+        hid, emb = dev_in[i % P]
+        tq.draft_head(hid, emb, w1, b1, w2, b2, y=y, workspace=ws)
+
+    # the warmup touches every replica once: a replica's first use in the timed
+    # region cost ~3 ms (measured: 0.38 ms per step over 100 steps, 0.032 over 1000)
+    for i in range(max(warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    # events bracket fc1's product (the library's stage events 0 and 1) on every step
+    timer = tq.StageTimer(steps, stages=[0])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        with timer.step():
+            step(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    fc1_s = timer.ms()[0] * 1e-3
+    splits = 1 if T > 256 else 8
+    fc1_bytes = 2 * m * 2 * h + 2 * T * 2 * h + 4 * T * m          # weights, input, fp32 product
+    head_bytes = 2 * (m * 2 * h + h * m) + 2 * (m + h) + 2 * T * 2 * h + 2 * T * h
+    ach = fc1_bytes / fc1_s / 1e9
+    ms_step = elapsed * 1e3 / steps
+    rec = {
+        "metric": MTP_METRIC,
+        "value": round(steps * T / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"k=1 draft head fc1 [{m} x {2 * h}] / gelu / fc2 [{h} x {m}] in fp16 "
+                               f"({per_copy / 1e6:.1f} MB of weights), {T} token(s) per evaluation",
+                   "name": workload, "tokens": T, "weight_replicas": R, "input_sets": P,
+                   "parallelism": "single-gpu", "setup_s": round(setup_s, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, MTP_SOURCES),
+                     "kernel": "xproj_split_kernel (fc1)" if T <= 256 else "dense_gemm_kernel (fc1)",
+                     "alg_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_s * 1e6, 2),
+                     "k_slices": splits},
+        "head": {"alg_bytes": int(head_bytes),
+                 "achieved_GBs": round(head_bytes / (ms_step * 1e-3) / 1e9, 1),
+                 "hbm_frac": round(head_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if with_cpu:
+        step(0)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().view(np.uint16)
+        print(f"{workload}: timed, {ms_step * 1e3:.1f} us per step; oracle on the host next", file=sys.stderr,
+              flush=True)
+        rec["cpu_baseline"], rec["parity_max_row_err"] = mtp_cpu_baseline(*inputs[0], w, got)
+    del copies, dev_in
+    torch.cuda.empty_cache()
+    return rec
+
+
 def calibrate_copy(mib: int, reps: int = 5):
     """Plain device copies of known size: each reads and writes mib MiB once."""
     import torch
@@ -576,7 +690,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
-                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(PLE_WORKLOADS))
+                    choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(PLE_WORKLOADS)
+                    + sorted(MTP_WORKLOADS))
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -609,6 +724,8 @@ def main():
         rec = run_quant(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     elif args.workload in PLE_WORKLOADS:
         rec = run_ple(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    elif args.workload in MTP_WORKLOADS:
+        rec = run_mtp(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     else:
         rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     print(json.dumps(rec), flush=True)

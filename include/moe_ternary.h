@@ -163,7 +163,7 @@ int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_
  * embedding (Scion-35B-A3B card, "Shipped Components" and "Highlights"):
  *   x = [hidden ; emb]  (hidden first, 2h values)
  *   y = W2 gelu(W1 x + b1) + b2,   gelu(v) = v (1 + erf(v / sqrt 2)) / 2
- *   hidden, emb  device bf16 [n_tokens x h] (bit patterns), row-major
+ *   hidden, emb  device bf16 [n_tokens x h] (bit patterns), row-major, 16-byte aligned
  *   w1           device fp16 [m x 2h], b1 fp16 [m] or NULL (no bias)
  *   w2           device fp16 [h x m],  b2 fp16 [h] or NULL
  *   y            device bf16 [n_tokens x h]

@@ -380,9 +380,9 @@ int32_t moe_draft_head(const uint16_t* hidden, const uint16_t* emb, int64_t T, i
   if (T == 0) return ok();
   if (!hidden || !emb || !w1 || !w2 || !y || !ws) return fail(MOE_E_ARG, "NULL pointer");
   if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
-  if ((uintptr_t)w1 % 4 || (uintptr_t)w2 % 4 || (uintptr_t)hidden % 2 || (uintptr_t)emb % 2 || (uintptr_t)y % 2 ||
-      (uintptr_t)b1 % 2 || (uintptr_t)b2 % 2)
-    return fail(MOE_E_ARG, "weights must be 4-byte and vectors 2-byte aligned");
+  if ((uintptr_t)w1 % 4 || (uintptr_t)w2 % 4 || (uintptr_t)hidden % 16 || (uintptr_t)emb % 16 ||
+      (uintptr_t)y % 2 || (uintptr_t)b1 % 2 || (uintptr_t)b2 % 2)
+    return fail(MOE_E_ARG, "hidden and emb must be 16-byte, weights 4-byte and y, biases 2-byte aligned");
   const int64_t need = moe::head_plan(T, h, m).total;
   if (ws_bytes < need)
     return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);

@@ -10,7 +10,8 @@
 // Both products are the x-projection's dense kernels: up to 256 tokens the
 // split kernel (fp32 partials over at most eight K slices, every weight row
 // streamed once and spread over the chip), beyond that the tiled matrix-core
-// GEMM.  A small kernel then adds the slices in order, the bias and the gelu.
+// GEMM.  A small kernel then adds the slices in order, the bias and the gelu;
+// another one first concatenates the two inputs into the workspace.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -38,6 +39,17 @@ __global__ __launch_bounds__(kFinishThreads) void head_finish_kernel(const float
   if (bias) v += f16_to_f32(bias[n]);
   if (GELU) v = 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
   out[i] = (uint16_t)f32_to_bf16(v);
+}
+
+// x = [hidden ; emb]: 16-byte pieces, T rows of 2h values (h % 8 == 0).
+__global__ __launch_bounds__(kFinishThreads) void head_concat_kernel(const u32x4* __restrict__ hidden,
+                                                                     const u32x4* __restrict__ emb, int64_t T,
+                                                                     int h8, u32x4* __restrict__ xc) {
+  const int64_t i = (int64_t)blockIdx.x * kFinishThreads + threadIdx.x;
+  if (i >= T * 2 * h8) return;
+  const int64_t t = i / (2 * h8);
+  const int c = (int)(i - t * 2 * h8);
+  xc[i] = c < h8 ? hidden[t * h8 + c] : emb[t * h8 + c - h8];
 }
 
 template <bool GELU>
@@ -78,11 +90,10 @@ hipError_t launch_head(const HeadArgs& a, char* ws, hipStream_t stream, void** s
     return stage_events && stage_events[i] ? hipEventRecord((hipEvent_t)stage_events[i], stream) : hipSuccess;
   };
   // x = [hidden ; embedding], rows of 2h
-  hipError_t e = hipMemcpy2DAsync(xc, 4 * (size_t)h, a.hidden, 2 * (size_t)h, 2 * (size_t)h, (size_t)T,
-                                  hipMemcpyDeviceToDevice, stream);
-  if (e == hipSuccess)
-    e = hipMemcpy2DAsync(xc + h, 4 * (size_t)h, a.emb, 2 * (size_t)h, 2 * (size_t)h, (size_t)T,
-                         hipMemcpyDeviceToDevice, stream);
+  const int64_t pieces = T * 2 * (h / 8);
+  head_concat_kernel<<<(unsigned)((pieces + kFinishThreads - 1) / kFinishThreads), kFinishThreads, 0, stream>>>(
+      (const u32x4*)a.hidden, (const u32x4*)a.emb, T, h / 8, (u32x4*)xc);
+  hipError_t e = hipGetLastError();
   for (int layer = 0; layer < 2 && e == hipSuccess; ++layer) {
     DenseArgs d{};
     d.act = layer == 0 ? xc : g;

@@ -187,6 +187,7 @@ def test_draft_head_validation():
     assert rc(w2=None) == -1 and rc(emb=None) == -1
     assert rc(ws=0x60010) == -1                        # workspace not 256-byte aligned
     assert rc(w1=0x30002) == -1                        # weights not 4-byte aligned
+    assert rc(hid=0x10008) == -1                       # inputs not 16-byte aligned
     assert rc(ws_bytes=1024) == -6
     assert rc(T=0) == 0
     assert L.moe_draft_head_workspace_bytes(4, 256, 512) > 0
