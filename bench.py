@@ -613,8 +613,7 @@ def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
         hid, emb = dev_in[i % P]
         tq.draft_head(hid, emb, w1, b1, w2, b2, y=y, workspace=ws)
 
-    # the warmup touches every replica once: a replica's first use in the timed
-    # region cost ~3 ms (measured: 0.38 ms per step over 100 steps, 0.032 over 1000)
+    # the warmup uses every weight copy once before the timed steps
     for i in range(max(warmup, R)):
         step(i)
     torch.cuda.synchronize()
