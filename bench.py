@@ -700,9 +700,9 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: the block's forward pass is data-parallel over tokens with no "
-              f"cross-GPU exchange, and this build runs on a single MI355X (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the block's forward pass is data-parallel over tokens with "
+              f"no cross-GPU exchange, so N GPUs run N independent copies of this single-GPU step "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
