@@ -185,28 +185,37 @@ __device__ __forceinline__ void quantize_groups4(u32x4 v, int64_t g, bool valid,
   }
 }
 
-// One wave per four consecutive groups, one block per 16.  (A grid-stride
-// loop with the next groups loaded ahead measured slower at every grid size
-// tried: 4 to 32 blocks per CU.)
-template <int FMT, int METHOD>
+// A wave takes four consecutive groups U times over, a block 16 U groups; the
+// loads of all U are issued first.  U = 2 for absmean (HBM-bound: 232 us
+// against 250 with U = 1 and 248 with U = 4 on 604 M weights), 1 for Lloyd
+// (VALU-bound).  A grid-stride loop with the next groups loaded ahead measured
+// slower at every grid size tried (4 to 32 blocks per CU).
+template <int FMT, int METHOD, int U>
 __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const u32x4* __restrict__ w, int64_t groups,
                                                                  uint8_t* __restrict__ dst, uint8_t* __restrict__ rounds) {
   const int lane = threadIdx.x & 63, i = lane & 15, row0 = lane & 48;
-  const int64_t g = (int64_t)blockIdx.x * kQuantGroupsPerBlock + (threadIdx.x >> 4);
-  const bool valid = g < groups;
-  u32x4 v = {0u, 0u, 0u, 0u};
-  if (valid) v = w[g * 16 + i];
-  quantize_groups4<FMT, METHOD>(v, g, valid, i, row0, dst, rounds);
+  u32x4 v[U];
+  int64_t g[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    g[u] = ((int64_t)blockIdx.x * U + u) * kQuantGroupsPerBlock + (threadIdx.x >> 4);
+    v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (g[u] < groups) v[u] = w[g[u] * 16 + i];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) quantize_groups4<FMT, METHOD>(v[u], g[u], g[u] < groups, i, row0, dst, rounds);
 }
 
 template <int FMT>
 hipError_t launch_quantize_fmt(int method, const u32x4* w, int64_t groups, uint8_t* dst, uint8_t* rounds,
                                hipStream_t stream) {
-  const int64_t blocks = (groups + kQuantGroupsPerBlock - 1) / kQuantGroupsPerBlock;
+  const int64_t per_block = kQuantGroupsPerBlock;
   if (method == MOE_QUANT_LLOYD)
-    quantize_kernel<FMT, MOE_QUANT_LLOYD><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst, rounds);
+    quantize_kernel<FMT, MOE_QUANT_LLOYD, 1><<<(unsigned)((groups + per_block - 1) / per_block), kQuantThreads, 0,
+                                              stream>>>(w, groups, dst, rounds);
   else
-    quantize_kernel<FMT, MOE_QUANT_ABSMEAN><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(w, groups, dst, rounds);
+    quantize_kernel<FMT, MOE_QUANT_ABSMEAN, 2><<<(unsigned)((groups + 2 * per_block - 1) / (2 * per_block)),
+                                                 kQuantThreads, 0, stream>>>(w, groups, dst, rounds);
   return hipGetLastError();
 }
 
