@@ -49,11 +49,13 @@
  * fp32).  Gate weights use fp32 exp.
  *
  * Ownership and ordering: the caller allocates and frees every buffer.  The
- * library allocates no device memory, keeps no pointer after a call returns and
- * holds no state except a thread-local error message.  Device entry points are
- * ordered on the given stream (a hipStream_t; NULL means the null stream) and
- * return once the work is enqueued: inputs must stay alive and unchanged until
- * the stream reaches the call, and concurrent streams need separate workspaces.
+ * library allocates no device memory and keeps no caller pointer after a call
+ * returns, except the stage events handed to moe_set_stage_events; besides
+ * those it holds only a thread-local error message and the device's compute
+ * unit count, read once.  Device entry points are ordered on the given stream
+ * (a hipStream_t; NULL means the null stream) and return once the work is
+ * enqueued: inputs must stay alive and unchanged until the stream reaches the
+ * call, and concurrent streams need separate workspaces.
  *
  * Errors: every argument, shape and format check happens on the host before the
  * first launch, so a call that returns an error has enqueued nothing.  A failed
