@@ -47,13 +47,15 @@ def run(h, m, T, bias=True, seed=0):
     return err
 
 
-@pytest.mark.parametrize("T", [1, 7, 64, 300])
+@pytest.mark.parametrize("T", [1, 7, 64, 256, 257, 300])
 def test_draft_head_small(T):
+    # 256 is the last batch of the split-K path, 257 the first of the tiled one
     assert run(256, 512, T) <= TOL
 
 
-@pytest.mark.parametrize("T", [1, 64, 300])
+@pytest.mark.parametrize("T", [1, 33, 64, 300])
 def test_draft_head_card_size(T):
+    # from 33 tokens on, the 2048- and 4096-row products take two row tiles per block
     # h = 2048, m = 4096: 25.2 M fp16 weights, the card's 50 MB
     assert run(2048, 4096, T) <= TOL
 
