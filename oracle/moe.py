@@ -179,6 +179,16 @@ def correction(x: np.ndarray, a: Optional[np.ndarray], b: Optional[np.ndarray]) 
     return (x @ a.T) @ b.T
 
 
+def lowrank_apply(x_bits, y_bits, a_bits, b_bits) -> np.ndarray:
+    """y + B (A x) per token, the same rank-r branch applied to another tensor:
+    the releases carry rank-512 branches on the attention output as well as on
+    the MoE block output (Scion-35B-A3B card, "Weight Representation").  x and
+    y are bf16 bits [T, d] (y None for zero), A [r, d] and B [d, r] fp16 bits."""
+    x = bf16_to_f64(x_bits)
+    y = np.zeros_like(x) if y_bits is None else bf16_to_f64(y_bits)
+    return y + correction(x, f16_to_f64(a_bits), f16_to_f64(b_bits))
+
+
 @dataclass
 class Result:
     y: np.ndarray         # [T, d] float64
