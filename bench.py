@@ -60,6 +60,10 @@ PLE_METRIC = "Q4_0 n-gram table rows gathered and decoded per second"
 # the k=1 draft head: name -> (tokens, hidden h, inner m); 2048 x 4096 is the card's 50 MB
 MTP_WORKLOADS = {"mtp-b1": (1, 2048, 4096), "mtp-b64": (64, 2048, 4096)}
 MTP_METRIC = "k=1 draft head evaluations (tokens) per second"
+# the rank-r branch on its own (as on the attention output): name -> (tokens, d, r, ternary A and B)
+LOWRANK_WORKLOADS = {"lowrank-b1": (1, 2048, 512, False), "lowrank-b64": (64, 2048, 512, False),
+                     "lowrank-p4096": (4096, 2048, 512, False), "lowrank-b1-q": (1, 2048, 512, True)}
+LOWRANK_METRIC = "rank-r branch applications y + B(A x) (tokens) per second"
 QUANT_METRIC = "ternary quantizer weights/s (bf16 -> PQ2_0 / PTQ1_0, absmean or Lloyd g128)"
 # VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
@@ -79,7 +83,8 @@ DESCR = {
 EXPERT_SOURCES = ("device_common.h", "moe_experts.hip", "moe_internal.h")
 QUANT_SOURCES = ("device_common.h", "moe_quant.hip", "wave_ops.h")
 PLE_SOURCES = ("device_common.h", "moe_ple.hip")
-MTP_SOURCES = ("device_common.h", "moe_kernels.hip", "moe_internal.h", "moe_mtp.hip")
+MTP_SOURCES = ("device_common.h", "dense_rows.h", "moe_kernels.hip", "moe_internal.h", "moe_mtp.hip")
+LOWRANK_SOURCES = ("device_common.h", "dense_rows.h", "moe_dense.hip", "moe_kernels.hip", "moe_internal.h")
 
 
 def kernel_source_hash(names=EXPERT_SOURCES) -> str:
@@ -670,6 +675,137 @@ def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     return rec
 
 
+# --------------------------------------------------------------------------- low-rank branch
+def lowrank_cpu_baseline(x, yin, a, b, got_bits):
+    """The oracle's y + B (A x), as it stands, on every token of the batch; its
+    rows are compared with the device's."""
+    import numpy as np
+    from oracle import moe as omoe
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    reps, dt = 0, 0.0
+    while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
+        t0 = time.perf_counter()
+        ref = omoe.lowrank_apply(x, yin, a, b)
+        dt += time.perf_counter() - t0
+        reps += 1
+    got = omoe.bf16_to_f64(got_bits)
+    err = float((np.abs(got - ref).max(axis=1) / np.linalg.norm(ref, axis=1)).max())
+    T = x.shape[0]
+    return ({"value": reps * T / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+             "sample": f"all {T} tokens, {reps} pass(es), {dt:.1f} s"}, err)
+
+
+def run_lowrank(workload: str, steps: int, warmup: int, with_cpu: bool = True):
+    import numpy as np
+    import torch
+    import ternary_quantized_moe_amd as tq
+    from synthetic import CONFIGS, LayerGen
+
+    T, d, r, ternary = LOWRANK_WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    t16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    t0 = time.time()
+    g = LayerGen(CONFIGS["a3b35"])        # d = 2048, rank 512
+    assert (g.cfg.d_model, g.cfg.rank) == (d, r)
+    if ternary:
+        (ta, sa), (tb, sb) = g.corr_a_q_parts(), g.corr_b_q_parts()
+        qa, qb = tq.pack(142, ta.reshape(-1), sa.reshape(-1)), tq.pack(142, tb.reshape(-1), sb.reshape(-1))
+        a_bits, b_bits = f16_expansion(ta, sa), f16_expansion(tb, sb)
+        per_copy = qa.nbytes + qb.nbytes
+        mk = lambda: (None, torch.from_numpy(qa).to(dev), None, torch.from_numpy(qb).to(dev))
+    else:
+        a_bits, b_bits = g.corr_a_bits(), g.corr_b_bits()
+        per_copy = 2 * 2 * r * d
+        mk = lambda: (t16(a_bits), None, t16(b_bits), None)
+    # R copies of the weights, so each step reads them from HBM (over the 256 MB Infinity Cache)
+    R = max(1, math.ceil(1.0e9 / per_copy)) if T <= 256 else 1
+    copies = [mk() for _ in range(R)]
+    P = 16 if T <= 256 else 2
+    inputs = [(g.tokens(T, 20 + 2 * p), g.tokens(T, 21 + 2 * p)) for p in range(P)]
+    dev_in = [(t16(x), t16(yi)) for x, yi in inputs]
+    y = torch.empty((T, d), dtype=torch.int16, device=dev)
+    ws = tq.alloc_workspace(tq.lib().moe_lowrank_workspace_bytes(T, d, r), dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step(i):
+        a, aq, b, bq = copies[i % R]
+        x, yi = dev_in[i % P]
+        tq.lowrank_apply(x, yi, a, b, r, a_q=aq, b_q=bq, y=y, workspace=ws)
+
+    for i in range(max(warmup, R)):
+        step(i)
+    torch.cuda.synchronize()
+    # events bracket the product A x (stage 0: up to 256 tokens the K-sliced
+    # kernel alone, its slices are added up after it) and B z + y_in (stage 1)
+    timer = tq.StageTimer(steps, stages=[0, 1])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        with timer.step():
+            step(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    s0, s1 = timer.ms()[0] * 1e-3, timer.ms()[1] * 1e-3
+    wbytes = per_copy // 2
+    # algorithmic bytes of each product: its weights, its input, its output (and
+    # y_in); up to 256 tokens A x leaves fp32 slices, one per K slice
+    b0 = wbytes + 2 * T * d + (4 * 8 * T * r if T <= 256 else 2 * T * r)
+    b1 = wbytes + 2 * T * r + 2 * 2 * T * d
+    flops = 2.0 * T * r * d                 # per product
+    # the roofline is the product A x's (the two products take about the same time)
+    sec = s0
+    kname = "xproj_split_kernel (A x)" if T <= 256 else "split_kernel + dense_gemm_kernel<0> (A x)"
+    ms_step = elapsed * 1e3 / steps
+    if T <= 256:
+        alg = b0
+        roof = {"bound": "hbm", "achieved": round(alg / sec / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(alg / sec / 1e9 / HBM_PEAK_GBS, 4), "alg_bytes_per_launch": int(alg)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / sec / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "alg_flops_per_launch": int(flops)}
+    roof.update({"traffic": load_traffic(workload, LOWRANK_SOURCES), "kernel": kname,
+                 "avg_launch_us": round(sec * 1e6, 2)})
+    rec = {
+        "metric": LOWRANK_METRIC,
+        "value": round(steps * T / elapsed, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"rank-{r} branch y + B(A x) on d={d}, A [{r} x {d}] and B [{d} x {r}] "
+                               f"{'as PQ2_0 containers' if ternary else 'in fp16'} "
+                               f"({per_copy / 1e6:.2f} MB of weights), {T} token(s) per call",
+                   "name": workload, "tokens": T, "weight_replicas": R, "input_sets": P,
+                   "parallelism": "single-gpu", "setup_s": round(setup_s, 1)},
+        "roofline": roof,
+        "stages_us": {"A x": round(s0 * 1e6, 2), "B z + y_in": round(s1 * 1e6, 2)},
+        "B_product": {"alg_bytes": int(b1), "achieved_GBs": round(b1 / s1 / 1e9, 1),
+                      "hbm_frac": round(b1 / s1 / 1e9 / HBM_PEAK_GBS, 4)},
+    }
+    if with_cpu:
+        step(0)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().view(np.uint16)
+        print(f"{workload}: timed, {ms_step * 1e3:.1f} us per step; oracle on the host next", file=sys.stderr,
+              flush=True)
+        rec["cpu_baseline"], rec["parity_max_row_err"] = lowrank_cpu_baseline(*inputs[0], a_bits, b_bits, got)
+    del copies, dev_in
+    torch.cuda.empty_cache()
+    return rec
+
+
 def calibrate_copy(mib: int, reps: int = 5):
     """Plain device copies of known size: each reads and writes mib MiB once."""
     import torch
@@ -690,7 +826,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     choices=sorted(WORKLOADS) + sorted(QUANT_WORKLOADS) + sorted(PLE_WORKLOADS)
-                    + sorted(MTP_WORKLOADS))
+                    + sorted(MTP_WORKLOADS) + sorted(LOWRANK_WORKLOADS))
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
@@ -725,6 +861,8 @@ def main():
         rec = run_ple(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     elif args.workload in MTP_WORKLOADS:
         rec = run_mtp(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+    elif args.workload in LOWRANK_WORKLOADS:
+        rec = run_lowrank(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     else:
         rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     print(json.dumps(rec), flush=True)

@@ -160,6 +160,27 @@ int32_t moe_quantize_device(int32_t fmt, int32_t method, const uint16_t* d_w, in
 int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_len, const int64_t* d_idx,
                             int64_t n_idx, float* d_out, void* stream);
 
+/* Device: the rank-r branch on its own, y = y_in + B (A x), for the other
+ * tensor the releases correct the same way: rank-512 branches sit on the
+ * attention output as well as on the MoE block output (Scion-35B-A3B card,
+ * "Weight Representation"; project README, "The idea").
+ *   x           device bf16 [n_tokens x d] (the branch input), 16-byte aligned
+ *   y_in        device bf16 [n_tokens x d], or NULL for zero; y may equal y_in
+ *               (an in-place update of the residual stream)
+ *   A / A_q     fp16 [r x d] or a ternary PQ2_0 container of it (row-major
+ *               groups); exactly one of the two
+ *   B / B_q     fp16 [d x r] or PQ2_0 (then r % 128 == 0); exactly one
+ *   y           device bf16 [n_tokens x d], 16-byte aligned, not x
+ *   workspace   >= moe_lowrank_workspace_bytes(n_tokens, d, r), 256-byte aligned
+ * The numerics are the block's correction: fp32 products on matrix cores, z =
+ * A x rounded to bf16, y summed in fp32 as (B z) + y_in and rounded to bf16.
+ * d % 128 == 0, r % 8 == 0, r <= 4096.  Errors: MOE_E_SHAPE, MOE_E_ARG,
+ * MOE_E_SPACE, MOE_E_DEVICE. */
+int64_t moe_lowrank_workspace_bytes(int64_t n_tokens, int32_t d, int32_t r);
+int32_t moe_lowrank_apply(const uint16_t* x, const uint16_t* y_in, int64_t n_tokens, int32_t d,
+                          const uint16_t* A, const uint8_t* A_q, const uint16_t* B, const uint8_t* B_q,
+                          int32_t r, uint16_t* y, void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Device: the k=1 draft head that ships beside the 35B-A3B release, an fp16
  * fc1 / gelu / fc2 head over the model's own hidden state and the next token's
  * embedding (Scion-35B-A3B card, "Shipped Components" and "Highlights"):
@@ -284,7 +305,9 @@ int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t 
  * n_events = 0) turn recording off.  Stages:
  * 0 router/correction projection, 1 routing (top-k, ranking, scan, scatter),
  * 2 gate/up experts, 3 down experts, 4 combine.  moe_draft_head records
- * events[0], [1] around its fc1 product and [2], [3] around its fc2 product.
+ * events[0], [1] around its fc1 product and [2], [3] around its fc2 product;
+ * moe_lowrank_apply [0], [1] around the product A x (up to 256 tokens its fp32
+ * slices, added up after events[1]) and [2], [3] around B z + y_in.
  * The library keeps the pointer until it is replaced; the caller keeps the
  * events alive meanwhile. */
 enum { MOE_N_STAGES = 5 };

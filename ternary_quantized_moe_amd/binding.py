@@ -26,7 +26,7 @@ _ERRORS = {
 EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
     "moe_quantize_device", "moe_ple_gather_q4_0", "moe_ternary_forward_q", "moe_draft_head_workspace_bytes",
-    "moe_draft_head",
+    "moe_draft_head", "moe_lowrank_workspace_bytes", "moe_lowrank_apply",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -74,6 +74,8 @@ def lib():
                                             i32, vp, vp, i64, vp]),
             "moe_draft_head_workspace_bytes": (i64, [i64, i32, i32]),
             "moe_draft_head": (i32, [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_lowrank_workspace_bytes": (i64, [i64, i32, i32]),
+            "moe_lowrank_apply": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp, i64, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -321,6 +323,24 @@ def draft_head(hidden, emb, w1, b1, w2, b2, y=None, workspace=None, stream=None)
     wp, wn = _aligned(workspace)
     _check(lib().moe_draft_head(_dev_ptr(hidden), _dev_ptr(emb), T, h, m, _dev_ptr(w1), _dev_ptr(b1), _dev_ptr(w2),
                                 _dev_ptr(b2), _dev_ptr(y), wp, wn, _stream(stream)))
+    return y
+
+
+def lowrank_apply(x, y_in, a, b, rank: int, a_q=None, b_q=None, y=None, workspace=None, stream=None):
+    """y = y_in + B (A x): x, y_in bf16 [T, d] (y_in may be None, y may be y_in);
+    A fp16 [r, d] or a_q its PQ2_0 container, B fp16 [d, r] or b_q."""
+    import torch
+    T, d = x.shape
+    if y is None:
+        y = torch.empty_like(x)
+    need = lib().moe_lowrank_workspace_bytes(T, d, rank)
+    if need < 0:
+        raise MoeError(-3, f"invalid low-rank shape T={T} d={d} r={rank}")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_lowrank_apply(_dev_ptr(x), _dev_ptr(y_in), T, d, _dev_ptr(a), _dev_ptr(a_q), _dev_ptr(b),
+                                   _dev_ptr(b_q), rank, _dev_ptr(y), wp, wn, _stream(stream)))
     return y
 
 

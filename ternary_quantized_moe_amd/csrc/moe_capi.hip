@@ -366,6 +366,94 @@ int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_
   return ok();
 }
 
+// ------------------------------------------------------------ low-rank branch
+struct LowrankPlan {
+  int64_t z, part, wsplit, total;
+  bool large;
+};
+
+static LowrankPlan lowrank_plan(int64_t T, int d, int r) {
+  LowrankPlan p{};
+  p.large = T > moe::kGroupMaxT;
+  int64_t o = 0;
+  p.z = o; o += up(T * (int64_t)r * 2);
+  p.part = o;
+  if (!p.large) o += up((int64_t)moe::xproj_split(d).splits * T * r * 4);
+  p.wsplit = o;
+  if (p.large) o += up(std::max(moe::dense_split_bytes(r, d), moe::dense_split_bytes(d, r)));
+  p.total = o;
+  return p;
+}
+
+int64_t moe_lowrank_workspace_bytes(int64_t n_tokens, int32_t d, int32_t r) {
+  if (n_tokens < 0 || d <= 0 || r <= 0) return -1;
+  return lowrank_plan(n_tokens, d, r).total;
+}
+
+int32_t moe_lowrank_apply(const uint16_t* x, const uint16_t* y_in, int64_t T, int32_t d, const uint16_t* A,
+                          const uint8_t* A_q, const uint16_t* B, const uint8_t* B_q, int32_t r, uint16_t* y,
+                          void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    if (T < 0) return fail(MOE_E_SHAPE, "negative token count %lld", (long long)T);
+    if (d <= 0 || d % 128) return fail(MOE_E_SHAPE, "d_model %d is not a positive multiple of 128", (int)d);
+    if (r <= 0 || r % 8 || r > 4096)
+      return fail(MOE_E_SHAPE, "rank %d must be a positive multiple of 8, at most 4096", (int)r);
+    if (B_q && r % 128) return fail(MOE_E_SHAPE, "a ternary B needs a rank that is a multiple of 128 (got %d)", (int)r);
+    if ((A == nullptr) == (A_q == nullptr) || (B == nullptr) == (B_q == nullptr))
+      return fail(MOE_E_ARG, "give exactly one of A, A_q and one of B, B_q");
+    if (T == 0) return ok();
+    if (!x || !y || !ws) return fail(MOE_E_ARG, "NULL pointer");
+    if (x == y) return fail(MOE_E_ARG, "y must not alias x");
+    if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
+    if ((uintptr_t)x % 16 || (uintptr_t)y % 16 || (uintptr_t)y_in % 16)
+      return fail(MOE_E_ARG, "x, y and y_in must be 16-byte aligned");
+    if ((uintptr_t)A % 4 || (uintptr_t)B % 4 || (uintptr_t)A_q % 2 || (uintptr_t)B_q % 2)
+      return fail(MOE_E_ARG, "A, B must be 4-byte and ternary containers 2-byte aligned");
+    const LowrankPlan p = lowrank_plan(T, d, r);
+    if (ws_bytes < p.total)
+      return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
+    const hipStream_t st = (hipStream_t)stream;
+    uint16_t* z = at<uint16_t>(ws, p.z);
+    moe::DenseArgs xa{};
+    xa.act = x;
+    xa.lda = d;
+    xa.T = T;
+    xa.K = d;
+    xa.N0 = 0;
+    xa.w1 = A;
+    xa.q1 = A_q;
+    xa.N1 = r;
+    xa.z = z;
+    xa.part = p.large ? nullptr : at<float>(ws, p.part);
+    xa.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
+    hipError_t e = stage_mark(0, false, st);
+    if (e == hipSuccess) e = moe::launch_xproj(xa, st);
+    if (e == hipSuccess) e = stage_mark(0, true, st);
+    if (e == hipSuccess && !p.large) e = moe::launch_fold_bf16(xa.part, moe::xproj_split(d).splits, T, r, z, st);
+    if (e != hipSuccess) return device_fail(e, "low-rank projection launch");
+    moe::DenseArgs ca{};
+    ca.act = z;
+    ca.lda = r;
+    ca.T = T;
+    ca.K = r;
+    ca.w0 = B;
+    ca.q0 = B_q;
+    ca.N0 = d;
+    ca.slots = y_in;           // y_in enters as the one "shared" slot of each token
+    ca.top_k = 0;
+    ca.n_shared = y_in ? 1 : 0;
+    ca.y = y;
+    ca.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
+    e = stage_mark(1, false, st);
+    if (e == hipSuccess) e = moe::launch_combine(ca, st);
+    if (e == hipSuccess) e = stage_mark(1, true, st);
+    if (e != hipSuccess) return device_fail(e, "low-rank combine launch");
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_lowrank_apply");
+  }
+}
+
 int64_t moe_draft_head_workspace_bytes(int64_t n_tokens, int32_t hidden, int32_t inner) {
   if (n_tokens < 0 || hidden <= 0 || inner <= 0) return -1;
   return moe::head_plan(n_tokens, hidden, inner).total;

@@ -152,6 +152,8 @@ struct HeadPlan {
 HeadPlan head_plan(int64_t T, int h, int m);
 // stage_events: NULL or the caller's events; [0..1] bracket fc1's product, [2..3] fc2's.
 hipError_t launch_head(const HeadArgs& a, char* ws, hipStream_t stream, void** stage_events);
+// out[t, n] = bf16 of the sum, in slice order, of fp32 partials part[s][t][n].
+hipError_t launch_fold_bf16(const float* part, int splits, int64_t T, int N, uint16_t* out, hipStream_t stream);
 // Compute units of the current device (256 if the query fails).
 int cu_count();
 // Quantizer: groups of 128 bfloat16 weights (w 16-byte aligned, dst 4-byte

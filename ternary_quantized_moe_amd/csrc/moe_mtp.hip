@@ -65,6 +65,10 @@ int64_t up256(int64_t v) { return (v + 255) / 256 * 256; }
 
 }  // namespace
 
+hipError_t launch_fold_bf16(const float* part, int splits, int64_t T, int N, uint16_t* out, hipStream_t stream) {
+  return launch_finish<false>(part, splits, T, N, nullptr, out, stream);
+}
+
 HeadPlan head_plan(int64_t T, int h, int m) {
   HeadPlan p{};
   p.large = T > kGroupMaxT;

@@ -193,6 +193,28 @@ def test_draft_head_validation():
     assert L.moe_draft_head_workspace_bytes(4, 256, 512) > 0
     assert L.moe_draft_head_workspace_bytes(-1, 256, 512) == -1
 
+def test_lowrank_validation():
+    """moe_lowrank_apply checks on the host, before any launch."""
+    L = tq.lib()
+    args = dict(x=0x10000, yin=None, T=4, d=256, A=0x30000, Aq=None, B=0x40000, Bq=None, r=64, y=0x50000,
+                ws=0x60000, ws_bytes=1 << 40)
+
+    def rc(**kw):
+        a = dict(args, **kw)
+        return L.moe_lowrank_apply(a["x"], a["yin"], a["T"], a["d"], a["A"], a["Aq"], a["B"], a["Bq"], a["r"],
+                                   a["y"], a["ws"], a["ws_bytes"], None)
+    assert rc(d=200) == -3 and rc(r=12) == -3 and rc(r=8192) == -3 and rc(T=-1) == -3
+    assert rc(B=None, Bq=0x70000) == -3                # a ternary B needs r % 128 == 0
+    assert rc(A=None) == -1 and rc(Aq=0x70000) == -1   # exactly one form of each
+    assert rc(x=None) == -1 and rc(y=0x10000) == -1    # y aliasing x
+    assert rc(ws=0x60010) == -1
+    assert rc(yin=0x20008) == -1 and rc(A=0x30002) == -1
+    assert rc(ws_bytes=1024) == -6
+    assert rc(T=0) == 0
+    assert L.moe_lowrank_workspace_bytes(4, 256, 64) > 0
+    assert L.moe_lowrank_workspace_bytes(4, 0, 64) == -1
+
+
 def test_route_validation():
     L = tq.lib()
     assert L.moe_route(0x1000, 4, 100, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 1 << 30, None) == -3
