@@ -121,6 +121,13 @@ def router_logits(x: np.ndarray, w_r: np.ndarray, dw_r: Optional[np.ndarray]) ->
     return x @ w.T
 
 
+def factored_delta(u_bits, v_bits) -> np.ndarray:
+    """The router delta given as two low-rank fp16 factors, dW_r = U V with U
+    [E, rd] and V [rd, d] (FlashNext card, "Weight Representation": the router
+    deltas ship as rank-512 F16 factors), formed exactly in float64."""
+    return f16_to_f64(u_bits) @ f16_to_f64(v_bits)
+
+
 def select_topk(logits: np.ndarray, k: int) -> np.ndarray:
     """Per token, the k experts with the largest logits, in rank order; equal
     logits order by lower expert index (so -0.0 and +0.0 tie)."""
@@ -201,15 +208,21 @@ class Result:
 
 
 def forward(x_bits, router_bits, delta_bits, banks: Banks, a_bits, b_bits, top_k: int,
-            forced_idx: Optional[np.ndarray] = None) -> Result:
+            forced_idx: Optional[np.ndarray] = None, delta_factors=None) -> Result:
     """The block's forward pass over tokens x (bf16 bits [T, d]).  forced_idx, if
     given, replaces the oracle's own top-k choice (gate weights are still the
-    softmax of the oracle's logits at those indices)."""
+    softmax of the oracle's logits at those indices).  delta_factors, if given,
+    is (U, V) in fp16 bits, the router delta U V in place of delta_bits."""
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
     E = banks.n_experts
     w_r = f16_to_f64(router_bits)
-    dw_r = None if delta_bits is None else f16_to_f64(delta_bits)
+    if delta_factors is not None:
+        if delta_bits is not None:
+            raise ValueError("give the router delta dense or as factors, not both")
+        dw_r = factored_delta(*delta_factors)
+    else:
+        dw_r = None if delta_bits is None else f16_to_f64(delta_bits)
     a = None if a_bits is None else f16_to_f64(a_bits)
     b = None if b_bits is None else f16_to_f64(b_bits)
 
