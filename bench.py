@@ -44,7 +44,11 @@ WORKLOADS = {
     "olmoe-b1-q": ("olmoe", 1, "decode", "q"), "a3b35-b1-q": ("a3b35", 1, "decode", "q"),
     "flashnext-b1-q": ("flashnext", 1, "decode", "q"), "flashnext-b64-q": ("flashnext", 64, "decode", "q"),
     "a3b35-p4096-q": ("a3b35", 4096, "prefill", "q"),
+    # the router delta as rank-512 fp16 factors U V (the FlashNext release's form)
+    "flashnext-b1-fd": ("flashnext", 1, "decode", "fd"), "flashnext-b64-fd": ("flashnext", 64, "decode", "fd"),
+    "flashnext-p4096-fd": ("flashnext", 4096, "prefill", "fd"),
 }
+DELTA_FACTOR_RANK = 512
 DEFAULT_WORKLOAD = "olmoe-b64"
 # the ternary quantizer (bfloat16 weights -> containers) on every expert bank of a
 # layer: name -> (layer config, container id, rule 0 absmean / 1 Lloyd)
@@ -112,6 +116,13 @@ def load_traffic(workload: str, sources=EXPERT_SOURCES):
     return rec.get("traffic_bytes_per_launch")
 
 
+def f16_bits_of(dtype, factors):
+    """fp16 bits of the product U V of two fp16-bit factor matrices."""
+    import numpy as np
+    u, v = [np.ascontiguousarray(a).view(np.float16).astype(dtype) for a in factors]
+    return (u @ v).astype(np.float16).view(np.uint16)
+
+
 def f16_expansion(trits, scale_bits):
     """fp16 bits of s * t for trits [rows, cols] and scale bits [rows, cols/128]:
     the scale with its sign flipped for t = -1, +0 for t = 0."""
@@ -133,7 +144,8 @@ class Bench:
         self.np, self.torch, self.tq = np, torch, tq
         self.workload = workload
         cname, self.T, self.mode = WORKLOADS[workload][:3]
-        self.ternary_corr = len(WORKLOADS[workload]) > 3
+        variant = WORKLOADS[workload][3] if len(WORKLOADS[workload]) > 3 else ""
+        self.ternary_corr, self.factored = variant == "q", variant == "fd"
         self.cfg = c = CONFIGS[cname]
         self.gen = g = LayerGen(c)
         self.formats = g.formats()
@@ -159,7 +171,15 @@ class Bench:
             self.delta, self.corr_a, self.corr_b = [
                 torch.from_numpy(tq.pack(142, tr.reshape(-1), sb.reshape(-1))).to(dev) for tr, sb in parts]
             self.delta_bits, self.a_bits, self.b_bits = [f16_expansion(tr, sb) for tr, sb in parts]
+            self.delta_factors = None
+        elif self.factored:
+            self.delta_factors = g.delta_factor_bits(DELTA_FACTOR_RANK)
+            self.du, self.dv = [t(a) for a in self.delta_factors]
+            self.delta_bits = self.delta = None
+            self.a_bits, self.b_bits = g.corr_a_bits(), g.corr_b_bits()
+            self.corr_a, self.corr_b = t(self.a_bits), t(self.b_bits)
         else:
+            self.delta_factors = None
             self.delta_bits = g.delta_bits()
             self.a_bits, self.b_bits = g.corr_a_bits(), g.corr_b_bits()
             self.delta = t(self.delta_bits)
@@ -168,11 +188,19 @@ class Bench:
         self.x_bits = [g.tokens(self.T, p) for p in range(self.P)]
         self.x = [t(xb) for xb in self.x_bits]
         self.y = torch.empty_like(self.x[0])
-        self.ws = tq.alloc_workspace(tq.workspace_bytes(self.banks[0], self.T, c.top_k, c.rank), dev)
+        if self.factored:
+            need = tq.lib().moe_workspace_bytes_factored(self.banks[0].c, self.T, c.top_k, c.rank, DELTA_FACTOR_RANK)
+            # the routing of the sets below takes U V rounded to fp16 as a dense
+            # delta: it stands in for the factored choice (touched banks, bytes)
+            uv = f16_bits_of(np.float64, self.delta_factors)
+        else:
+            need = tq.workspace_bytes(self.banks[0], self.T, c.top_k, c.rank)
+            uv = self.delta_bits
+        self.ws = tq.alloc_workspace(need, dev)
         # realised routing of every activation set (untimed): touched banks, slots
         self.touched, self.idx = [], []
         for p in range(self.P):
-            r = tq.route(self.x[p], self.router, t(self.delta_bits), c.n_experts, c.top_k)
+            r = tq.route(self.x[p], self.router, t(uv), c.n_experts, c.top_k)
             counts = r["counts"].cpu().numpy()
             touched = np.nonzero(counts)[0]
             self.touched.append(np.concatenate([touched, np.arange(c.n_experts, c.n_banks)]))
@@ -185,7 +213,10 @@ class Bench:
 
     def step(self, i: int):
         c = self.cfg
-        if self.ternary_corr:
+        if self.factored:
+            self.tq.forward_factored(self.x[i % self.P], self.router, self.du, self.dv, self.banks[i % self.R],
+                                     self.corr_a, self.corr_b, c.top_k, y=self.y, workspace=self.ws)
+        elif self.ternary_corr:
             self.tq.forward_q(self.x[i % self.P], self.router, self.delta, self.banks[i % self.R], self.corr_a,
                               self.corr_b, c.rank, c.top_k, y=self.y, workspace=self.ws)
         else:
@@ -203,8 +234,10 @@ class Bench:
         T = self.T
         toks = np.unique(np.linspace(0, T - 1, min(n_tokens, T)).astype(int))
         ob = omoe.LazyBanks(self.source, self.formats, c.d_model, c.d_ff, c.n_experts, c.n_shared)
+        # (with factors, the oracle's own top-k: the device's choice is not exported)
         ref = omoe.forward(self.x_bits[0][toks], self.router_bits, self.delta_bits, ob, self.a_bits,
-                           self.b_bits, c.top_k, forced_idx=self.idx[0][toks])
+                           self.b_bits, c.top_k, forced_idx=None if self.factored else self.idx[0][toks],
+                           delta_factors=self.delta_factors)
         yg = omoe.bf16_to_f64(y[toks])
         return float((np.abs(yg - ref.y).max(axis=1) / np.linalg.norm(ref.y, axis=1)).max())
 
@@ -218,9 +251,12 @@ class Bench:
         n_pos = T * k + S * T
         expert_bytes = int((self.gu_bytes[touched] + self.dn_bytes[touched]).sum())
         dense_bytes = 34 / 128 if self.ternary_corr else 2       # per weight of the delta, A and B
-        block_bytes = int(expert_bytes + 2 * E * d + dense_bytes * (E * d + 2 * r * d) + 4 * T * d)
+        delta_w = E * d if not self.factored else DELTA_FACTOR_RANK * (E + d)
+        block_bytes = int(expert_bytes + 2 * E * d + dense_bytes * (delta_w + 2 * r * d) + 4 * T * d)
         gu_bytes = int(self.gu_bytes[touched].sum()) + 2 * T * d + 2 * n_pos * f
         block_flops = 2 * (n_pos * 3 * d * f + T * E * d + 2 * T * r * d)
+        if self.factored:
+            block_flops += 2 * T * DELTA_FACTOR_RANK * (d + E)
         gu_flops = 2 * n_pos * 2 * f * d
         return block_bytes, gu_bytes, block_flops, gu_flops
 
@@ -236,7 +272,8 @@ def cpu_baseline(b: Bench, budget_s: float = 25.0):
     except Exception:
         cores = os.cpu_count() or 1
     x = omoe.bf16_to_f64(b.x_bits[0])
-    w = omoe.f16_to_f64(b.router_bits) + omoe.f16_to_f64(b.delta_bits)
+    w = omoe.f16_to_f64(b.router_bits) + (omoe.factored_delta(*b.delta_factors) if b.factored
+                                          else omoe.f16_to_f64(b.delta_bits))
     order = np.argsort(-(x @ w.T), axis=1, kind="stable")[:, :c.top_k]
 
     def needed(s):
@@ -266,7 +303,8 @@ def cpu_baseline(b: Bench, budget_s: float = 25.0):
     reps, dt = 0, 0.0
     while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
         t0 = time.perf_counter()
-        omoe.forward(b.x_bits[0][:s], b.router_bits, b.delta_bits, banks, b.a_bits, b.b_bits, c.top_k)
+        omoe.forward(b.x_bits[0][:s], b.router_bits, b.delta_bits, banks, b.a_bits, b.b_bits, c.top_k,
+                     delta_factors=b.delta_factors)
         dt += time.perf_counter() - t0
         reps += 1
     return {"value": reps * s / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
@@ -352,7 +390,8 @@ def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{DESCR[c.name]}, {b.mode} {b.T} tokens"
-                               + (", router delta and correction as ternary PQ2_0 containers" if b.ternary_corr else ""),
+                               + (", router delta and correction as ternary PQ2_0 containers" if b.ternary_corr else "")
+                               + (f", router delta as rank-{DELTA_FACTOR_RANK} fp16 factors" if b.factored else ""),
                    "name": workload,
                    "tokens": b.T, "mode": b.mode, "bank_replicas": b.R, "activation_sets": b.P,
                    "parallelism": "single-gpu"},

@@ -279,6 +279,27 @@ int32_t moe_ternary_forward_q(const uint16_t* x, int64_t n_tokens, const uint16_
                               int32_t top_k, uint16_t* y, void* workspace, int64_t workspace_bytes,
                               void* stream);
 
+/* The same forward pass with the router delta given as two low-rank factors,
+ * the way the FlashNext release ships it (Scion-FlashNext-176B-A6B card,
+ * "Weight Representation": rank-512 F16 factors for the router deltas): the
+ * logits are W_r x + U (V x).
+ *   delta_U     device fp16 [E x delta_rank], 16-byte aligned
+ *   delta_V     device fp16 [delta_rank x d_model], 4-byte aligned
+ *   delta_rank  a positive multiple of 8, at most 1024
+ * V x is computed as the router's own product (fp32 on matrix cores, fp16
+ * weights as exact bf16 pairs) and kept in fp32; U (V x) accumulates in fp32
+ * and joins the router logits before the top-k.  The workspace is
+ * moe_workspace_bytes_factored's; corrections are fp16 (or NULL), and the
+ * other arguments and the errors are moe_ternary_forward's (MOE_E_SHAPE for a
+ * bad delta_rank). */
+int64_t moe_workspace_bytes_factored(const moe_expert_banks* banks, int64_t n_tokens, int32_t top_k,
+                                     int32_t corr_rank, int32_t delta_rank);
+int32_t moe_ternary_forward_factored(const uint16_t* x, int64_t n_tokens, const uint16_t* router,
+                                     const uint16_t* delta_U, const uint16_t* delta_V, int32_t delta_rank,
+                                     const moe_expert_banks* banks, const uint16_t* corr_A,
+                                     const uint16_t* corr_B, int32_t corr_rank, int32_t top_k, uint16_t* y,
+                                     void* workspace, int64_t workspace_bytes, void* stream);
+
 /* Workspace bytes moe_route needs. */
 int64_t moe_route_workspace_bytes(int64_t n_tokens, int32_t d_model, int32_t n_experts,
                                   int32_t top_k);

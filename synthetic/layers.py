@@ -33,6 +33,7 @@ PTQ1_0 = 143   # (Scion-35B-A3B card "Quickstart"; FlashNext card "About the Hub
 # ternary-coded dW_r, A, B)
 _K_X, _K_WR, _K_DWR, _K_CODES, _K_SCALES, _K_A, _K_B, _K_OUTL, _K_FMT, _K_ZIPF = range(10)
 _K_DWR_Q, _K_A_Q, _K_B_Q = 10, 11, 12
+_K_DU, _K_DV = 13, 14
 # group-scale spread of the ternary-coded router delta and correction: a
 # ternary code set with P(+-1) = 0.3 each and scale |N(0, sigma)| has about the
 # magnitude of the dense N(0, 0.002) delta and N(0, 0.01) factors
@@ -146,6 +147,15 @@ class LayerGen:
     def corr_b_bits(self) -> np.ndarray:
         c = self.cfg
         return f16_bits(self.rng(_K_B).normal(0.0, 0.01, size=(c.d_model, c.rank)))
+
+    def delta_factor_bits(self, rank: int):
+        """(U [E, rank], V [rank, d]) fp16 bits of a factorised router delta;
+        entries N(0, 0.02), so U V has a spread of about 0.02^2 sqrt(rank)
+        (0.009 at rank 512, half the router weights')."""
+        c = self.cfg
+        u = self.rng(_K_DU, rank).normal(0.0, 0.02, size=(c.n_experts, rank))
+        v = self.rng(_K_DV, rank).normal(0.0, 0.02, size=(rank, c.d_model))
+        return f16_bits(u), f16_bits(v)
 
     # -- ternary-coded router delta and correction -----------------------------
     def _ternary(self, kind: int, rows: int, cols: int):

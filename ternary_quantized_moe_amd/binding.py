@@ -27,6 +27,7 @@ EXPORTS = [
     "moe_block_bytes", "moe_packed_bytes", "moe_pack", "moe_unpack", "moe_unpack_device",
     "moe_quantize_device", "moe_ple_gather_q4_0", "moe_ternary_forward_q", "moe_draft_head_workspace_bytes",
     "moe_draft_head", "moe_lowrank_workspace_bytes", "moe_lowrank_apply",
+    "moe_workspace_bytes_factored", "moe_ternary_forward_factored",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
     "moe_set_stage_events", "moe_last_error",
 ]
@@ -76,6 +77,9 @@ def lib():
             "moe_draft_head": (i32, [vp, vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, i64, vp]),
             "moe_lowrank_workspace_bytes": (i64, [i64, i32, i32]),
             "moe_lowrank_apply": (i32, [vp, vp, i64, i32, vp, vp, vp, vp, i32, vp, vp, i64, vp]),
+            "moe_workspace_bytes_factored": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32, i32]),
+            "moe_ternary_forward_factored": (i32, [vp, i64, vp, vp, vp, i32, ctypes.POINTER(ExpertBanksC), vp, vp,
+                                                   i32, i32, vp, vp, i64, vp]),
             "moe_tile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_untile_container": (i32, [i32, vp, i64, i64, vp, i64]),
             "moe_workspace_bytes": (i64, [ctypes.POINTER(ExpertBanksC), i64, i32, i32]),
@@ -304,6 +308,27 @@ def forward_q(x, router, router_delta_q, banks: ExpertBanks, corr_a_q, corr_b_q,
     _check(lib().moe_ternary_forward_q(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta_q), banks.c,
                                        _dev_ptr(corr_a_q), _dev_ptr(corr_b_q), r, top_k, _dev_ptr(y), wp, wn,
                                        _stream(stream)))
+    return y
+
+
+def forward_factored(x, router, delta_u, delta_v, banks: ExpertBanks, corr_a, corr_b, top_k: int, y=None,
+                     workspace=None, stream=None):
+    """forward() with the router delta as fp16 factors U [E, rd] and V [rd, d]."""
+    import torch
+    T = x.shape[0]
+    rd = delta_u.shape[1]
+    r = 0 if corr_a is None else corr_a.shape[0]
+    if y is None:
+        y = torch.empty_like(x)
+    need = lib().moe_workspace_bytes_factored(banks.c, T, top_k, r, rd)
+    if need < 0:
+        raise MoeError(-1, "invalid arguments for the workspace size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_ternary_forward_factored(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(delta_u), _dev_ptr(delta_v),
+                                              rd, banks.c, _dev_ptr(corr_a), _dev_ptr(corr_b), r, top_k,
+                                              _dev_ptr(y), wp, wn, _stream(stream)))
     return y
 
 

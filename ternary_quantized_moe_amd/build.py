@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_ternary.so")
-SOURCES = ["moe_capi.hip", "moe_kernels.hip", "moe_experts.hip", "moe_dense.hip", "moe_quant.hip", "moe_ple.hip", "moe_mtp.hip"]
+SOURCES = ["moe_capi.hip", "moe_kernels.hip", "moe_experts.hip", "moe_dense.hip", "moe_quant.hip", "moe_ple.hip", "moe_mtp.hip", "moe_router_delta.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -13,6 +13,7 @@
 
 #include "moe_ternary.h"
 #include "moe_internal.h"
+#include "router_delta.h"
 
 namespace {
 
@@ -60,14 +61,16 @@ int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t T, Tk, n_pos, nb, max_items;
-  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, xpart, h, slots;
+  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, xpart, vpart, h, slots;
+  int rd;  // rank of a factorised router delta, 0 for none
   bool large;
   int64_t route_end, total;
 };
 
-Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
+Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) {
   Plan p{};
   p.T = T;
+  p.rd = rd;
   p.Tk = T * k;
   p.n_pos = p.Tk + (int64_t)S * T;
   p.nb = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
@@ -88,10 +91,17 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r) {
   // large batches: split dense weights of the x-projection, later of the combine
   p.large = T > moe::kGroupMaxT;
   p.wsplit = o;
-  if (p.large) o += up(std::max(moe::dense_split_bytes(E + r, d), moe::dense_split_bytes(d, r)));
-  // small batches: fp32 x-projection partials over the K slices
+  if (p.large)
+    o += up(std::max({moe::dense_split_bytes(E + r, d), moe::dense_split_bytes(d, r),
+                      rd ? moe::dense_split_bytes(rd, d) : (int64_t)0}));
+  // small batches: fp32 x-projection partials over the K slices (and with a
+  // factorised router delta one more slice, its U (V x) and zeros)
+  const int splits = moe::xproj_split(d).splits;
   p.xpart = o;
-  if (!p.large && T > 0) o += up((int64_t)moe::xproj_split(d).splits * T * (E + r) * 4);
+  if (!p.large && T > 0) o += up((int64_t)(splits + (rd ? 1 : 0)) * T * (E + r) * 4);
+  // V x of a factorised delta: its fp32 slices (small batches) or fp32 rows
+  p.vpart = o;
+  if (rd) o += up((int64_t)(p.large ? 1 : splits) * T * rd * 4);
   p.route_end = o;
   p.z = o; o += up(T * (int64_t)r * 2);
   p.h = o; o += up(p.n_pos * f * 2);
@@ -492,11 +502,29 @@ int64_t moe_workspace_bytes(const moe_expert_banks* banks, int64_t n_tokens, int
 
 // delta_q, corr_A_q: the router delta and A as ternary PQ2_0 containers (in
 // place of delta, corr_A), or NULL.
+// delta_U, delta_V: the router delta as factors U [E x p.rd], V [p.rd x d]
+// (p.rd > 0), in place of delta / delta_q.
 static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, const uint16_t* router,
                           const uint16_t* delta, const uint8_t* delta_q, const uint16_t* corr_A,
                           const uint8_t* corr_A_q, int r, int k, const Plan& p, void* ws, hipStream_t stream,
                           float* logits, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
-                          int32_t* perm) {
+                          int32_t* perm, const uint16_t* delta_U = nullptr, const uint16_t* delta_V = nullptr) {
+  const int splits = moe::xproj_split(d).splits;
+  hipError_t e = stage_mark(0, false, stream);
+  if (p.rd && e == hipSuccess) {  // V x first, as an x-projection of its own with fp32 outputs
+    moe::DenseArgs va{};
+    va.act = x;
+    va.lda = d;
+    va.T = T;
+    va.K = d;
+    va.w0 = delta_V;
+    va.N0 = p.rd;
+    va.logits = at<float>(ws, p.vpart);
+    va.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
+    va.part = p.large ? nullptr : at<float>(ws, p.vpart);
+    e = moe::launch_xproj(va, stream);
+  }
+  if (e != hipSuccess) return device_fail(e, "router delta V x launch");
   moe::DenseArgs da{};
   da.act = x;
   da.lda = d;
@@ -513,8 +541,15 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.z = at<uint16_t>(ws, p.z);
   da.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
   da.part = p.large ? nullptr : at<float>(ws, p.xpart);
-  hipError_t e = stage_mark(0, false, stream);
-  if (e == hipSuccess) e = moe::launch_xproj(da, stream);
+  e = moe::launch_xproj(da, stream);
+  if (e == hipSuccess && p.rd) {
+    // U (V x): added to the logits (large batches), or written as one more
+    // partial slice that the routing adds last (small batches)
+    const int lN = da.N0 + da.N1;
+    float* dst = p.large ? logits : da.part + (int64_t)splits * T * lN;
+    e = moe::launch_router_delta(at<float>(ws, p.vpart), p.large ? 1 : splits, T, p.rd, delta_U, E, dst,
+                                 p.large ? E : lN, p.large, stream);
+  }
   if (e == hipSuccess) e = stage_mark(0, true, stream);
   if (e != hipSuccess) return device_fail(e, "xproj launch");
 
@@ -537,7 +572,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.chunk = moe::item_chunk(T);
   if (!p.large) {  // the routing adds up the partials: the logits, and z for the combine
     ra.lpart = da.part;
-    ra.lsplits = moe::xproj_split(d).splits;
+    ra.lsplits = splits + (p.rd ? 1 : 0);
     ra.lN = da.N0 + da.N1;
     ra.z = da.N1 > 0 ? da.z : nullptr;
     ra.zr = da.N1;
@@ -577,7 +612,8 @@ int32_t moe_route(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint
 static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
                             const uint8_t* delta_q, const moe_expert_banks* banks, const uint16_t* corr_A,
                             const uint8_t* corr_A_q, const uint16_t* corr_B, const uint8_t* corr_B_q, int32_t r,
-                            int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream) {
+                            int32_t k, uint16_t* y, void* ws, int64_t ws_bytes, void* stream,
+                            const uint16_t* delta_U = nullptr, const uint16_t* delta_V = nullptr, int rd = 0) {
   {
     int32_t rc = check_banks(banks);
     if (rc) return rc;
@@ -595,19 +631,29 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
       return fail(MOE_E_ARG, "ternary containers must be 2-byte aligned");
     if (r % 8) return fail(MOE_E_SHAPE, "corr_rank must be a multiple of 8 (got %d)", r);
     if (r > 4096) return fail(MOE_E_SHAPE, "corr_rank above 4096 is not supported (got %d)", r);
+    if (rd) {
+      if (rd < 0 || rd % 8 || rd > moe::kDeltaMaxRank)
+        return fail(MOE_E_SHAPE, "delta_rank must be a positive multiple of 8, at most %d (got %d)",
+                    moe::kDeltaMaxRank, rd);
+      if (delta || delta_q) return fail(MOE_E_ARG, "give the router delta dense or as factors, not both");
+    }
     if (T == 0) return ok();
     if (!x || !router || !y || !ws) return fail(MOE_E_ARG, "NULL pointer");
+    if (rd && (!delta_U || !delta_V)) return fail(MOE_E_ARG, "NULL delta factor");
+    if ((uintptr_t)delta_U % 16 || (uintptr_t)delta_V % 4)
+      return fail(MOE_E_ARG, "delta_U must be 16-byte and delta_V 4-byte aligned");
     if (x == y) return fail(MOE_E_ARG, "y must not alias x");
     if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
     if ((uintptr_t)x % 16 || (uintptr_t)y % 4) return fail(MOE_E_ARG, "x must be 16-byte and y 4-byte aligned");
-    const Plan p = make_plan(T, d, E, S, f, k, r);
+    const Plan p = make_plan(T, d, E, S, f, k, r, rd);
     if (ws_bytes < p.total)
       return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
     const hipStream_t st = (hipStream_t)stream;
 
     rc = route_impl(x, T, d, E, S, router, delta, delta_q, corr_A, corr_A_q, r, k, p, ws, st,
                     at<float>(ws, p.logits), at<int32_t>(ws, p.idx), at<float>(ws, p.w),
-                    at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm));
+                    at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), delta_U,
+                    delta_V);
     if (rc) return rc;
 
     moe::ExpertArgs ea{};
@@ -664,6 +710,27 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t T, const uint16_t* router
                         ws_bytes, stream);
   } catch (...) {
     return fail(MOE_E_ARG, "internal error in moe_ternary_forward");
+  }
+}
+
+int64_t moe_workspace_bytes_factored(const moe_expert_banks* banks, int64_t n_tokens, int32_t top_k,
+                                     int32_t corr_rank, int32_t delta_rank) {
+  if (!banks || n_tokens < 0 || top_k < 1 || corr_rank < 0 || delta_rank < 1) return -1;
+  return make_plan(n_tokens, banks->d_model, banks->n_experts, banks->n_shared, banks->d_ff, top_k, corr_rank,
+                   delta_rank)
+      .total;
+}
+
+int32_t moe_ternary_forward_factored(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta_U,
+                                     const uint16_t* delta_V, int32_t delta_rank, const moe_expert_banks* banks,
+                                     const uint16_t* corr_A, const uint16_t* corr_B, int32_t r, int32_t k, uint16_t* y,
+                                     void* ws, int64_t ws_bytes, void* stream) {
+  try {
+    if (delta_rank <= 0) return fail(MOE_E_SHAPE, "delta_rank must be positive (got %d)", (int)delta_rank);
+    return forward_impl(x, T, router, nullptr, nullptr, banks, corr_A, nullptr, corr_B, nullptr, r, k, y, ws,
+                        ws_bytes, stream, delta_U, delta_V, delta_rank);
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_ternary_forward_factored");
   }
 }
 

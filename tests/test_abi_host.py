@@ -173,6 +173,23 @@ def test_ternary_forward_validation():
     assert rc(k=9) == -3
 
 
+def test_factored_forward_validation():
+    """moe_ternary_forward_factored checks on the host, before any launch."""
+    L = tq.lib()
+    c, keep = _fake_banks()
+
+    def rc(rd=64, U=0x50000, V=0x60000, T=4, ws_bytes=1 << 40):
+        return L.moe_ternary_forward_factored(0x10000, T, 0x70000, U, V, rd, ctypes.byref(c), None, None, 0, 2,
+                                              0x20000, 0x40000, ws_bytes, None)
+    assert rc(rd=12) == -3 and rc(rd=0) == -3 and rc(rd=2048) == -3
+    assert rc(U=None) == -1 and rc(V=None) == -1
+    assert rc(U=0x50008) == -1 and rc(V=0x60002) == -1     # U 16-byte, V 4-byte aligned
+    assert rc(ws_bytes=4096) == -6
+    assert rc(T=0) == 0
+    assert L.moe_workspace_bytes_factored(ctypes.byref(c), 16, 2, 0, 64) > L.moe_workspace_bytes(ctypes.byref(c), 16, 2, 0)
+    assert L.moe_workspace_bytes_factored(ctypes.byref(c), 16, 2, 0, 0) == -1
+
+
 def test_draft_head_validation():
     """moe_draft_head checks on the host, before any launch."""
     L = tq.lib()
