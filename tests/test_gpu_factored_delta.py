@@ -14,6 +14,7 @@ import pytest
 
 from layer_fixtures import Layer, row_metric
 from oracle import moe as omoe
+from synthetic import LayerConfig
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -119,3 +120,28 @@ def test_factored_delta_batch_independence():
     y_part = tq.forward_factored(part["x"], part["router"], du, dv, L.device(), part["a"], part["b"], c.top_k)
     torch.cuda.synchronize()
     assert np.array_equal(bits(y_full)[7:9], bits(y_part))
+
+
+# edge shapes: 13 experts (row groups of four with a ragged last one), the
+# smallest and largest factor ranks, the 256 / 257 token boundary between the
+# K-sliced and the tiled x-projection
+ODD = LayerConfig("odd13", 21, 256, 13, 128, 3, 1, 16, "mixed")
+
+
+@pytest.mark.parametrize("cfg,rank,T", [(ODD, 8, 5), (ODD, 1024, 16), (ODD, 1024, 300), (ODD, 24, 256),
+                                        (ODD, 24, 257)])
+def test_factored_delta_edge_shapes(cfg, rank, T):
+    import ternary_quantized_moe_amd as tq
+    L = Layer(cfg)
+    c = L.cfg
+    u, v = L.gen.delta_factor_bits(rank)
+    x_bits = decided_tokens(L, u, v, T, 11)
+    say(f"factored delta {c.name} E={c.n_experts} T={T} rank={rank}")
+    d = L.tensors(x_bits, use_delta=False)
+    y = tq.forward_factored(d["x"], d["router"], dev16(u), dev16(v), L.device(), d["a"], d["b"], c.top_k)
+    torch.cuda.synchronize()
+    ref = omoe.forward(x_bits, L.router, None, L.oracle_banks, L.corr_a, L.corr_b, c.top_k,
+                       delta_factors=(u, v))
+    m = row_metric(bits(y), ref.y)
+    say(f"  max row metric {m.max():.3e}")
+    assert m.max() <= TOL

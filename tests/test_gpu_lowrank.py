@@ -14,7 +14,7 @@ import pytest
 
 from layer_fixtures import row_metric
 from oracle import codec, moe as omoe
-from synthetic import CONFIGS, LayerGen
+from synthetic import CONFIGS, LayerGen, bf16_bits, f16_bits
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -136,3 +136,21 @@ def test_lowrank_errors_on_device():
     with pytest.raises(tq.MoeError):
         tq.lowrank_apply(xd, None, dev16(a), dev16(b), c.rank, workspace=torch.empty(64, dtype=torch.uint8,
                                                                                       device="cuda"))
+
+
+@pytest.mark.parametrize("d,r,T", [(128, 8, 3), (128, 8, 300), (256, 4096, 2), (256, 4096, 260), (384, 136, 64)])
+def test_lowrank_edge_shapes(d, r, T):
+    """The smallest width and rank, the largest rank, a rank that is not a
+    multiple of 16, on both sides of the 256-token boundary."""
+    import ternary_quantized_moe_amd as tq
+    rng = np.random.default_rng(d * 7 + r + T)
+    x = bf16_bits(rng.normal(size=(T, d)))
+    yin = bf16_bits(rng.normal(size=(T, d)))
+    a = f16_bits(rng.normal(scale=1 / np.sqrt(d), size=(r, d)))
+    b = f16_bits(rng.normal(scale=1 / np.sqrt(r), size=(d, r)))
+    say(f"lowrank edge d={d} r={r} T={T}")
+    y = tq.lowrank_apply(dev16(x), dev16(yin), dev16(a), dev16(b), r)
+    torch.cuda.synchronize()
+    m = row_metric(bits(y), omoe.lowrank_apply(x, yin, a, b))
+    say(f"  max row metric {m.max():.3e}")
+    assert m.max() <= TOL
