@@ -94,14 +94,15 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   if (p.large)
     o += up(std::max({moe::dense_split_bytes(E + r, d), moe::dense_split_bytes(d, r),
                       rd ? moe::dense_split_bytes(rd, d) : (int64_t)0}));
-  // small batches: fp32 x-projection partials over the K slices (and with a
-  // factorised router delta one more slice, its U (V x) and zeros)
+  // small batches: fp32 x-projection partials over the K slices; a factorised
+  // router delta adds its V rows to the projection and one more slice, its
+  // U (V x) and zeros
   const int splits = moe::xproj_split(d).splits;
   p.xpart = o;
-  if (!p.large && T > 0) o += up((int64_t)(splits + (rd ? 1 : 0)) * T * (E + r) * 4);
-  // V x of a factorised delta: its fp32 slices (small batches) or fp32 rows
+  if (!p.large && T > 0) o += up((int64_t)(splits + (rd ? 1 : 0)) * T * (E + r + rd) * 4);
+  // large batches: V x of a factorised delta as fp32 rows
   p.vpart = o;
-  if (rd) o += up((int64_t)(p.large ? 1 : splits) * T * rd * 4);
+  if (rd && p.large) o += up(T * (int64_t)rd * 4);
   p.route_end = o;
   p.z = o; o += up(T * (int64_t)r * 2);
   p.h = o; o += up(p.n_pos * f * 2);
@@ -511,7 +512,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
                           int32_t* perm, const uint16_t* delta_U = nullptr, const uint16_t* delta_V = nullptr) {
   const int splits = moe::xproj_split(d).splits;
   hipError_t e = stage_mark(0, false, stream);
-  if (p.rd && e == hipSuccess) {  // V x first, as an x-projection of its own with fp32 outputs
+  if (p.rd && p.large && e == hipSuccess) {  // V x first, a tiled product of its own with fp32 outputs
     moe::DenseArgs va{};
     va.act = x;
     va.lda = d;
@@ -520,8 +521,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
     va.w0 = delta_V;
     va.N0 = p.rd;
     va.logits = at<float>(ws, p.vpart);
-    va.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
-    va.part = p.large ? nullptr : at<float>(ws, p.vpart);
+    va.wsplit = at<void>(ws, p.wsplit);
     e = moe::launch_xproj(va, stream);
   }
   if (e != hipSuccess) return device_fail(e, "router delta V x launch");
@@ -541,14 +541,20 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   da.z = at<uint16_t>(ws, p.z);
   da.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
   da.part = p.large ? nullptr : at<float>(ws, p.xpart);
+  if (p.rd && !p.large) {  // V's rows join the projection, after the router's and A's
+    da.w2 = delta_V;
+    da.N2 = p.rd;
+  }
+  const int lN = da.N0 + da.N1 + da.N2;
   e = moe::launch_xproj(da, stream);
   if (e == hipSuccess && p.rd) {
     // U (V x): added to the logits (large batches), or written as one more
     // partial slice that the routing adds last (small batches)
-    const int lN = da.N0 + da.N1;
-    float* dst = p.large ? logits : da.part + (int64_t)splits * T * lN;
-    e = moe::launch_router_delta(at<float>(ws, p.vpart), p.large ? 1 : splits, T, p.rd, delta_U, E, dst,
-                                 p.large ? E : lN, p.large, stream);
+    if (p.large)
+      e = moe::launch_router_delta(at<float>(ws, p.vpart), 1, p.rd, T, p.rd, delta_U, E, logits, E, true, stream);
+    else
+      e = moe::launch_router_delta(da.part + da.N0 + da.N1, splits, lN, T, p.rd, delta_U, E,
+                                   da.part + (int64_t)splits * T * lN, lN, false, stream);
   }
   if (e == hipSuccess) e = stage_mark(0, true, stream);
   if (e != hipSuccess) return device_fail(e, "xproj launch");
@@ -573,7 +579,7 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   if (!p.large) {  // the routing adds up the partials: the logits, and z for the combine
     ra.lpart = da.part;
     ra.lsplits = splits + (p.rd ? 1 : 0);
-    ra.lN = da.N0 + da.N1;
+    ra.lN = lN;
     ra.z = da.N1 > 0 ? da.z : nullptr;
     ra.zr = da.N1;
   }

@@ -44,6 +44,10 @@ struct DenseArgs {
   const uint8_t* q0;
   const uint8_t* q0b;
   const uint8_t* q1;
+  // small-batch x-projection only: rows [N0 + N1, N0 + N1 + N2) = w2 (fp16),
+  // which reach the fp32 partials and nothing else
+  const uint16_t* w2;
+  int N2;
   // xproj epilogue
   float* logits;   // fp32 [T x N0]
   uint16_t* z;     // bf16 [T x N1]

@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
   __shared__ f32x4 red[3][RT][MT][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
-  const int N = a.N0 + a.N1;
+  const int N = a.N0 + a.N1 + a.N2;
   const int64_t t0 = (int64_t)blockIdx.z * 64;
   const int nsteps = (a.K + 31) / 32;
   const int s_begin = (blockIdx.y * 4 + wave) * kpw, s_end = min(nsteps, s_begin + kpw);
@@ -259,9 +259,11 @@ __global__ __launch_bounds__(256) void xproj_split_kernel(DenseArgs a, int kpw) 
       wrow[r] = a.w0 + (int64_t)n * a.K;
       if (TQ && a.q0b) qrowb[r] = a.q0b + n * pq2_row_bytes(a.K);
       else if (a.w0b) wrowb[r] = a.w0b + (int64_t)n * a.K;
-    } else if (n < N) {
+    } else if (n < a.N0 + a.N1) {
       if (TQ && a.q1) qrow[r] = a.q1 + (n - a.N0) * pq2_row_bytes(a.K);
       else wrow[r] = a.w1 + (int64_t)(n - a.N0) * a.K;
+    } else if (n < N) {
+      wrow[r] = a.w2 + (int64_t)(n - a.N0 - a.N1) * a.K;
     }
     summed[r] = wrowb[r] != nullptr || qrowb[r] != nullptr;
   }
@@ -444,7 +446,8 @@ static hipError_t launch_dense(const DenseArgs& a, int N, hipStream_t stream) {
 
 // Large batches take the LDS-tiled matrix-core kernels (moe_dense.hip).
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
-  const int N = a.N0 + a.N1;
+  if (a.N2 && !(a.T <= kGroupMaxT && a.part)) return hipErrorInvalidValue;  // w2 rows: split path only
+  const int N = a.N0 + a.N1 + a.N2;
   if (a.T > kGroupMaxT && a.wsplit) return launch_dense_gemm<EPI_XPROJ>(a, N, stream);
   if (a.T <= kGroupMaxT && a.part) {
     const XprojSplit sp = xproj_split(a.K);

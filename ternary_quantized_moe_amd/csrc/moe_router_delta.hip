@@ -1,6 +1,7 @@
 // U (V x) for the factorised router delta, on the vector units.  A block
 // takes TB tokens and folds their V x slices (in slice order) into shared
-// memory, with every slice's 16-byte loads in flight together; each wave then
+// memory, with every slice's loads in flight together (V x comes as columns of
+// the router's own partials up to 256 tokens, as an fp32 matrix beyond); each wave then
 // walks groups of router rows, RB rows for each 16-lane row of the wave.  Lane
 // c of a row takes the 8-wide chunks c, c + 16, ... of the rd inputs, so its
 // loads of U and its shared-memory reads of V x are contiguous across the
@@ -33,35 +34,61 @@ __device__ __forceinline__ float row16_sum(float v) {
 
 template <int TB, int RB, bool ADD>
 __global__ __launch_bounds__(kDeltaThreads) void router_delta_kernel(const float* __restrict__ vpart, int vsplits,
-                                                                     int64_t T, int rd,
+                                                                     int ldv, int64_t T, int rd,
                                                                      const uint16_t* __restrict__ U, int E,
                                                                      float* __restrict__ dst, int ldd) {
   static_assert(TB <= 16, "one token per lane of a 16-lane row");
   extern __shared__ __align__(16) float vs[];  // [TB][rd]
   const int64_t t0 = (int64_t)blockIdx.x * TB;
   const int nt = (int)min<int64_t>(TB, T - t0);
-  const int nv = TB * rd / 4;  // 16-byte pieces of the block's V x
-  const int64_t slice = T * rd / 4;
-  for (int i0 = threadIdx.x; i0 < nv; i0 += 4 * kDeltaThreads) {
-    f32x4 part[4][kDeltaMaxSlices];
+  if (ldv % 4 == 0 && (uintptr_t)vpart % 16 == 0) {  // 16-byte pieces
+    const int nv = TB * rd / 4;
+    const int64_t slice = T * ldv / 4;
+    for (int i0 = threadIdx.x; i0 < nv; i0 += 4 * kDeltaThreads) {
+      f32x4 part[4][kDeltaMaxSlices];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kDeltaThreads;
-      const int tl = 4 * i / rd;
-      const bool live = i < nv && tl < nt;
-      const f32x4* src = (const f32x4*)vpart + (t0 + tl) * (rd / 4) + (i - tl * (rd / 4));
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kDeltaThreads;
+        const int tl = 4 * i / rd;
+        const bool live = i < nv && tl < nt;
+        const f32x4* src = (const f32x4*)vpart + (t0 + tl) * (ldv / 4) + (i - tl * (rd / 4));
 #pragma unroll
-      for (int s = 0; s < kDeltaMaxSlices; ++s)
-        part[u][s] = (live && s < vsplits) ? src[s * slice] : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < kDeltaMaxSlices; ++s)
+          part[u][s] = (live && s < vsplits) ? src[s * slice] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kDeltaThreads;
+        f32x4 v = part[u][0];
+#pragma unroll
+        for (int s = 1; s < kDeltaMaxSlices; ++s)
+          if (s < vsplits) v += part[u][s];
+        if (i < nv) ((f32x4*)vs)[i] = v;
+      }
     }
+  } else {  // single values (a partial row whose V x columns are not 16-byte aligned)
+    const int nv = TB * rd;
+    const int64_t slice = T * (int64_t)ldv;
+    for (int i0 = threadIdx.x; i0 < nv; i0 += 4 * kDeltaThreads) {
+      float part[4][kDeltaMaxSlices];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kDeltaThreads;
-      f32x4 v = part[u][0];
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kDeltaThreads;
+        const int tl = i / rd;
+        const bool live = i < nv && tl < nt;
+        const float* src = vpart + (t0 + tl) * ldv + (i - tl * rd);
 #pragma unroll
-      for (int s = 1; s < kDeltaMaxSlices; ++s)
-        if (s < vsplits) v += part[u][s];
-      if (i < nv) ((f32x4*)vs)[i] = v;
+        for (int s = 0; s < kDeltaMaxSlices; ++s) part[u][s] = (live && s < vsplits) ? src[s * slice] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = i0 + u * kDeltaThreads;
+        float v = part[u][0];
+#pragma unroll
+        for (int s = 1; s < kDeltaMaxSlices; ++s)
+          if (s < vsplits) v += part[u][s];
+        if (i < nv) vs[i] = v;
+      }
     }
   }
   __syncthreads();
@@ -137,7 +164,7 @@ __global__ __launch_bounds__(kDeltaThreads) void router_delta_kernel(const float
 }
 
 template <int TB, int RB>
-hipError_t launch_tb(const float* vpart, int vsplits, int64_t T, int rd, const uint16_t* U, int E, float* dst,
+hipError_t launch_tb(const float* vpart, int vsplits, int ldv, int64_t T, int rd, const uint16_t* U, int E, float* dst,
                      int ldd, bool add, int64_t target_blocks, hipStream_t stream) {
   const int64_t bx = (T + TB - 1) / TB;
   if (bx > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -148,24 +175,27 @@ hipError_t launch_tb(const float* vpart, int vsplits, int64_t T, int rd, const u
   const size_t lds = (size_t)TB * rd * sizeof(float);
   const dim3 grid((unsigned)bx, by);
   if (add)
-    router_delta_kernel<TB, RB, true><<<grid, kDeltaThreads, lds, stream>>>(vpart, vsplits, T, rd, U, E, dst, ldd);
+    router_delta_kernel<TB, RB, true><<<grid, kDeltaThreads, lds, stream>>>(vpart, vsplits, ldv, T, rd, U, E, dst,
+                                                                                     ldd);
   else
-    router_delta_kernel<TB, RB, false><<<grid, kDeltaThreads, lds, stream>>>(vpart, vsplits, T, rd, U, E, dst, ldd);
+    router_delta_kernel<TB, RB, false><<<grid, kDeltaThreads, lds, stream>>>(vpart, vsplits, ldv, T, rd, U, E, dst,
+                                                                                     ldd);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_router_delta(const float* vpart, int vsplits, int64_t T, int rd, const uint16_t* U, int E,
-                               float* dst, int ldd, bool add, hipStream_t stream) {
+hipError_t launch_router_delta(const float* vpart, int vsplits, int ldv, int64_t T, int rd, const uint16_t* U,
+                               int E, float* dst, int ldd, bool add, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
-  if (rd <= 0 || rd % 8 || rd > kDeltaMaxRank || E <= 0 || ldd < E || vsplits < 1 || vsplits > kDeltaMaxSlices)
+  if (rd <= 0 || rd % 8 || rd > kDeltaMaxRank || E <= 0 || ldd < E || ldv < rd || vsplits < 1 ||
+      vsplits > kDeltaMaxSlices)
     return hipErrorInvalidValue;
   // few tokens: 8 per block, one row per lane row, many row slices; many
   // tokens (one fp32 V x): 16 per block and 4 rows per lane row, so each read
   // of V x feeds four rows, about four blocks per compute unit
-  if (T <= 256) return launch_tb<8, 1>(vpart, vsplits, T, rd, U, E, dst, ldd, add, 256, stream);
-  return launch_tb<16, 4>(vpart, vsplits, T, rd, U, E, dst, ldd, add, 1024, stream);
+  if (T <= 256) return launch_tb<8, 1>(vpart, vsplits, ldv, T, rd, U, E, dst, ldd, add, 256, stream);
+  return launch_tb<16, 4>(vpart, vsplits, ldv, T, rd, U, E, dst, ldd, add, 1024, stream);
 }
 
 }  // namespace moe
