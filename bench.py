@@ -558,16 +558,23 @@ def run_ple(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     for i in range(warmup):
         tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # events around one launch in four for small row lists (a record costs host
+    # time comparable to the launch), around every launch otherwise
+    every = 4 if tokens <= 256 else 1
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range((steps + every - 1) // every)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        ev[i][0].record(stream)
-        tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out, stream=stream)
-        ev[i][1].record(stream)
+        if i % every == 0:
+            ev[i // every][0].record(stream)
+            tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out, stream=stream)
+            ev[i // every][1].record(stream)
+        else:
+            tq.ple_gather(d_table, PLE_ROWS, PLE_ROW_LEN, lists[i % P], out=out, stream=stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    launch_s = sum(a.elapsed_time(b) for a, b in ev) / steps * 1e-3
+    launch_s = sum(a.elapsed_time(b) for a, b in ev) / len(ev) * 1e-3
     row_bytes = PLE_ROW_LEN // 32 * 18
     alg_bytes = n_idx * (8 + row_bytes + 4 * PLE_ROW_LEN)       # index, Q4_0 row, fp32 row
     hbm = alg_bytes / launch_s / 1e9
@@ -592,7 +599,7 @@ def run_ple(workload: str, steps: int, warmup: int, with_cpu: bool = True):
         "roofline": {"bound": "hbm", "achieved": round(hbm, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(hbm / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, PLE_SOURCES),
                      "kernel": "ple_gather_kernel", "alg_bytes_per_launch": int(alg_bytes),
-                     "avg_launch_us": round(launch_s * 1e6, 2)},
+                     "avg_launch_us": round(launch_s * 1e6, 2), "timed_steps_with_events": f"1 in {every}"},
     }
     if with_cpu:
         print(f"{workload}: timed, {launch_s * 1e6:.1f} us per launch; oracle on the host next",
@@ -661,12 +668,16 @@ def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     for i in range(max(warmup, R)):
         step(i)
     torch.cuda.synchronize()
-    # events bracket fc1's product (the library's stage events 0 and 1) on every step
-    timer = tq.StageTimer(steps, stages=[0])
+    # events bracket fc1's product (the library's stage events 0 and 1)
+    every = 4 if T <= 256 else 1      # events on one step in four at decode sizes
+    timer = tq.StageTimer((steps + every - 1) // every, stages=[0])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        with timer.step():
+        if i % every == 0:
+            with timer.step():
+                step(warmup + i)
+        else:
             step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -697,7 +708,7 @@ def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, MTP_SOURCES),
                      "kernel": "xproj_split_kernel (fc1)" if T <= 256 else "dense_gemm_kernel (fc1)",
                      "alg_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_s * 1e6, 2),
-                     "k_slices": splits},
+                     "k_slices": splits, "timed_steps_with_events": f"1 in {every}"},
         "head": {"alg_bytes": int(head_bytes),
                  "achieved_GBs": round(head_bytes / (ms_step * 1e-3) / 1e9, 1),
                  "hbm_frac": round(head_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
@@ -781,11 +792,17 @@ def run_lowrank(workload: str, steps: int, warmup: int, with_cpu: bool = True):
     torch.cuda.synchronize()
     # events bracket the product A x (stage 0: up to 256 tokens the K-sliced
     # kernel alone, its slices are added up after it) and B z + y_in (stage 1)
-    timer = tq.StageTimer(steps, stages=[0, 1])
+    # (on one step in four up to 256 tokens: an event record costs host time
+    # that a call of a few microseconds would otherwise pay on every step)
+    every = 4 if T <= 256 else 1
+    timer = tq.StageTimer((steps + every - 1) // every, stages=[0, 1])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        with timer.step():
+        if i % every == 0:
+            with timer.step():
+                step(warmup + i)
+        else:
             step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -809,7 +826,7 @@ def run_lowrank(workload: str, steps: int, warmup: int, with_cpu: bool = True):
                 "unit": "TFLOP/s", "frac": round(flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                 "alg_flops_per_launch": int(flops)}
     roof.update({"traffic": load_traffic(workload, LOWRANK_SOURCES), "kernel": kname,
-                 "avg_launch_us": round(sec * 1e6, 2)})
+                 "avg_launch_us": round(sec * 1e6, 2), "timed_steps_with_events": f"1 in {every}"})
     rec = {
         "metric": LOWRANK_METRIC,
         "value": round(steps * T / elapsed, 1),

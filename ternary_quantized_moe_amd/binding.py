@@ -112,9 +112,16 @@ def _dev_ptr(t):
 
 
 def _stream(stream):
+    """The HIP stream handle: the given torch stream's, else torch's current
+    stream on the current device (read through torch's C binding where it has
+    one, which costs less per call than building a Stream object)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    try:
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    except AttributeError:
+        return torch.cuda.current_stream().cuda_stream
 
 
 # ------------------------------------------------------------------ host codec
@@ -278,10 +285,10 @@ def forward(x, router, router_delta, banks: ExpertBanks, corr_a, corr_b, top_k: 
     r = 0 if corr_a is None else corr_a.shape[0]
     if y is None:
         y = torch.empty_like(x)
-    need = workspace_bytes(banks, T, top_k, r)
-    if need < 0:
-        raise MoeError(-1, "invalid arguments for the workspace size")
     if workspace is None:
+        need = workspace_bytes(banks, T, top_k, r)
+        if need < 0:
+            raise MoeError(-1, "invalid arguments for the workspace size")
         workspace = alloc_workspace(need, x.device)
     wp, wn = _aligned(workspace)
     _check(lib().moe_ternary_forward(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta), banks.c,
@@ -299,10 +306,10 @@ def forward_q(x, router, router_delta_q, banks: ExpertBanks, corr_a_q, corr_b_q,
     r = 0 if corr_a_q is None else corr_rank
     if y is None:
         y = torch.empty_like(x)
-    need = workspace_bytes(banks, T, top_k, r)
-    if need < 0:
-        raise MoeError(-1, "invalid arguments for the workspace size")
     if workspace is None:
+        need = workspace_bytes(banks, T, top_k, r)
+        if need < 0:
+            raise MoeError(-1, "invalid arguments for the workspace size")
         workspace = alloc_workspace(need, x.device)
     wp, wn = _aligned(workspace)
     _check(lib().moe_ternary_forward_q(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta_q), banks.c,
@@ -320,10 +327,10 @@ def forward_factored(x, router, delta_u, delta_v, banks: ExpertBanks, corr_a, co
     r = 0 if corr_a is None else corr_a.shape[0]
     if y is None:
         y = torch.empty_like(x)
-    need = lib().moe_workspace_bytes_factored(banks.c, T, top_k, r, rd)
-    if need < 0:
-        raise MoeError(-1, "invalid arguments for the workspace size")
     if workspace is None:
+        need = lib().moe_workspace_bytes_factored(banks.c, T, top_k, r, rd)
+        if need < 0:
+            raise MoeError(-1, "invalid arguments for the workspace size")
         workspace = alloc_workspace(need, x.device)
     wp, wn = _aligned(workspace)
     _check(lib().moe_ternary_forward_factored(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(delta_u), _dev_ptr(delta_v),
@@ -340,10 +347,10 @@ def draft_head(hidden, emb, w1, b1, w2, b2, y=None, workspace=None, stream=None)
     if y is None:
         import torch
         y = torch.empty_like(hidden)
-    need = lib().moe_draft_head_workspace_bytes(T, h, m)
-    if need < 0:
-        raise MoeError(-3, f"invalid draft head shape T={T} h={h} m={m}")
     if workspace is None:
+        need = lib().moe_draft_head_workspace_bytes(T, h, m)
+        if need < 0:
+            raise MoeError(-3, f"invalid draft head shape T={T} h={h} m={m}")
         workspace = alloc_workspace(need, hidden.device)
     wp, wn = _aligned(workspace)
     _check(lib().moe_draft_head(_dev_ptr(hidden), _dev_ptr(emb), T, h, m, _dev_ptr(w1), _dev_ptr(b1), _dev_ptr(w2),
@@ -358,10 +365,10 @@ def lowrank_apply(x, y_in, a, b, rank: int, a_q=None, b_q=None, y=None, workspac
     T, d = x.shape
     if y is None:
         y = torch.empty_like(x)
-    need = lib().moe_lowrank_workspace_bytes(T, d, rank)
-    if need < 0:
-        raise MoeError(-3, f"invalid low-rank shape T={T} d={d} r={rank}")
     if workspace is None:
+        need = lib().moe_lowrank_workspace_bytes(T, d, rank)
+        if need < 0:
+            raise MoeError(-3, f"invalid low-rank shape T={T} d={d} r={rank}")
         workspace = alloc_workspace(need, x.device)
     wp, wn = _aligned(workspace)
     _check(lib().moe_lowrank_apply(_dev_ptr(x), _dev_ptr(y_in), T, d, _dev_ptr(a), _dev_ptr(a_q), _dev_ptr(b),
@@ -383,10 +390,10 @@ def route(x, router, router_delta, n_experts: int, top_k: int, workspace=None, s
         offsets=torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
         perm=torch.empty(max(T * top_k, 1), dtype=torch.int32, device=dev),
     )
-    need = lib().moe_route_workspace_bytes(T, d, n_experts, top_k)
-    if need < 0:
-        raise MoeError(-1, "invalid arguments for the routing workspace size")
     if workspace is None:
+        need = lib().moe_route_workspace_bytes(T, d, n_experts, top_k)
+        if need < 0:
+            raise MoeError(-1, "invalid arguments for the routing workspace size")
         workspace = alloc_workspace(need, dev)
     wp, wn = _aligned(workspace)
     _check(lib().moe_route(_dev_ptr(x), T, d, n_experts, _dev_ptr(router), _dev_ptr(router_delta), top_k,
