@@ -706,7 +706,8 @@ def run_mtp(workload: str, steps: int, warmup: int, with_cpu: bool = True):
                    "parallelism": "single-gpu", "setup_s": round(setup_s, 1)},
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic(workload, MTP_SOURCES),
-                     "kernel": "xproj_split_kernel (fc1)" if T <= 256 else "dense_gemm_kernel (fc1)",
+                     "kernel": ("xproj_split_kernel (fc1)" if T <= 32 else "xproj_wide_kernel (fc1)") if T <= 256
+                     else "dense_gemm_kernel (fc1)",
                      "alg_bytes_per_launch": int(fc1_bytes), "avg_launch_us": round(fc1_s * 1e6, 2),
                      "k_slices": splits, "timed_steps_with_events": f"1 in {every}"},
         "head": {"alg_bytes": int(head_bytes),

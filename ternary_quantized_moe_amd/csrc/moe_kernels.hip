@@ -223,8 +223,7 @@ __global__ __launch_bounds__(64 * KS) void dense_kernel(DenseArgs a) {
 // order and the block stores one fp32 partial; the partials are added in slice
 // order by their consumers, so no block waits for another and the weight bytes
 // spread over the whole chip.
-constexpr int kXprojWideRows = 2048;  // output rows from which blocks take several row tiles
-constexpr int kXprojWideTiles = 2;
+constexpr int kXprojWideRows = 2048;  // output rows from which 33+ tokens take xproj_wide_kernel
 
 // TQ: some rows come from ternary PQ2_0 containers (a.q0b, a.q1).  RT: row
 // tiles per block; each activation load then feeds RT tiles (worth it where the
@@ -444,6 +443,156 @@ static hipError_t launch_dense(const DenseArgs& a, int N, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Small-batch x-projection of many rows for 33-256 tokens (fp16 weights): the
+// same K slices and fp32 partials as xproj_split_kernel, but a block stages its
+// 64 tokens' activations for the slice in LDS, one 128-wide group at a time
+// (double-buffered), and each of its four row waves takes RW 16-row tiles over
+// the slice (KS wave groups splitting each group's k-steps), so the
+// activations are read from L2 once per 64 RW rows instead of once per 16.
+constexpr int kWideRowBytes = 256 + 16;  // one token's staged group, padded
+
+template <int MT, int RW, int KS>
+__global__ __launch_bounds__(256 * KS) void xproj_wide_kernel(DenseArgs a, int kpw) {
+  // KS: wave groups that split each staged group's four k-steps between them
+  // (more waves per block where blocks are few), adding up at the end
+  constexpr int JS = 4 / KS;           // k-steps per wave and group
+  constexpr int NP = 4 / KS;           // staged pieces per thread and group
+  __shared__ __align__(16) char stage[2][64 * kWideRowBytes];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wt = wave & 3, ks = wave >> 2;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int N = a.N0 + a.N1 + a.N2;
+  const int64_t t0 = (int64_t)blockIdx.z * 64;
+  const int nsteps = (a.K + 31) / 32;
+  const int s_begin = blockIdx.y * 4 * kpw, s_end = min(nsteps, s_begin + 4 * kpw);
+  const int g_begin = s_begin / 4, g_end = (s_end + 3) / 4;  // 128-wide groups of the slice
+
+  const uint16_t* wrow[RW];
+  const uint16_t* wrowb[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int n = blockIdx.x * (64 * RW) + (wt * RW + r) * 16 + i16;
+    wrow[r] = wrowb[r] = nullptr;
+    if (n < a.N0) {
+      wrow[r] = a.w0 + (int64_t)n * a.K;
+      if (a.w0b) wrowb[r] = a.w0b + (int64_t)n * a.K;
+    } else if (n < a.N0 + a.N1) {
+      wrow[r] = a.w1 + (int64_t)(n - a.N0) * a.K;
+    } else if (n < N) {
+      wrow[r] = a.w2 + (int64_t)(n - a.N0 - a.N1) * a.K;
+    }
+  }
+
+  // staging roles: piece u = threadIdx.x + 256 KS p is token row u / 16,
+  // 16-byte chunk u % 16 of the group
+  const uint16_t* srow[NP];
+  int soff[NP], schunk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int u = threadIdx.x + 256 * KS * p;
+    const int64_t t = t0 + (u >> 4);
+    schunk[p] = u & 15;
+    srow[p] = t < a.T ? a.act + t * a.lda + 8 * schunk[p] : nullptr;
+    soff[p] = (u >> 4) * kWideRowBytes + schunk[p] * 16;
+  }
+  auto stage_load = [&](int g, u32x4 (&raw)[NP]) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int k = g * 128 + 8 * schunk[p];
+      raw[p] = (srow[p] && g < g_end && k < a.K) ? *(const u32x4*)(srow[p] + g * 128) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage_store = [&](const u32x4 (&raw)[NP], char* buf) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) *(u32x4*)(buf + soff[p]) = raw[p];
+  };
+
+  f32x4 acc[RW][MT];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 raw[NP];
+  stage_load(g_begin, raw);
+  stage_store(raw, stage[0]);
+  stage_load(g_begin + 1, raw);
+  __syncthreads();
+  for (int g = g_begin; g < g_end; ++g) {
+    // the wave's steps of the group, their weight loads in flight together
+    u32x4 wv[JS][RW], wb[JS][RW];
+#pragma unroll
+    for (int jj = 0; jj < JS; ++jj) {
+      const int st = 4 * g + ks * JS + jj;
+      const int kb = 32 * st + 8 * q;
+      const bool kin = st < s_end && kb < a.K;
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        wv[jj][r] = (wrow[r] && kin) ? *(const u32x4_a4*)(wrow[r] + kb) : u32x4{0u, 0u, 0u, 0u};
+        wb[jj][r] = (wrowb[r] && kin) ? *(const u32x4_a4*)(wrowb[r] + kb) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    const char* buf = stage[(g - g_begin) & 1];
+#pragma unroll
+    for (int jj = 0; jj < JS; ++jj) {
+      const int j = ks * JS + jj;
+      if (4 * g + j >= s_end) break;
+      u32x4 av[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) av[m] = *(const u32x4*)(buf + (16 * m + i16) * kWideRowBytes + (4 * j + q) * 16);
+#pragma unroll
+      for (int r = 0; r < RW; ++r) {
+        u32x4 hi, lo;
+        if (wrowb[r])
+          split_sum_f16x8(wv[jj][r], wb[jj][r], hi, lo);
+        else
+          split_f16x8(wv[jj][r], hi, lo);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          acc[r][m] = mfma16(av[m], hi, acc[r][m]);
+          acc[r][m] = mfma16(av[m], lo, acc[r][m]);
+        }
+      }
+    }
+    if (g + 1 < g_end) {
+      stage_store(raw, stage[(g + 1 - g_begin) & 1]);
+      stage_load(g + 2, raw);
+    }
+    __syncthreads();
+  }
+  // the other wave groups' sums meet the first's in shared memory, in group order
+  f32x4* red = (f32x4*)stage[0];  // [4 row waves][RW][MT][64 lanes]
+  for (int kk = 1; kk < KS; ++kk) {
+    if (ks == kk)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) red[((wt * RW + r) * MT + m) * 64 + lane] = acc[r][m];
+    __syncthreads();
+    if (ks == 0)
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[r][m] += red[((wt * RW + r) * MT + m) * 64 + lane];
+    __syncthreads();
+  }
+  if (ks > 0) return;
+  float* out = a.part + (int64_t)blockIdx.y * a.T * N;
+  // lane holds tokens t0 + 16m + 4q + j, row n of each tile
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int n = blockIdx.x * (64 * RW) + (wt * RW + r) * 16 + i16;
+    if (n >= N) continue;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + 16 * m + 4 * q + j;
+        if (t < a.T) out[t * N + n] = acc[r][m][j];
+      }
+  }
+}
+
 // Large batches take the LDS-tiled matrix-core kernels (moe_dense.hip).
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
   if (a.N2 && !(a.T <= kGroupMaxT && a.part)) return hipErrorInvalidValue;  // w2 rows: split path only
@@ -453,15 +602,25 @@ hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
     const XprojSplit sp = xproj_split(a.K);
     const dim3 grid((unsigned)((N + 15) / 16), (unsigned)sp.splits, (unsigned)((a.T + 63) / 64));
     const int mt = (int)std::min<int64_t>(4, (a.T + 15) / 16);
-    // two row tiles per block where many tokens meet many rows (the draft
-    // head's 2048-4096 rows at 33-256 tokens; measured at 64 tokens and 4096
-    // rows: 26.9 us against 30.3 with one tile and 32.0 with four); one elsewhere
+    // where many tokens meet many fp16 rows (the draft head's 2048-4096 rows
+    // at 33-256 tokens) the LDS-staged kernel; one 16-row tile per block elsewhere
     const bool tq = a.q0b || a.q1;
-    const int rt = (!tq && mt >= 3 && N >= kXprojWideRows) ? kXprojWideTiles : 1;
-    const dim3 g((unsigned)((N + 16 * rt - 1) / (16 * rt)), grid.y, grid.z);
-    if (rt > 1) {
-      if (mt == 3) xproj_split_kernel<3, kXprojWideTiles, false><<<g, 256, 0, stream>>>(a, sp.kpw);
-      else xproj_split_kernel<4, kXprojWideTiles, false><<<g, 256, 0, stream>>>(a, sp.kpw);
+    const dim3 g((unsigned)((N + 15) / 16), grid.y, grid.z);
+    if (!tq && mt >= 3 && N >= kXprojWideRows) {
+      // 64 rows per block, and eight waves (two per 16-row tile, splitting the
+      // k-steps) where that leaves fewer than four blocks per compute unit.
+      // Measured on the draft head at 64 tokens (fc1 4096 rows, 512 blocks):
+      // 128 rows and four waves per block 22.2 us, 64 rows and four waves
+      // 17.8, 64 rows and eight waves 17.0, sixteen waves 20.8
+      const dim3 gw((unsigned)((N + 63) / 64), grid.y, grid.z);
+      const bool ks2 = (int64_t)gw.x * gw.y * gw.z < 1024;
+      if (ks2) {
+        if (mt == 3) xproj_wide_kernel<3, 1, 2><<<gw, 512, 0, stream>>>(a, sp.kpw);
+        else xproj_wide_kernel<4, 1, 2><<<gw, 512, 0, stream>>>(a, sp.kpw);
+      } else {
+        if (mt == 3) xproj_wide_kernel<3, 1, 1><<<gw, 256, 0, stream>>>(a, sp.kpw);
+        else xproj_wide_kernel<4, 1, 1><<<gw, 256, 0, stream>>>(a, sp.kpw);
+      }
     } else if (tq) {
       if (mt == 1) xproj_split_kernel<1, 1, true><<<g, 256, 0, stream>>>(a, sp.kpw);
       else if (mt == 2) xproj_split_kernel<2, 1, true><<<g, 256, 0, stream>>>(a, sp.kpw);
