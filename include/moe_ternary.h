@@ -174,6 +174,9 @@ int32_t moe_ple_gather_q4_0(const uint8_t* d_table, int64_t n_rows, int32_t row_
  *   workspace   >= moe_lowrank_workspace_bytes(n_tokens, d, r), 256-byte aligned
  * The numerics are the block's correction: fp32 products on matrix cores, z =
  * A x rounded to bf16, y summed in fp32 as (B z) + y_in and rounded to bf16.
+ * With r >= 2048 and fp16 A, A x adds its K steps in another order from 33 to
+ * 256 tokens than below 33, so results can differ in their last bits between
+ * such batches (the block's own projection keeps one order for every batch).
  * d % 128 == 0, r % 8 == 0, r <= 4096.  Errors: MOE_E_SHAPE, MOE_E_ARG,
  * MOE_E_SPACE, MOE_E_DEVICE. */
 int64_t moe_lowrank_workspace_bytes(int64_t n_tokens, int32_t d, int32_t r);
@@ -193,7 +196,10 @@ int32_t moe_lowrank_apply(const uint16_t* x, const uint16_t* y_in, int64_t n_tok
  *   workspace    device, >= moe_draft_head_workspace_bytes(...), 256-byte aligned
  * h and m are multiples of 128 (h = 2048, m = 4096 is the card's 50 MB).
  * Products accumulate in fp32 on matrix cores (fp16 weights as exact bf16
- * pairs); gelu(W1 x + b1) and y are rounded to bf16.  n_tokens = 0 is a no-op.
+ * pairs); gelu(W1 x + b1) and y are rounded to bf16.  From 33 to 256 tokens a
+ * product of 2048 or more rows adds its K steps in another order than below 33
+ * tokens, so a token's y can differ in its last bits between such batches.
+ * n_tokens = 0 is a no-op.
  * Errors: MOE_E_SHAPE, MOE_E_ARG (NULL, misaligned), MOE_E_SPACE, MOE_E_DEVICE. */
 int64_t moe_draft_head_workspace_bytes(int64_t n_tokens, int32_t hidden, int32_t inner);
 int32_t moe_draft_head(const uint16_t* hidden, const uint16_t* emb, int64_t n_tokens, int32_t h, int32_t m,

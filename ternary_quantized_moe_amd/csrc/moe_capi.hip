@@ -436,6 +436,7 @@ int32_t moe_lowrank_apply(const uint16_t* x, const uint16_t* y_in, int64_t T, in
     xa.N1 = r;
     xa.z = z;
     xa.part = p.large ? nullptr : at<float>(ws, p.part);
+    xa.staged = true;
     xa.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
     hipError_t e = stage_mark(0, false, st);
     if (e == hipSuccess) e = moe::launch_xproj(xa, st);

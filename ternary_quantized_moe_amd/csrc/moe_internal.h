@@ -48,6 +48,10 @@ struct DenseArgs {
   // which reach the fp32 partials and nothing else
   const uint16_t* w2;
   int N2;
+  // the caller accepts xproj_wide_kernel for 33-256 tokens and 2048+ fp16 rows
+  // (w0 without w0b, or w1): its K-step order differs from the split kernel's,
+  // so a row's sums are no longer the same for every batch size
+  bool staged;
   // xproj epilogue
   float* logits;   // fp32 [T x N0]
   uint16_t* z;     // bf16 [T x N1]

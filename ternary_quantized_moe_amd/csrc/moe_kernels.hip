@@ -461,26 +461,18 @@ __global__ __launch_bounds__(256 * KS) void xproj_wide_kernel(DenseArgs a, int k
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wt = wave & 3, ks = wave >> 2;
   const int i16 = lane & 15, q = lane >> 4;
-  const int N = a.N0 + a.N1 + a.N2;
+  const int N = a.N0 + a.N1;
   const int64_t t0 = (int64_t)blockIdx.z * 64;
   const int nsteps = (a.K + 31) / 32;
   const int s_begin = blockIdx.y * 4 * kpw, s_end = min(nsteps, s_begin + 4 * kpw);
   const int g_begin = s_begin / 4, g_end = (s_end + 3) / 4;  // 128-wide groups of the slice
 
+  // rows [0, N0) of w0, then [N0, N) of w1 (no summed delta, no third segment)
   const uint16_t* wrow[RW];
-  const uint16_t* wrowb[RW];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     const int n = blockIdx.x * (64 * RW) + (wt * RW + r) * 16 + i16;
-    wrow[r] = wrowb[r] = nullptr;
-    if (n < a.N0) {
-      wrow[r] = a.w0 + (int64_t)n * a.K;
-      if (a.w0b) wrowb[r] = a.w0b + (int64_t)n * a.K;
-    } else if (n < a.N0 + a.N1) {
-      wrow[r] = a.w1 + (int64_t)(n - a.N0) * a.K;
-    } else if (n < N) {
-      wrow[r] = a.w2 + (int64_t)(n - a.N0 - a.N1) * a.K;
-    }
+    wrow[r] = n < a.N0 ? a.w0 + (int64_t)n * a.K : n < N ? a.w1 + (int64_t)(n - a.N0) * a.K : nullptr;
   }
 
   // staging roles: piece u = threadIdx.x + 256 KS p is token row u / 16,
@@ -520,17 +512,15 @@ __global__ __launch_bounds__(256 * KS) void xproj_wide_kernel(DenseArgs a, int k
   __syncthreads();
   for (int g = g_begin; g < g_end; ++g) {
     // the wave's steps of the group, their weight loads in flight together
-    u32x4 wv[JS][RW], wb[JS][RW];
+    u32x4 wv[JS][RW];
 #pragma unroll
     for (int jj = 0; jj < JS; ++jj) {
       const int st = 4 * g + ks * JS + jj;
       const int kb = 32 * st + 8 * q;
       const bool kin = st < s_end && kb < a.K;
 #pragma unroll
-      for (int r = 0; r < RW; ++r) {
+      for (int r = 0; r < RW; ++r)
         wv[jj][r] = (wrow[r] && kin) ? *(const u32x4_a4*)(wrow[r] + kb) : u32x4{0u, 0u, 0u, 0u};
-        wb[jj][r] = (wrowb[r] && kin) ? *(const u32x4_a4*)(wrowb[r] + kb) : u32x4{0u, 0u, 0u, 0u};
-      }
     }
     const char* buf = stage[(g - g_begin) & 1];
 #pragma unroll
@@ -543,10 +533,7 @@ __global__ __launch_bounds__(256 * KS) void xproj_wide_kernel(DenseArgs a, int k
 #pragma unroll
       for (int r = 0; r < RW; ++r) {
         u32x4 hi, lo;
-        if (wrowb[r])
-          split_sum_f16x8(wv[jj][r], wb[jj][r], hi, lo);
-        else
-          split_f16x8(wv[jj][r], hi, lo);
+        split_f16x8(wv[jj][r], hi, lo);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           acc[r][m] = mfma16(av[m], hi, acc[r][m]);
@@ -606,7 +593,7 @@ hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream) {
     // at 33-256 tokens) the LDS-staged kernel; one 16-row tile per block elsewhere
     const bool tq = a.q0b || a.q1;
     const dim3 g((unsigned)((N + 15) / 16), grid.y, grid.z);
-    if (!tq && mt >= 3 && N >= kXprojWideRows) {
+    if (a.staged && !tq && !a.w0b && !a.N2 && mt >= 3 && N >= kXprojWideRows) {
       // 64 rows per block, and eight waves (two per 16-row tile, splitting the
       // k-steps) where that leaves fewer than four blocks per compute unit.
       // Measured on the draft head at 64 tokens (fc1 4096 rows, 512 blocks):

@@ -109,6 +109,7 @@ hipError_t launch_head(const HeadArgs& a, char* ws, hipStream_t stream, void** s
     d.logits = part;  // the tiled path writes the whole fp32 product here
     d.wsplit = p.large ? ws + p.wsplit : nullptr;
     d.part = p.large ? nullptr : part;
+    d.staged = true;
     e = mark(2 * layer);
     if (e == hipSuccess) e = launch_xproj(d, stream);
     if (e == hipSuccess) e = mark(2 * layer + 1);

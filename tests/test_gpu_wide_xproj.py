@@ -1,9 +1,11 @@
-"""GPU tests of the LDS-staged x-projection (33-256 tokens, 2048 or more fp16
-rows), through the C ABI: a block whose correction rank makes the projection
-wide (router rows with the summed delta, then A's rows, a row tile straddling
-the two), and the stand-alone branch with a wide A.  The bar is the oracle
-within the block tolerance; block outputs are compared on tokens whose expert
-choice is decided (fp64 top-k margin above four times the fp32 logit bound)."""
+"""GPU tests of wide x-projections (33-256 tokens, 2048 or more rows), through
+the C ABI.  The stand-alone branch with a wide A takes the LDS-staged kernel;
+a block whose rank-2048 correction makes its projection wide (router rows with
+the summed delta, then A's rows, a row tile straddling the two) keeps the
+K-split kernel, so its logits stay the same with and without the correction
+rows (checked bit for bit).  The bar otherwise is the oracle within the block
+tolerance; block outputs are compared on tokens whose expert choice is decided
+(fp64 top-k margin above four times the fp32 logit bound)."""
 import sys
 
 import numpy as np
@@ -62,6 +64,21 @@ def test_wide_projection_block(T):
     m = row_metric(y.cpu().numpy().view(np.uint16), ref.y)
     say(f"  max row metric {m.max():.3e}")
     assert m.max() <= TOL
+
+
+def test_wide_block_zero_correction_is_bit_exact():
+    """Zero A and B of rank 2048 leave the block bit for bit as without them:
+    the 2068-row projection sums each logit as the 20-row one does."""
+    import ternary_quantized_moe_amd as tq
+    L = Layer(WIDE)
+    c = L.cfg
+    x_bits = L.gen.tokens(64, 4)
+    d = L.tensors(x_bits)
+    za, zb = torch.zeros_like(d["a"]), torch.zeros_like(d["b"])
+    y_z = tq.forward(d["x"], d["router"], d["delta"], L.device(), za, zb, c.top_k)
+    y_n = tq.forward(d["x"], d["router"], d["delta"], L.device(), None, None, c.top_k)
+    torch.cuda.synchronize()
+    assert torch.equal(y_z, y_n)
 
 
 @pytest.mark.parametrize("d,r,T", [(256, 2048, 64), (512, 4096, 33), (384, 2056, 100)])
