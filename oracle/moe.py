@@ -208,11 +208,17 @@ class Result:
 
 
 def forward(x_bits, router_bits, delta_bits, banks: Banks, a_bits, b_bits, top_k: int,
-            forced_idx: Optional[np.ndarray] = None, delta_factors=None) -> Result:
+            forced_idx: Optional[np.ndarray] = None, delta_factors=None, banks_subset=None) -> Result:
     """The block's forward pass over tokens x (bf16 bits [T, d]).  forced_idx, if
     given, replaces the oracle's own top-k choice (gate weights are still the
     softmax of the oracle's logits at those indices).  delta_factors, if given,
-    is (U, V) in fp16 bits, the router delta U V in place of delta_bits."""
+    is (U, V) in fp16 bits, the router delta U V in place of delta_bits.
+
+    banks_subset, if given, is a collection of bank numbers (routed 0..E-1,
+    shared E..E+S-1): y then holds only those banks' terms and no correction.
+    y is a sum of per-bank terms plus the correction, so the results over
+    disjoint subsets that cover every bank, plus correction(x, A, B), add up to
+    the whole block (up to the order of the float64 additions)."""
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
     E = banks.n_experts
@@ -231,17 +237,20 @@ def forward(x_bits, router_bits, delta_bits, banks: Banks, a_bits, b_bits, top_k
     w = gate_weights(logits, idx)
     counts, offsets, perm = grouping(idx, E)
 
+    wanted = (lambda e: True) if banks_subset is None else set(int(e) for e in banks_subset).__contains__
     y = np.zeros_like(x)
     for e in range(E):                        # routed experts, one at a time
-        if counts[e] == 0:
+        if counts[e] == 0 or not wanted(e):
             continue
         slots = perm[offsets[e]:offsets[e + 1]]
         toks, which = slots // top_k, slots % top_k
         o = expert_ffn(*banks.matrices(e), x[toks])
         y[toks] += w[toks, which][:, None] * o
     for s in range(banks.n_shared):           # always-on shared experts, weight 1
-        y += expert_ffn(*banks.matrices(E + s), x)
-    y += correction(x, a, b)
+        if wanted(E + s):
+            y += expert_ffn(*banks.matrices(E + s), x)
+    if banks_subset is None:
+        y += correction(x, a, b)
     return Result(y, logits, idx, w, counts, offsets, perm)
 
 

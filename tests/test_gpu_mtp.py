@@ -53,11 +53,19 @@ def test_draft_head_small(T):
     assert run(256, 512, T) <= TOL
 
 
-@pytest.mark.parametrize("T", [1, 33, 64, 300])
+@pytest.mark.parametrize("T", [1, 33, 64, 200, 300])
 def test_draft_head_card_size(T):
-    # from 33 tokens on, the 2048- and 4096-row products take two row tiles per block
+    # from 33 tokens on, the 2048- and 4096-row products take the LDS-staged
+    # kernel: eight waves per block while the grid has fewer than 1024 blocks,
+    # four waves beyond (fc1 at 200 tokens: 64 x 8 x 4 blocks)
     # h = 2048, m = 4096: 25.2 M fp16 weights, the card's 50 MB
     assert run(2048, 4096, T) <= TOL
+
+
+def test_draft_head_wide_inner_three_token_tiles():
+    # m = 8192 rows at 40 tokens: three token tiles and 128 x 8 blocks, the
+    # four-wave LDS-staged kernel with three token tiles
+    assert run(2048, 8192, 40) <= TOL
 
 
 def test_draft_head_without_biases():

@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 
 from layer_fixtures import Layer, logit_bound, row_metric
+from oracle_threads import forward_y
 from oracle import codec, moe as omoe
 from synthetic import CONFIGS, PQ2_0, PTQ1_0, LayerConfig
 
@@ -151,8 +152,39 @@ def sample_tokens(T, n, seed=0):
     return np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), n - 2, replace=False)]))
 
 
+def item_edge_tokens(counts, offsets, perm, T, k, n_shared, chunk=64, hot=5):
+    """Tokens where the large-batch expert kernels' work items begin and end.
+
+    A routed expert's work items are consecutive runs of `chunk` slots of its
+    segment of the permutation (the last one partial); a shared expert's are the
+    token ranges [chunk j, chunk (j + 1)).  Returned: for the `hot` experts with
+    the most slots, the first and last token of every item; for every other
+    expert with slots, its first and last token and the first token of its last
+    item; for a shared expert, tokens chunk j - 1 and chunk j for every j."""
+    counts = np.asarray(counts, np.int64)
+    offsets = np.asarray(offsets, np.int64)
+    pos = set()
+    for e in np.nonzero(counts)[0]:
+        o, n = int(offsets[e]), int(counts[e])
+        pos.update([o, o + n - 1, o + (n - 1) // chunk * chunk])
+    for e in np.argsort(-counts, kind="stable")[:hot]:
+        o, n = int(offsets[e]), int(counts[e])
+        for j in range(0, n, chunk):
+            pos.update([o + j, o + min(j + chunk, n) - 1])
+    toks = {int(perm[p]) // k for p in pos}
+    if n_shared:
+        for j in range(chunk, T, chunk):
+            toks.update([j - 1, j])
+    return np.array(sorted(toks), dtype=np.int64)
+
+
 @pytest.mark.parametrize("name,T", CASES)
 def test_forward_parity(name, T):
+    """Every token is compared up to 4096 tokens.  At 16384 tokens (Zipf-skewed
+    routing) the compared tokens are the edges of every work item of the five
+    hottest experts (the hottest holds about 37x the mean load), the first and
+    last token and last-item start of every expert, both sides of every shared
+    expert item boundary, and 256 random tokens."""
     tq = tq_mod()
     L = Layer(name)
     c = L.cfg
@@ -164,16 +196,18 @@ def test_forward_parity(name, T):
     r = tq.route(d["x"], d["router"], d["delta"], c.n_experts, c.top_k)
     y = tq.forward(d["x"], d["router"], d["delta"], banks, d["a"], d["b"], c.top_k)
     torch.cuda.synchronize()
-    n_sample = {"olmoe": 64, "a3b35": 12, "flashnext": 6, "skewed": 4}.get(name, 64)
-    if name == "flashnext" and T <= 8:
-        n_sample = T
-    toks = sample_tokens(T, n_sample)
+    if T <= 4096:
+        toks = np.arange(T)
+    else:
+        edges = item_edge_tokens(r["counts"].cpu().numpy(), r["offsets"].cpu().numpy(),
+                                 r["perm"].cpu().numpy(), T, c.top_k, c.n_shared)
+        toks = np.union1d(edges, sample_tokens(T, 256, seed=3))
+        assert len(toks) >= 512
     idx, undecided = check_routing(L, x_bits, r, toks)
-    say(f"  undecided tokens in sample: {undecided}/{len(toks)}")
-    ref = omoe.forward(x_bits[toks], L.router, L.delta, L.oracle_banks, L.corr_a, L.corr_b, c.top_k,
-                       forced_idx=idx[toks])
+    say(f"  {len(toks)} tokens compared, {undecided} undecided (routing forced to the GPU's choice)")
+    ref = forward_y(L, x_bits[toks], L.router, L.delta, L.corr_a, L.corr_b, c.top_k, idx[toks])
     y_bits = y.cpu().numpy().view(np.uint16)
-    m = row_metric(y_bits[toks], ref.y)
+    m = row_metric(y_bits[toks], ref)
     say(f"  max row metric {m.max():.3e}")
     assert m.max() <= TOL
 
@@ -242,11 +276,10 @@ def test_many_experts(T):
     r = tq.route(d["x"], d["router"], d["delta"], c.n_experts, c.top_k)
     y = tq.forward(d["x"], d["router"], d["delta"], L.device(), d["a"], d["b"], c.top_k)
     torch.cuda.synchronize()
-    toks = sample_tokens(T, 24)
+    toks = np.arange(T)
     idx, _ = check_routing(L, x_bits, r, toks)
-    ref = omoe.forward(x_bits[toks], L.router, L.delta, L.oracle_banks, L.corr_a, L.corr_b, c.top_k,
-                       forced_idx=idx[toks])
-    assert row_metric(y.cpu().numpy().view(np.uint16)[toks], ref.y).max() <= TOL
+    ref = forward_y(L, x_bits, L.router, L.delta, L.corr_a, L.corr_b, c.top_k, idx)
+    assert row_metric(y.cpu().numpy().view(np.uint16), ref).max() <= TOL
 
 
 def run_fwd(L, x_bits, k=None, use_delta=True, use_corr=True, corr_b=None, banks=None):

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 from layer_fixtures import Layer, row_metric
+from oracle_threads import forward_y
 from oracle import codec, moe as omoe
 from synthetic import CONFIGS, LayerGen
 
@@ -87,11 +88,13 @@ def test_ternary_delta_without_correction():
     assert np.array_equal(y_q, y_d)
 
 
-def test_ternary_corrections_against_the_oracle():
+@pytest.mark.parametrize("name,T", [("olmoe", 16), ("olmoe", 64), ("a3b35", 300)])
+def test_ternary_corrections_against_the_oracle(name, T):
+    """Every token of the batch (300 tokens take the large-batch kernels)."""
     import ternary_quantized_moe_amd as tq
-    L = Layer("olmoe")
+    L = Layer(name)
     c = L.cfg
-    T = 16
+    say(f"ternary corrections against the oracle {name} T={T}")
     x_bits, q, dense, y_q, _ = run_both(L, T)
     # the oracle decodes the containers the library packed with its own codec
     dec = {}
@@ -102,8 +105,8 @@ def test_ternary_corrections_against_the_oracle():
         assert np.array_equal(dec[k], dense[k])
     r = tq.route(dev16(x_bits), dev16(L.router), dev16(dec["delta"]), c.n_experts, c.top_k)
     idx = r["idx"].cpu().numpy()
-    ref = omoe.forward(x_bits, L.router, dec["delta"], L.oracle_banks, dec["a"], dec["b"], c.top_k, forced_idx=idx)
-    m = row_metric(y_q, ref.y)
+    ref = forward_y(L, x_bits, L.router, dec["delta"], dec["a"], dec["b"], c.top_k, idx)
+    m = row_metric(y_q, ref)
     say(f"  max row metric {m.max():.3e}")
     assert m.max() <= TOL
 

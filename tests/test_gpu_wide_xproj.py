@@ -81,7 +81,8 @@ def test_wide_block_zero_correction_is_bit_exact():
     assert torch.equal(y_z, y_n)
 
 
-@pytest.mark.parametrize("d,r,T", [(256, 2048, 64), (512, 4096, 33), (384, 2056, 100)])
+# (4096, 4096, 160): 64 x 8 x 3 blocks, the four-wave form of the LDS-staged kernel
+@pytest.mark.parametrize("d,r,T", [(256, 2048, 64), (512, 4096, 33), (384, 2056, 100), (4096, 4096, 160)])
 def test_wide_projection_branch(d, r, T):
     import ternary_quantized_moe_amd as tq
     rng = np.random.default_rng(d + r + T)

@@ -215,3 +215,33 @@ def test_skewed_config_has_hot_experts():
     hottest = int(np.argmax(load))
     assert g.zipf_ranks()[hottest] == 1
     assert g.formats()[hottest] == PQ2_0
+
+
+@pytest.mark.parametrize("cfg", [TINY, SMALL_SHARED])
+def test_bank_subsets_add_up_to_the_block(cfg):
+    """forward(..., banks_subset=P) over a partition P of the banks, plus the
+    correction, equals the brute-force block (every expert on every token, then
+    masked), which has no grouping and no subsets."""
+    L = build_layer(cfg, n_tokens=24, set_index=3)
+    ref = moe.forward_bruteforce(L["x"], L["wr"], L["dwr"], L["banks"], L["a"], L["b"], L["k"])
+    nb = cfg.n_banks
+    parts = [list(range(0, nb, 3)), list(range(1, nb, 3)), list(range(2, nb, 3))]
+    y = moe.correction(moe.bf16_to_f64(L["x"]), moe.f16_to_f64(L["a"]), moe.f16_to_f64(L["b"]))
+    for p in parts:
+        y = y + run(L, banks_subset=p).y
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-13)
+    # an empty subset contributes nothing and leaves out the correction
+    assert not run(L, banks_subset=[]).y.any()
+
+
+def test_threaded_oracle_equals_one_call():
+    """tests/oracle_threads.py splits the banks over threads; the sum equals one
+    serial oracle call."""
+    from layer_fixtures import Layer
+    from oracle_threads import forward_y
+    L = Layer(SMALL_SHARED)
+    c = L.cfg
+    x = L.gen.tokens(40, 5)
+    ref = moe.forward(x, L.router, L.delta, L.oracle_banks, L.corr_a, L.corr_b, c.top_k)
+    y = forward_y(L, x, L.router, L.delta, L.corr_a, L.corr_b, c.top_k, ref.idx, threads=4)
+    assert np.allclose(y, ref.y, rtol=1e-12, atol=1e-13)
