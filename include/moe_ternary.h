@@ -230,6 +230,11 @@ int32_t moe_untile_container(int32_t fmt, const uint8_t* src, int64_t rows, int6
  * expert kernels read each block with one 12-byte load that can run 2 bytes
  * past the block); the slack's content is ignored. */
 enum { MOE_BANK_SLACK = 16 };
+/* Block order of the containers in a moe_expert_banks.  The expert kernels read
+ * only the tile-major order; the field makes the caller state it, so banks
+ * straight from moe_pack (row-major) are refused with MOE_E_ARG instead of
+ * being read in the wrong order. */
+enum { MOE_BANKS_ROW_MAJOR = 1, MOE_BANKS_TILE_MAJOR = 2 };
 typedef struct moe_expert_banks {
   int32_t d_model;              /* d: multiple of 128                              */
   int32_t d_ff;                 /* f: multiple of 128                              */
@@ -241,6 +246,7 @@ typedef struct moe_expert_banks {
   const uint8_t* formats;       /* device uint8[E+S]: 142 or 143                   */
   const int64_t* offsets_host;  /* host copy of offsets (validation)               */
   const uint8_t* formats_host;  /* host copy of formats (validation, dispatch)     */
+  int32_t layout;               /* must be MOE_BANKS_TILE_MAJOR                    */
 } moe_expert_banks;
 
 /* Workspace bytes moe_ternary_forward needs for n_tokens tokens. */
@@ -324,6 +330,23 @@ int32_t moe_route(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t 
                   float* logits, int32_t* topk_idx, float* topk_w, int32_t* counts,
                   int32_t* offsets, int32_t* perm, void* workspace, int64_t workspace_bytes,
                   void* stream);
+
+/* The routing half of moe_ternary_forward_factored, with every intermediate
+ * exported: the router delta as fp16 factors U [E x delta_rank] (16-byte
+ * aligned) and V [delta_rank x d_model] (4-byte aligned), logits W_r x + U (V x)
+ * (FlashNext card, "Weight Representation": rank-512 F16 factors for the
+ * router deltas).  Outputs and their layouts are moe_route's; the kernels and
+ * their summation order are those moe_ternary_forward_factored runs, so the
+ * exported choice is the one the forward pass makes for the same tokens.  The
+ * workspace is moe_route_workspace_bytes_factored's.  Errors: moe_route's, and
+ * MOE_E_SHAPE for a delta_rank that is not a positive multiple of 8 up to 1024. */
+int64_t moe_route_workspace_bytes_factored(int64_t n_tokens, int32_t d_model, int32_t n_experts,
+                                           int32_t top_k, int32_t delta_rank);
+int32_t moe_route_factored(const uint16_t* x, int64_t n_tokens, int32_t d_model, int32_t n_experts,
+                           const uint16_t* router, const uint16_t* delta_U, const uint16_t* delta_V,
+                           int32_t delta_rank, int32_t top_k, float* logits, int32_t* topk_idx,
+                           float* topk_w, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Measurement hook.  With events != NULL (n_events >= 2 * MOE_N_STAGES
  * hipEvent_t handles created by the caller), every later moe_ternary_forward

@@ -29,6 +29,7 @@ EXPORTS = [
     "moe_draft_head", "moe_lowrank_workspace_bytes", "moe_lowrank_apply",
     "moe_workspace_bytes_factored", "moe_ternary_forward_factored",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
+    "moe_route_workspace_bytes_factored", "moe_route_factored",
     "moe_set_stage_events", "moe_last_error",
 ]
 N_STAGES = 5
@@ -49,7 +50,11 @@ class ExpertBanksC(ctypes.Structure):
         ("banks", ctypes.c_void_p), ("banks_bytes", ctypes.c_int64),
         ("offsets", ctypes.c_void_p), ("formats", ctypes.c_void_p),
         ("offsets_host", ctypes.c_void_p), ("formats_host", ctypes.c_void_p),
+        ("layout", ctypes.c_int32),
     ]
+
+
+BANKS_ROW_MAJOR, BANKS_TILE_MAJOR = 1, 2
 
 
 _lib = None
@@ -87,6 +92,9 @@ def lib():
                                           i32, vp, vp, i64, vp]),
             "moe_route_workspace_bytes": (i64, [i64, i32, i32, i32]),
             "moe_route": (i32, [vp, i64, i32, i32, vp, vp, i32, vp, vp, vp, vp, vp, vp, vp, i64, vp]),
+            "moe_route_workspace_bytes_factored": (i64, [i64, i32, i32, i32, i32]),
+            "moe_route_factored": (i32, [vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64,
+                                         vp]),
             "moe_set_stage_events": (i32, [ctypes.POINTER(ctypes.c_void_p), i32]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
@@ -224,7 +232,9 @@ def ple_gather(d_table, n_rows: int, row_len: int, d_idx, out=None, stream=None)
 class ExpertBanks:
     """One layer's expert containers in device memory plus the host copies the
     library validates against.  `data` is the concatenation of every bank's
-    [gate | up | down] containers; bank e starts at offsets[e]."""
+    [gate | up | down] containers, each in the tile-major block order of
+    tile_container (layers.build_banks writes that order); bank e starts at
+    offsets[e]."""
 
     def __init__(self, data: np.ndarray, offsets: np.ndarray, formats: np.ndarray, d_model: int,
                  d_ff: int, n_experts: int, n_shared: int, device="cuda"):
@@ -238,7 +248,7 @@ class ExpertBanks:
         self.nbytes = int(data.size)
         self._c = ExpertBanksC(d_model, d_ff, n_experts, n_shared, self.data.data_ptr(), self.nbytes,
                                self.offsets.data_ptr(), self.formats.data_ptr(),
-                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data)
+                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data, BANKS_TILE_MAJOR)
 
     @classmethod
     def from_tensors(cls, data_dev, offsets_host, formats_host, d_model, d_ff, n_experts, n_shared):
@@ -254,7 +264,7 @@ class ExpertBanks:
         self.nbytes = int(data_dev.numel())
         self._c = ExpertBanksC(d_model, d_ff, n_experts, n_shared, data_dev.data_ptr(), self.nbytes,
                                self.offsets.data_ptr(), self.formats.data_ptr(),
-                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data)
+                               self.offsets_host.ctypes.data, self.formats_host.ctypes.data, BANKS_TILE_MAJOR)
         return self
 
     @property
@@ -374,6 +384,38 @@ def lowrank_apply(x, y_in, a, b, rank: int, a_q=None, b_q=None, y=None, workspac
     _check(lib().moe_lowrank_apply(_dev_ptr(x), _dev_ptr(y_in), T, d, _dev_ptr(a), _dev_ptr(a_q), _dev_ptr(b),
                                    _dev_ptr(b_q), rank, _dev_ptr(y), wp, wn, _stream(stream)))
     return y
+
+
+def _route_outputs(T, n_experts, top_k, dev):
+    import torch
+    return dict(
+        logits=torch.empty((T, n_experts), dtype=torch.float32, device=dev),
+        idx=torch.empty((T, top_k), dtype=torch.int32, device=dev),
+        w=torch.empty((T, top_k), dtype=torch.float32, device=dev),
+        counts=torch.empty(n_experts, dtype=torch.int32, device=dev),
+        offsets=torch.empty(n_experts + 1, dtype=torch.int32, device=dev),
+        perm=torch.empty(max(T * top_k, 1), dtype=torch.int32, device=dev),
+    )
+
+
+def route_factored(x, router, delta_u, delta_v, n_experts: int, top_k: int, workspace=None, stream=None):
+    """Routing half of forward_factored (router delta as fp16 factors U [E, rd],
+    V [rd, d]); returns the same dict as route()."""
+    T, d = x.shape
+    rd = delta_u.shape[1]
+    out = _route_outputs(T, n_experts, top_k, x.device)
+    if workspace is None:
+        need = lib().moe_route_workspace_bytes_factored(T, d, n_experts, top_k, rd)
+        if need < 0:
+            raise MoeError(-1, "invalid arguments for the routing workspace size")
+        workspace = alloc_workspace(need, x.device)
+    wp, wn = _aligned(workspace)
+    _check(lib().moe_route_factored(_dev_ptr(x), T, d, n_experts, _dev_ptr(router), _dev_ptr(delta_u),
+                                    _dev_ptr(delta_v), rd, top_k, _dev_ptr(out["logits"]), _dev_ptr(out["idx"]),
+                                    _dev_ptr(out["w"]), _dev_ptr(out["counts"]), _dev_ptr(out["offsets"]),
+                                    _dev_ptr(out["perm"]), wp, wn, _stream(stream)))
+    out["perm"] = out["perm"][: T * top_k]
+    return out
 
 
 def route(x, router, router_delta, n_experts: int, top_k: int, workspace=None, stream=None):

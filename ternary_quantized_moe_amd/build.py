@@ -12,7 +12,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_ternary.so")
-SOURCES = ["moe_capi.hip", "moe_kernels.hip", "moe_experts.hip", "moe_dense.hip", "moe_quant.hip", "moe_ple.hip", "moe_mtp.hip", "moe_router_delta.hip"]
+OBJ = os.path.join(PKG, "_build")
+SOURCES = ["host_codec.cpp", "moe_capi.hip", "moe_kernels.hip", "moe_experts.hip", "moe_dense.hip", "moe_quant.hip", "moe_ple.hip", "moe_mtp.hip", "moe_router_delta.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -29,20 +30,34 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = True) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
     noise = "is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln and ln.strip()]
+    if res.returncode != 0:
+        sys.stderr.write("\n".join(msgs) + "\n")
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd[-3:])}")
     if msgs and verbose:
         sys.stderr.write("\n".join(msgs) + "\n")
+
+
+def build(verbose: bool = True, jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel), then link the library."""
+    from concurrent.futures import ThreadPoolExecutor
+    os.makedirs(OBJ, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs, cmds = [], []
+    for s in SOURCES:
+        obj = os.path.join(OBJ, os.path.splitext(s)[0] + ".o")
+        objs.append(obj)
+        cmds.append([HIPCC, *compile_flags, "-c", os.path.join(CSRC, s), "-o", obj])
+    n = jobs or min(len(cmds), os.cpu_count() or 1, 16)
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

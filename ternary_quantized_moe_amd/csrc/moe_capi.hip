@@ -12,12 +12,12 @@
 #include <string>
 
 #include "moe_ternary.h"
+#include "host_error.h"
 #include "moe_internal.h"
 #include "router_delta.h"
 
 namespace {
 
-thread_local std::string g_err;
 thread_local void** g_stage_events = nullptr;
 
 // Record the stage's start (end=false) or end event if measurement is on.
@@ -27,29 +27,10 @@ hipError_t stage_mark(int stage, bool end, hipStream_t st) {
   return ev ? hipEventRecord(ev, st) : hipSuccess;
 }
 
-int32_t fail(int32_t code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  g_err = buf;
-  return code;
-}
-
-int32_t ok() {
-  g_err.clear();
-  return MOE_OK;
-}
-
-bool known_fmt(int32_t fmt) { return fmt == MOE_PQ2_0 || fmt == MOE_PTQ1_0; }
-
-int32_t bad_fmt(int32_t fmt) {
-  return fail(MOE_E_FORMAT, "unknown container id %d; valid ids are 142 (PQ2_0) and 143 (PTQ1_0)",
-              (int)fmt);
-}
-
-bool finite_f16(uint16_t h) { return (h & 0x7C00u) != 0x7C00u; }
+using moe::bad_fmt;
+using moe::fail;
+using moe::known_fmt;
+using moe::ok;
 
 int32_t device_fail(hipError_t e, const char* what) {
   return fail(MOE_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
@@ -141,6 +122,13 @@ int32_t check_banks(const moe_expert_banks* b) {
     return fail(MOE_E_SHAPE, "n_experts must be in [1, %d] (got %d)", moe::kMaxExperts, b->n_experts);
   if (!b->banks || !b->offsets || !b->formats || !b->formats_host || !b->offsets_host)
     return fail(MOE_E_ARG, "expert_banks has a NULL pointer");
+  if (b->layout == MOE_BANKS_ROW_MAJOR)
+    return fail(MOE_E_ARG,
+                "expert_banks.layout is MOE_BANKS_ROW_MAJOR (moe_pack's block order); reorder each container "
+                "with moe_tile_container and set layout = MOE_BANKS_TILE_MAJOR");
+  if (b->layout != MOE_BANKS_TILE_MAJOR)
+    return fail(MOE_E_ARG, "expert_banks.layout is %d; it must be MOE_BANKS_TILE_MAJOR (%d), the block order of "
+                "moe_tile_container", (int)b->layout, (int)MOE_BANKS_TILE_MAJOR);
   const int nb = b->n_experts + b->n_shared;
   const int64_t nblocks = 3 * (int64_t)b->d_ff * b->d_model / 128;
   for (int e = 0; e < nb; ++e) {
@@ -163,8 +151,6 @@ int32_t check_banks(const moe_expert_banks* b) {
 
 extern "C" {
 
-const char* moe_last_error(void) { return g_err.c_str(); }
-
 int32_t moe_set_stage_events(void** events, int32_t n_events) {
   if (events == nullptr || n_events == 0) {
     g_stage_events = nullptr;
@@ -174,155 +160,6 @@ int32_t moe_set_stage_events(void** events, int32_t n_events) {
     return fail(MOE_E_ARG, "need %d events, got %d", 2 * MOE_N_STAGES, (int)n_events);
   g_stage_events = events;
   return ok();
-}
-
-int64_t moe_block_bytes(int32_t fmt) {
-  if (fmt == MOE_PQ2_0) return 34;
-  if (fmt == MOE_PTQ1_0) return 28;
-  return -1;
-}
-
-int64_t moe_packed_bytes(int32_t fmt, int64_t n) {
-  if (!known_fmt(fmt) || n < 0 || n % 128) return -1;
-  return n / 128 * moe_block_bytes(fmt);
-}
-
-int32_t moe_pack(int32_t fmt, const int8_t* trits, const uint16_t* scales, int64_t n, uint8_t* dst,
-                 int64_t dst_bytes) {
-  try {
-    if (!known_fmt(fmt)) return bad_fmt(fmt);
-    if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
-    if (n > 0 && (!trits || !scales || !dst)) return fail(MOE_E_ARG, "NULL pointer");
-    const int64_t need = moe_packed_bytes(fmt, n);
-    if (dst_bytes < need)
-      return fail(MOE_E_SPACE, "dst holds %lld bytes, %lld needed", (long long)dst_bytes, (long long)need);
-    const int64_t nb = n / 128;
-    for (int64_t b = 0; b < nb; ++b)
-      if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
-    for (int64_t i = 0; i < n; ++i)
-      if (trits[i] < -1 || trits[i] > 1)
-        return fail(MOE_E_ARG, "weight %lld is %d, not in {-1, 0, +1}", (long long)i, (int)trits[i]);
-    if (fmt == MOE_PQ2_0) {
-      for (int64_t b = 0; b < nb; ++b) {
-        const int8_t* t = trits + b * 128;
-        uint8_t* o = dst + b * 34;
-        for (int j = 0; j < 32; ++j) {
-          uint32_t v = 0;
-          for (int i = 0; i < 4; ++i) v |= (uint32_t)(t[4 * j + i] & 3) << (2 * i);  // 0->00, 1->01, -1->11
-          o[j] = (uint8_t)v;
-        }
-        o[32] = (uint8_t)(scales[b] & 0xFF);
-        o[33] = (uint8_t)(scales[b] >> 8);
-      }
-    } else {
-      for (int64_t b = 0; b < nb; ++b) {
-        const int8_t* t = trits + b * 128;
-        uint8_t* o = dst + b * 28;
-        auto digit = [](int8_t v) { return v < 0 ? 2u : (uint32_t)v; };
-        for (int j = 0; j < 24; ++j) {
-          uint32_t v = 0, p = 1;
-          for (int i = 0; i < 5; ++i, p *= 3) v += digit(t[5 * j + i]) * p;
-          o[j] = (uint8_t)v;
-        }
-        for (int m = 0; m < 2; ++m) {
-          uint32_t v = 0, p = 1;
-          for (int i = 0; i < 4; ++i, p *= 3) v += digit(t[120 + 4 * m + i]) * p;
-          o[24 + m] = (uint8_t)v;
-        }
-        o[26] = (uint8_t)(scales[b] & 0xFF);
-        o[27] = (uint8_t)(scales[b] >> 8);
-      }
-    }
-    return ok();
-  } catch (...) {
-    return fail(MOE_E_ARG, "internal error in moe_pack");
-  }
-}
-
-int32_t moe_unpack(int32_t fmt, const uint8_t* src, int64_t src_bytes, int8_t* trits, uint16_t* scales,
-                   int64_t n) {
-  try {
-    if (!known_fmt(fmt)) return bad_fmt(fmt);
-    if (n < 0 || n % 128) return fail(MOE_E_SHAPE, "weight count %lld is not a multiple of 128", (long long)n);
-    if (n > 0 && (!trits || !scales || !src)) return fail(MOE_E_ARG, "NULL pointer");
-    const int64_t need = moe_packed_bytes(fmt, n);
-    if (src_bytes < need)
-      return fail(MOE_E_SPACE, "container holds %lld bytes, %lld needed", (long long)src_bytes, (long long)need);
-    const int64_t nb = n / 128;
-    if (fmt == MOE_PQ2_0) {
-      for (int64_t b = 0; b < nb; ++b) {
-        const uint8_t* blk = src + b * 34;
-        for (int j = 0; j < 32; ++j) {
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t c = (blk[j] >> (2 * i)) & 3u;
-            if (c == 2)
-              return fail(MOE_E_CODE, "invalid 2-bit code 10 in group %lld, byte %d", (long long)b, j);
-            trits[b * 128 + 4 * j + i] = c == 3 ? -1 : (int8_t)c;
-          }
-        }
-        scales[b] = (uint16_t)(blk[32] | (blk[33] << 8));
-        if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
-      }
-    } else {
-      for (int64_t b = 0; b < nb; ++b) {
-        const uint8_t* blk = src + b * 28;
-        for (int j = 0; j < 26; ++j) {
-          const int nd = j < 24 ? 5 : 4;
-          const uint32_t lim = j < 24 ? 243u : 81u;
-          if (blk[j] >= lim)
-            return fail(MOE_E_CODE, "base-3 %s byte %d > %u in group %lld, byte %d", j < 24 ? "data" : "tail",
-                        (int)blk[j], lim - 1, (long long)b, j);
-          uint32_t v = blk[j];
-          const int base = j < 24 ? 5 * j : 120 + 4 * (j - 24);
-          for (int i = 0; i < nd; ++i) {
-            const uint32_t dgt = v % 3;
-            v /= 3;
-            trits[b * 128 + base + i] = dgt == 2 ? -1 : (int8_t)dgt;
-          }
-        }
-        scales[b] = (uint16_t)(blk[26] | (blk[27] << 8));
-        if (!finite_f16(scales[b])) return fail(MOE_E_NONFINITE, "non-finite fp16 scale in group %lld", (long long)b);
-      }
-    }
-    return ok();
-  } catch (...) {
-    return fail(MOE_E_ARG, "internal error in moe_unpack");
-  }
-}
-
-// Block (row n, group g) of a [rows x cols] container: row-major index n G + g,
-// tile-major index ((n / 16) G + g) 16 + n % 16, with G = cols / 128.
-static int32_t retile(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
-                      int64_t dst_bytes, bool to_tiles) {
-  try {
-    if (!known_fmt(fmt)) return bad_fmt(fmt);
-    if (rows < 0 || rows % 16 || cols < 0 || cols % 128)
-      return fail(MOE_E_SHAPE, "a %lld x %lld container needs rows %% 16 == 0 and cols %% 128 == 0",
-                  (long long)rows, (long long)cols);
-    if (rows > 0 && cols > 0 && (!src || !dst)) return fail(MOE_E_ARG, "NULL pointer");
-    const int64_t bb = moe_block_bytes(fmt), G = cols / 128, bytes = rows * G * bb;
-    if (dst_bytes < bytes)
-      return fail(MOE_E_SPACE, "destination holds %lld bytes, %lld needed", (long long)dst_bytes, (long long)bytes);
-    if (bytes > 0 && src < dst + bytes && dst < src + bytes) return fail(MOE_E_ARG, "src and dst overlap");
-    for (int64_t n = 0; n < rows; ++n)
-      for (int64_t g = 0; g < G; ++g) {
-        const int64_t plain = n * G + g, tiled = ((n / 16) * G + g) * 16 + n % 16;
-        std::memcpy(dst + (to_tiles ? tiled : plain) * bb, src + (to_tiles ? plain : tiled) * bb, (size_t)bb);
-      }
-    return ok();
-  } catch (...) {
-    return fail(MOE_E_ARG, "internal error in the container reorder");
-  }
-}
-
-int32_t moe_tile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
-                           int64_t dst_bytes) {
-  return retile(fmt, src, rows, cols, dst, dst_bytes, true);
-}
-
-int32_t moe_untile_container(int32_t fmt, const uint8_t* src, int64_t rows, int64_t cols, uint8_t* dst,
-                             int64_t dst_bytes) {
-  return retile(fmt, src, rows, cols, dst, dst_bytes, false);
 }
 
 int32_t moe_unpack_device(int32_t fmt, const uint8_t* d_src, int64_t n, int8_t* d_trits, uint16_t* d_scales,
@@ -610,6 +447,40 @@ int32_t moe_route(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint
     return ok();
   } catch (...) {
     return fail(MOE_E_ARG, "internal error in moe_route");
+  }
+}
+
+int64_t moe_route_workspace_bytes_factored(int64_t n_tokens, int32_t d_model, int32_t n_experts, int32_t top_k,
+                                           int32_t delta_rank) {
+  if (n_tokens < 0 || n_experts < 1 || top_k < 1 || delta_rank < 1) return -1;
+  return make_plan(n_tokens, d_model, n_experts, 0, 128, top_k, 0, delta_rank).route_end;
+}
+
+int32_t moe_route_factored(const uint16_t* x, int64_t T, int32_t d, int32_t E, const uint16_t* router,
+                           const uint16_t* delta_U, const uint16_t* delta_V, int32_t rd, int32_t k, float* logits,
+                           int32_t* idx, float* w, int32_t* counts, int32_t* offsets, int32_t* perm, void* ws,
+                           int64_t ws_bytes, void* stream) {
+  try {
+    int32_t rc = check_dims(T, d, E, k);
+    if (rc) return rc;
+    if (rd <= 0 || rd % 8 || rd > moe::kDeltaMaxRank)
+      return fail(MOE_E_SHAPE, "delta_rank must be a positive multiple of 8, at most %d (got %d)",
+                  moe::kDeltaMaxRank, (int)rd);
+    if (T == 0) return ok();
+    if (!x || !router || !delta_U || !delta_V || !logits || !idx || !w || !counts || !offsets || !perm || !ws)
+      return fail(MOE_E_ARG, "NULL pointer");
+    if ((uintptr_t)ws % kAlign || (uintptr_t)x % 16) return fail(MOE_E_ARG, "workspace must be 256-byte and x 16-byte aligned");
+    if ((uintptr_t)delta_U % 16 || (uintptr_t)delta_V % 4)
+      return fail(MOE_E_ARG, "delta_U must be 16-byte and delta_V 4-byte aligned");
+    const Plan p = make_plan(T, d, E, 0, 128, k, 0, rd);
+    if (ws_bytes < p.route_end)
+      return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.route_end);
+    rc = route_impl(x, T, d, E, 0, router, nullptr, nullptr, nullptr, nullptr, 0, k, p, ws, (hipStream_t)stream,
+                    logits, idx, w, counts, offsets, perm, delta_U, delta_V);
+    if (rc) return rc;
+    return ok();
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_route_factored");
   }
 }
 

@@ -111,13 +111,13 @@ def test_codec_error_codes():
     assert ei.value.name == "MOE_E_NONFINITE"
 
 
-def _fake_banks(d=256, f=128, E=8, S=0, fmts=None, offsets=None, nbytes=None):
+def _fake_banks(d=256, f=128, E=8, S=0, fmts=None, offsets=None, nbytes=None, layout=binding.BANKS_TILE_MAJOR):
     fmts = np.full(E + S, PQ2_0, np.uint8) if fmts is None else np.asarray(fmts, np.uint8)
     size = 3 * d * f // 128 * 34
     offsets = np.arange(E + S, dtype=np.int64) * size if offsets is None else np.asarray(offsets, np.int64)
     keep = (fmts, offsets)
     c = binding.ExpertBanksC(d, f, E, S, 0x1000, nbytes if nbytes is not None else size * (E + S) + 16, 0x2000,
-                             0x3000, offsets.ctypes.data, fmts.ctypes.data)
+                             0x3000, offsets.ctypes.data, fmts.ctypes.data, layout)
     return c, keep
 
 
@@ -154,6 +154,18 @@ def test_forward_validation_happens_before_launch():
     assert _forward_rc(c7) == -1 and "multiple of 16" in L.moe_last_error().decode()
     assert L.moe_workspace_bytes(ctypes.byref(c), 16, 2, 16) > 0
     assert L.moe_workspace_bytes(None, 16, 2, 16) == -1
+
+
+def test_banks_must_declare_the_tile_major_order():
+    """Banks in moe_pack's row-major block order, or with no declared order,
+    are refused before any launch."""
+    L = tq.lib()
+    c, keep = _fake_banks(layout=binding.BANKS_ROW_MAJOR)
+    assert _forward_rc(c) == -1 and "moe_tile_container" in L.moe_last_error().decode()
+    c, keep = _fake_banks(layout=0)
+    assert _forward_rc(c) == -1 and "MOE_BANKS_TILE_MAJOR" in L.moe_last_error().decode()
+    c, keep = _fake_banks()
+    assert _forward_rc(c, T=0) == 0
 
 
 
@@ -241,6 +253,22 @@ def test_route_validation():
     assert L.moe_route(0x1000, 0, 256, 8, 0x2000, None, 2, 1, 1, 1, 1, 1, 1, 0x4000, 0, None) == 0
     assert L.moe_unpack_device(99, 1, 128, 1, 1, None) == -2
     assert L.moe_unpack_device(142, 1, 100, 1, 1, None) == -3
+
+
+def test_route_factored_validation():
+    """moe_route_factored checks on the host, before any launch."""
+    L = tq.lib()
+
+    def rc(T=4, d=256, E=8, U=0x50000, V=0x60000, rd=64, k=2, ws_bytes=1 << 30):
+        return L.moe_route_factored(0x1000, T, d, E, 0x2000, U, V, rd, k, 1, 1, 1, 1, 1, 1, 0x4000, ws_bytes, None)
+    assert rc(d=100) == -3 and rc(k=9) == -3
+    assert rc(rd=12) == -3 and rc(rd=0) == -3 and rc(rd=2048) == -3
+    assert rc(U=None) == -1 and rc(V=None) == -1
+    assert rc(U=0x50008) == -1 and rc(V=0x60002) == -1
+    assert rc(ws_bytes=16) == -6
+    assert rc(T=0) == 0
+    assert L.moe_route_workspace_bytes_factored(16, 256, 8, 2, 64) > L.moe_route_workspace_bytes(16, 256, 8, 2)
+    assert L.moe_route_workspace_bytes_factored(16, 256, 8, 2, 0) == -1
 
 
 def test_quantize_validation():
