@@ -270,6 +270,27 @@ int32_t moe_ternary_forward(const uint16_t* x, int64_t n_tokens, const uint16_t*
                             int32_t top_k, uint16_t* y, void* workspace, int64_t workspace_bytes,
                             void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward pass as moe_ternary_forward, with its workspace taken from a
+ * library-owned device array of MOE_NOALLOC_SCRATCH_BYTES bytes (one per GPU,
+ * loaded with the library and held until the process ends) instead of a
+ * caller buffer.  The call allocates nothing.  The caller still passes every
+ * input and y, with moe_ternary_forward's layouts; results equal
+ * moe_ternary_forward's bit for bit.  A batch whose moe_workspace_bytes exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES returns MOE_E_SPACE before any launch (decode
+ * batches of up to 256 tokens fit at every layer shape of the releases).  All
+ * calls on one GPU share its array and nothing in it needs clearing between
+ * calls (every byte a call reads it wrote first), so calls that overlap on one
+ * GPU (concurrent streams, or threads) race; serialise them.  Errors: those of
+ * moe_ternary_forward, MOE_E_SPACE as above, MOE_E_DEVICE if the array's device
+ * address cannot be resolved. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int32_t moe_ternary_forward_noalloc(const uint16_t* x, int64_t n_tokens, const uint16_t* router,
+                                    const uint16_t* router_delta, const moe_expert_banks* banks,
+                                    const uint16_t* corr_A, const uint16_t* corr_B, int32_t corr_rank,
+                                    int32_t top_k, uint16_t* y, void* stream);
+
 /* The same forward pass with the router delta and the correction stored as
  * ternary PQ2_0 containers, the way the 35B-A3B release ships them (Scion-
  * 35B-A3B card, "Weight Representation" and "Shipped Components": the

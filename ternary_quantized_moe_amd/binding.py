@@ -29,7 +29,7 @@ EXPORTS = [
     "moe_draft_head", "moe_lowrank_workspace_bytes", "moe_lowrank_apply",
     "moe_workspace_bytes_factored", "moe_ternary_forward_factored",
     "moe_tile_container", "moe_untile_container", "moe_workspace_bytes", "moe_ternary_forward", "moe_route_workspace_bytes", "moe_route",
-    "moe_route_workspace_bytes_factored", "moe_route_factored",
+    "moe_route_workspace_bytes_factored", "moe_route_factored", "moe_ternary_forward_noalloc",
     "moe_set_stage_events", "moe_last_error",
 ]
 N_STAGES = 5
@@ -95,6 +95,8 @@ def lib():
             "moe_route_workspace_bytes_factored": (i64, [i64, i32, i32, i32, i32]),
             "moe_route_factored": (i32, [vp, i64, i32, i32, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, i64,
                                          vp]),
+            "moe_ternary_forward_noalloc": (i32, [vp, i64, vp, vp, ctypes.POINTER(ExpertBanksC), vp, vp, i32, i32,
+                                                  vp, vp]),
             "moe_set_stage_events": (i32, [ctypes.POINTER(ctypes.c_void_p), i32]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
@@ -304,6 +306,21 @@ def forward(x, router, router_delta, banks: ExpertBanks, corr_a, corr_b, top_k: 
     _check(lib().moe_ternary_forward(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta), banks.c,
                                      _dev_ptr(corr_a), _dev_ptr(corr_b), r, top_k, _dev_ptr(y), wp, wn,
                                      _stream(stream)))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def forward_noalloc(x, router, router_delta, banks: ExpertBanks, corr_a, corr_b, top_k: int, y, stream=None):
+    """forward() with the library's own scratch as workspace (nothing is
+    allocated, by the library or here: the caller passes y).  Calls that overlap
+    on one GPU share that scratch and race."""
+    T = x.shape[0]
+    r = 0 if corr_a is None else corr_a.shape[0]
+    _check(lib().moe_ternary_forward_noalloc(_dev_ptr(x), T, _dev_ptr(router), _dev_ptr(router_delta), banks.c,
+                                             _dev_ptr(corr_a), _dev_ptr(corr_b), r, top_k, _dev_ptr(y),
+                                             _stream(stream)))
     return y
 
 

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "moe_ternary.h"
@@ -620,6 +621,72 @@ int32_t moe_ternary_forward_q(const uint16_t* x, int64_t T, const uint16_t* rout
                         ws_bytes, stream);
   } catch (...) {
     return fail(MOE_E_ARG, "internal error in moe_ternary_forward_q");
+  }
+}
+
+// ------------------------------------------------------- no-allocation forward
+// The workspace of moe_ternary_forward_noalloc: one array per device, loaded
+// with the library's code object and held until the process ends.  In host
+// code the name `scratch` is only a stand-in for the symbol: its device address
+// comes from hipGetSymbolAddress, taken once per device on the first call made
+// with that device current, and only that address reaches a kernel.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, or NULL after setting the error.
+void* device_scratch() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    device_fail(e, "hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(MOE_E_DEVICE, "device %d is beyond the %d devices the scratch table covers", dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      device_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+int32_t moe_ternary_forward_noalloc(const uint16_t* x, int64_t T, const uint16_t* router, const uint16_t* delta,
+                                    const moe_expert_banks* banks, const uint16_t* corr_A, const uint16_t* corr_B,
+                                    int32_t r, int32_t k, uint16_t* y, void* stream) {
+  try {
+    int32_t rc = check_banks(banks);
+    if (rc) return rc;
+    rc = check_dims(T, banks->d_model, banks->n_experts, k);
+    if (rc) return rc;
+    if (r < 0) return fail(MOE_E_ARG, "corr_rank must be >= 0 (got %d)", r);
+    const int64_t need = make_plan(T, banks->d_model, banks->n_experts, banks->n_shared, banks->d_ff, k,
+                                   (corr_A || corr_B) ? r : 0)
+                             .total;
+    if (need > (int64_t)MOE_NOALLOC_SCRATCH_BYTES)
+      return fail(MOE_E_SPACE,
+                  "%lld tokens need %lld bytes of workspace; the library's scratch holds %lld "
+                  "(moe_ternary_forward takes a caller workspace of any size)",
+                  (long long)T, (long long)need, (long long)MOE_NOALLOC_SCRATCH_BYTES);
+    if (T == 0) return ok();
+    void* ws = device_scratch();
+    if (!ws) return MOE_E_DEVICE;
+    return forward_impl(x, T, router, delta, nullptr, banks, corr_A, nullptr, corr_B, nullptr, r, k, y, ws,
+                        (int64_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+  } catch (...) {
+    return fail(MOE_E_ARG, "internal error in moe_ternary_forward_noalloc");
   }
 }
 

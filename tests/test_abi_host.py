@@ -164,9 +164,28 @@ def test_banks_must_declare_the_tile_major_order():
     assert _forward_rc(c) == -1 and "moe_tile_container" in L.moe_last_error().decode()
     c, keep = _fake_banks(layout=0)
     assert _forward_rc(c) == -1 and "MOE_BANKS_TILE_MAJOR" in L.moe_last_error().decode()
+    assert L.moe_ternary_forward_noalloc(0x10000, 4, 0x70000, None, ctypes.byref(c), None, None, 0, 2, 0x20000,
+                                         None) == -1
     c, keep = _fake_banks()
     assert _forward_rc(c, T=0) == 0
 
+
+
+def test_noalloc_forward_validation():
+    """moe_ternary_forward_noalloc checks its arguments and the size of its
+    scratch on the host, before it touches the device."""
+    L = tq.lib()
+    c, keep = _fake_banks()
+
+    def rc(T=4, k=2, r=16, A=0x50000, B=0x60000):
+        return L.moe_ternary_forward_noalloc(0x10000, T, 0x70000, None, ctypes.byref(c), A, B, r, k, 0x20000, None)
+    assert rc(k=9) == -3 and rc(k=0) == -3
+    assert rc(r=-8) == -1
+    assert rc(T=0) == 0
+    need = L.moe_workspace_bytes(ctypes.byref(c), 1 << 20, 2, 16)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert rc(T=1 << 20) == -6 and "scratch" in L.moe_last_error().decode()
+    assert L.moe_ternary_forward_noalloc(0x10000, 4, 0x70000, None, None, None, None, 0, 2, 0x20000, None) == -1
 
 
 def test_ternary_forward_validation():
