@@ -49,7 +49,11 @@ WORKLOADS = {
     "flashnext-p4096-fd": ("flashnext", 4096, "prefill", "fd"),
 }
 DELTA_FACTOR_RANK = 512
-DEFAULT_WORKLOAD = "olmoe-b64"
+# the line the default run prints: the Flash-Next-shaped layer (the largest
+# configuration) at prefill 4096, with its decode b = 64 and the skewed
+# 16384-token prefill carried in the same record
+DEFAULT_WORKLOAD = "flashnext-p4096"
+EXTRA_WORKLOADS = ("flashnext-b64", "skewed-p16384")
 # the ternary quantizer (bfloat16 weights -> containers) on every expert bank of a
 # layer: name -> (layer config, container id, rule 0 absmean / 1 Lloyd)
 QUANT_WORKLOADS = {
@@ -261,16 +265,46 @@ class Bench:
         return block_bytes, gu_bytes, block_flops, gu_flops
 
 
-def cpu_baseline(b: Bench, budget_s: float = 25.0):
-    """The fp64 oracle, as it stands, on the first s tokens of activation set 0."""
+HOST = {}
+
+
+def host_cpu():
+    """The host CPU as lscpu reports it (model, physical cores = cores per
+    socket x sockets) and the CPUs this process may run on.  Called before the
+    GPU is touched: it starts lscpu as a child process."""
+    if HOST:
+        return HOST
+    import subprocess
+    model, phys = None, None
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        kv = {}
+        for line in out.splitlines():
+            if ":" in line:
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        model = kv.get("Model name")
+        phys = int(kv.get("Core(s) per socket", "0")) * int(kv.get("Socket(s)", "0")) or None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    HOST.update({"cpu_model": model or "unknown", "physical_cores": phys, "cpus_available": avail})
+    return HOST
+
+
+def cpu_baseline(b: Bench, budget_s: float = 4.0, runs: int = 3):
+    """The fp64 oracle, as it stands, on the first s tokens of activation set 0:
+    the median of `runs` passes with BLAS threads = the physical cores this
+    process may use, and the median of `runs` single-threaded passes."""
     np = b.np
     from oracle import codec, moe as omoe
+    from threadpoolctl import threadpool_limits
     c = b.cfg
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
+    host = host_cpu()
+    threads = min(host["physical_cores"] or host["cpus_available"], host["cpus_available"])
     x = omoe.bf16_to_f64(b.x_bits[0])
     w = omoe.f16_to_f64(b.router_bits) + (omoe.factored_delta(*b.delta_factors) if b.factored
                                           else omoe.f16_to_f64(b.delta_bits))
@@ -299,17 +333,26 @@ def cpu_baseline(b: Bench, budget_s: float = 25.0):
         pos += blob.size
     banks = omoe.Banks(np.concatenate(chunks), offsets, b.formats, c.d_model, c.d_ff, c.n_experts,
                        c.n_shared)
-    # the sample is repeated until it has taken at least 10 s (and stops before 30 s)
-    reps, dt = 0, 0.0
-    while dt < 10.0 and (reps == 0 or dt * (reps + 1) / reps < 30.0):
-        t0 = time.perf_counter()
-        omoe.forward(b.x_bits[0][:s], b.router_bits, b.delta_bits, banks, b.a_bits, b.b_bits, c.top_k,
-                     delta_factors=b.delta_factors)
-        dt += time.perf_counter() - t0
-        reps += 1
-    return {"value": reps * s / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+
+    def passes(n_threads):
+        times = []
+        with threadpool_limits(n_threads):
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                omoe.forward(b.x_bits[0][:s], b.router_bits, b.delta_bits, banks, b.a_bits, b.b_bits, c.top_k,
+                             delta_factors=b.delta_factors)
+                times.append(time.perf_counter() - t0)
+        return times
+
+    multi, single = passes(threads), passes(1)
+    med, med1 = float(np.median(multi)), float(np.median(single))
+    return {"value": s / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {s} of {b.T} tokens of activation set 0 ({len(banks_needed)} expert banks "
-                      f"decoded per pass), {reps} pass(es), {dt:.1f} s"}
+                      f"decoded per pass from the packed bytes); median of {runs} passes",
+            "times_s": [round(t, 3) for t in multi],
+            "single_thread": {"value": s / med1, "unit": "tokens/s", "cores": 1,
+                              "times_s": [round(t, 3) for t in single]},
+            "host": dict(host)}
 
 
 def run(workload: str, steps: int, warmup: int, with_cpu: bool = True):
@@ -887,6 +930,8 @@ def main():
     ap.add_argument("--sweep", metavar="FILE", help="run every workload, append JSON lines to FILE")
     ap.add_argument("--only", default="", help="comma-separated workloads for --sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload only: skip the extra workloads carried in its record")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run plain device-to-device copies of MIB MiB (the reference kernel for "
                          "scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -897,6 +942,8 @@ def main():
               f"no cross-GPU exchange, so N GPUs run N independent copies of this single-GPU step "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
+    if not args.no_cpu:
+        host_cpu()  # lscpu runs before anything touches the GPU
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
         return
@@ -922,6 +969,16 @@ def main():
         rec = run_lowrank(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
     else:
         rec = run(args.workload, args.steps, args.warmup, with_cpu=not args.no_cpu)
+        if args.workload == DEFAULT_WORKLOAD and not args.no_extra:
+            rec["extra_workloads"] = {}
+            for name in EXTRA_WORKLOADS:
+                e = run(name, args.steps, args.warmup, with_cpu=False)
+                rec["extra_workloads"][name] = {
+                    k: e[k] for k in ("value", "unit", "ms_per_step", "roofline", "block", "stages_ms",
+                                      "parity_max_row_err")}
+                rec["extra_workloads"][name]["workload"] = e["config"]["workload"]
+                print(f"{name}: {e['value']:.0f} tokens/s, {e['roofline']['bound']} frac "
+                      f"{e['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
     print(json.dumps(rec), flush=True)
 
 
