@@ -42,8 +42,9 @@ constexpr int64_t kAlign = 256;
 int64_t up(int64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int64_t T, Tk, n_pos, nb, max_items;
-  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, wsplit, xpart, vpart, h, slots;
+  int64_t T, Tk, n_pos, nb, max_items, max_items2;
+  int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, items2, nitems2, wsplit, xpart,
+      vpart, h, slots;
   int rd;  // rank of a factorised router delta, 0 for none
   bool large;
   int64_t route_end, total;
@@ -56,8 +57,9 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   p.Tk = T * k;
   p.n_pos = p.Tk + (int64_t)S * T;
   p.nb = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
-  const int64_t C = moe::item_chunk(T);
+  const int64_t C = moe::item_chunk(T), C2 = moe::down_chunk(T);
   p.max_items = p.Tk / C + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C - 1) / C);
+  p.max_items2 = C2 == C ? p.max_items : p.Tk / C2 + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C2 - 1) / C2);
   int64_t o = 0;
   p.logits = o; o += up(T * E * 4);
   p.idx = o; o += up(p.Tk * 4);
@@ -70,6 +72,14 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   p.perm = o; o += up(p.Tk * 4);
   p.items = o; o += up(std::max<int64_t>(p.max_items, 1) * (int64_t)sizeof(moe::Item));
   p.nitems = o; o += up(4);
+  // the down projection's own work items when they differ from gate/up's
+  p.items2 = o;
+  p.nitems2 = o;
+  if (C2 != C) {
+    o += up(std::max<int64_t>(p.max_items2, 1) * (int64_t)sizeof(moe::Item));
+    p.nitems2 = o;
+    o += up(4);
+  }
   // large batches: split dense weights of the x-projection, later of the combine
   p.large = T > moe::kGroupMaxT;
   p.wsplit = o;
@@ -348,7 +358,8 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
                           const uint16_t* delta, const uint8_t* delta_q, const uint16_t* corr_A,
                           const uint8_t* corr_A_q, int r, int k, const Plan& p, void* ws, hipStream_t stream,
                           float* logits, int32_t* idx, float* w, int32_t* counts, int32_t* offsets,
-                          int32_t* perm, const uint16_t* delta_U = nullptr, const uint16_t* delta_V = nullptr) {
+                          int32_t* perm, const uint16_t* delta_U = nullptr, const uint16_t* delta_V = nullptr,
+                          moe::RouteArgs* route_out = nullptr) {
   const int splits = moe::xproj_split(d).splits;
   hipError_t e = stage_mark(0, false, stream);
   if (p.rd && p.large && e == hipSuccess) {  // V x first, a tiled product of its own with fp32 outputs
@@ -415,6 +426,11 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.items = at<moe::Item>(ws, p.items);
   ra.n_items = at<int32_t>(ws, p.nitems);
   ra.chunk = moe::item_chunk(T);
+  if (moe::down_chunk(T) != ra.chunk) {
+    ra.items2 = at<moe::Item>(ws, p.items2);
+    ra.n_items2 = at<int32_t>(ws, p.nitems2);
+    ra.chunk2 = moe::down_chunk(T);
+  }
   if (!p.large) {  // the routing adds up the partials: the logits, and z for the combine
     ra.lpart = da.part;
     ra.lsplits = splits + (p.rd ? 1 : 0);
@@ -423,9 +439,11 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
     ra.zr = da.N1;
   }
   e = stage_mark(1, false, stream);
-  if (e == hipSuccess) e = moe::launch_route(ra, p.max_items, stream);
+  // route_out: the caller's expert kernel routes the batch itself (stage 1 stays empty)
+  if (e == hipSuccess && !route_out) e = moe::launch_route(ra, p.max_items, stream);
   if (e == hipSuccess) e = stage_mark(1, true, stream);
   if (e != hipSuccess) return device_fail(e, "routing launch");
+  if (route_out) *route_out = ra;
   return MOE_OK;
 }
 
@@ -528,11 +546,15 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     if (ws_bytes < p.total)
       return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
     const hipStream_t st = (hipStream_t)stream;
+    // up to four tokens: the gate/up kernel routes the batch itself and the
+    // down projection carries the combine (three launches instead of five)
+    const bool tiny = !p.large && moe::tiny_path_fits(T, E, k, S, d, f);
+    moe::RouteArgs ra{};
 
     rc = route_impl(x, T, d, E, S, router, delta, delta_q, corr_A, corr_A_q, r, k, p, ws, st,
                     at<float>(ws, p.logits), at<int32_t>(ws, p.idx), at<float>(ws, p.w),
                     at<int32_t>(ws, p.counts), at<int32_t>(ws, p.offsets), at<int32_t>(ws, p.perm), delta_U,
-                    delta_V);
+                    delta_V, tiny ? &ra : nullptr);
     if (rc) return rc;
 
     moe::ExpertArgs ea{};
@@ -548,6 +570,9 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     ea.Tk = T * k;
     ea.items = at<moe::Item>(ws, p.items);
     ea.n_items = at<int32_t>(ws, p.nitems);
+    const bool two_lists = moe::down_chunk(T) != moe::item_chunk(T);
+    ea.down_items = two_lists ? at<moe::Item>(ws, p.items2) : ea.items;
+    ea.down_n_items = two_lists ? at<int32_t>(ws, p.nitems2) : ea.n_items;
     ea.perm = at<int32_t>(ws, p.perm);
     ea.topk_w = at<float>(ws, p.w);
     ea.x = x;
@@ -557,8 +582,6 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     ea.nmax = (int)std::min<int64_t>(T, ea.chunk);
     ea.fmt_mask = 0;
     for (int e = 0; e < E + S; ++e) ea.fmt_mask |= banks->formats_host[e] == MOE_PQ2_0 ? 1 : 2;
-    hipError_t e = moe::launch_experts(ea, p.max_items, st, g_stage_events);
-    if (e != hipSuccess) return device_fail(e, "expert launch");
 
     moe::DenseArgs ca{};
     ca.act = at<uint16_t>(ws, p.z);
@@ -573,6 +596,15 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     ca.n_shared = S;
     ca.y = y;
     ca.wsplit = p.large ? at<void>(ws, p.wsplit) : nullptr;
+    if (tiny) {
+      hipError_t e = moe::launch_tiny(ea, ra, ca, p.max_items, st, g_stage_events);
+      if (e == hipSuccess) e = stage_mark(4, false, st);  // the combine is part of the down launch
+      if (e == hipSuccess) e = stage_mark(4, true, st);
+      if (e != hipSuccess) return device_fail(e, "expert launch");
+      return ok();
+    }
+    hipError_t e = moe::launch_experts(ea, p.max_items, p.max_items2, st, g_stage_events);
+    if (e != hipSuccess) return device_fail(e, "expert launch");
     e = stage_mark(4, false, st);
     if (e == hipSuccess) e = moe::launch_combine(ca, st);
     if (e == hipSuccess) e = stage_mark(4, true, st);

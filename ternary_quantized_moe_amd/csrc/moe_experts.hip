@@ -26,8 +26,10 @@
 #include <cmath>
 #include <type_traits>
 
+#include "dense_rows.h"
 #include "device_common.h"
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -420,16 +422,258 @@ __global__ __launch_bounds__(64 * WPB) void expert_dec_kernel(ExpertArgs a, int 
   }
 }
 
+// ============================================================ batches of at most 4 tokens
+// The block takes three launches instead of five: the x-projection; the
+// gate/up kernel below, whose blocks each route the batch themselves; and one
+// kernel for the down projection and the combine.
+//
+// Routing in the gate/up kernel: every block adds up the logit partials of the
+// T tokens and selects their top k with the routing kernels' own topk_token
+// (the same summation order, so the choice equals the one moe_route exports),
+// then groups the slots in shared memory: a bit mask of the tokens per expert,
+// exclusive scans over the experts for the offsets and the work items, and the
+// permutation in canonical (expert, token) order.  Block 0 also stores the
+// logits, indices, gate weights, counts, offsets, permutation and work items
+// for the down kernel.  Blocks past route_blocks fold z from the partials.
+
+// Shared-memory bytes of the routing area for T tokens, top k, E experts, S shared.
+__host__ __device__ constexpr int tiny_route_bytes(int T, int k, int E, int S) {
+  return (T * E + 2 * T * k + 4) * 4 + (std::min(E, T * k) + S) * (int)sizeof(Item);
+}
+
+// The batch's top k per token (waves 0 .. T-1, one token each), then the
+// grouping by one wave with one slot per lane (T k <= 64): slot s of token
+// t = s / k and expert e sorts by the key 4 e + t, so its position in the
+// canonical (expert, token) order is the number of smaller keys; the slot with
+// an expert's smallest key starts that expert's work item.
+template <int PER>
+__device__ void tiny_route(const RouteArgs& r, char* area, bool store, const int*& perm_out, const Item*& items_out,
+                           int& n_items_out) {
+  const int T = (int)r.T, k = r.k, E = r.E, S = r.S, Tk = T * k;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = (int)blockDim.x >> 6;
+  float* slog = (float*)area;
+  int* sidx = (int*)(slog + T * E);
+  int* perm = sidx + Tk;
+  int* nitems = perm + Tk;
+  Item* items = (Item*)(nitems + 4);
+  // the logits: every wave folds 64 experts of one token at a time
+  const int nch = (E + 63) / 64;
+  for (int c = wave; c < T * nch; c += nw) {
+    const int t = c / nch, e = (c % nch) * 64 + lane;
+    if (e < E) {
+      const float v = fold_logit(r, t, e);
+      slog[t * E + e] = v;
+      if (store) r.logits[(int64_t)t * E + e] = v;
+    }
+  }
+  __syncthreads();
+  if (wave < T) topk_token<PER>(r, wave, lane, sidx, store, slog);
+  __syncthreads();
+  if (wave == 0) {
+    const bool valid = lane < Tk;
+    const int e = valid ? sidx[lane] : 0x7FFFFFF;
+    const int key = valid ? 4 * e + lane / k : 0x7FFFFFFF;
+    int pos = 0, cnt = 0, before = 0;
+    for (int j = 0; j < Tk; ++j) {  // j is uniform: the loop runs the same count in every lane
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      pos += kj < key ? 1 : 0;
+      cnt += (kj >> 2) == e ? 1 : 0;
+      before += ((kj >> 2) == e && kj < key) ? 1 : 0;
+    }
+    const bool first = valid && before == 0;
+    const uint64_t firsts = __ballot(first);
+    int iidx = 0;
+    for (int j = 0; j < Tk; ++j) {
+      const int kj = __builtin_amdgcn_readlane(key, j);
+      iidx += (((firsts >> j) & 1ull) && kj < key) ? 1 : 0;
+    }
+    const int n_routed = __popcll(firsts);
+    if (valid) {
+      perm[pos] = lane;
+      if (store) r.perm[pos] = lane;
+    }
+    if (first) items[iidx] = Item{e, pos, cnt, 0};
+    if (lane < S) items[n_routed + lane] = Item{E + lane, Tk + lane * T, T, 0};
+    if (lane == 0) *nitems = n_routed + S;
+  }
+  __syncthreads();
+  const int n_items = *nitems;
+  if (store) {
+    for (int i = tid; i < n_items; i += blockDim.x) r.items[i] = items[i];
+    if (tid == 0) *r.n_items = n_items;
+  }
+  perm_out = perm;
+  items_out = items;
+  n_items_out = n_items;
+}
+
+// Dynamic LDS: [PTQ1_0 byte table][staged rows][slot table][KS reduction][routing area]
+template <int WPB, int KS, int RT, int D, int GW, int PER>
+__global__ __launch_bounds__(64 * WPB) void expert_route_dec_kernel(ExpertArgs a, RouteArgs r, int tblocks_per_item,
+                                                                    int route_blocks) {
+  extern __shared__ __align__(16) char smem[];
+  if ((int)blockIdx.x >= route_blocks) {  // the fold of z
+    fold_z(r, (int)blockIdx.x - route_blocks, (int)gridDim.x - route_blocks);
+    return;
+  }
+  const int K = a.d;
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  char* xs = smem + lut_bytes;
+  int* slot_of = (int*)(xs + a.nmax * stage_stride(K));
+  float* wgt_of = (float*)(slot_of + a.nmax);
+  f32x4* red = (f32x4*)(xs + a.nmax * stage_stride(K) + slot_table_bytes(a.nmax));
+  char* area = (char*)red + (KS > 1 ? (WPB / KS) * (KS - 1) * RT * 64 * 16 : 0);
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the routing's syncs
+  const int* perm;
+  const Item* items;
+  int n_items;
+  tiny_route<PER>(r, area, blockIdx.x == 0, perm, items, n_items);
+  ExpertArgs la = a;
+  la.perm = perm;  // this block's own permutation (block 0's global copy is not yet visible to the others)
+  const int64_t units = (int64_t)n_items * tblocks_per_item;
+  for (int64_t u = blockIdx.x; u < units; u += route_blocks) {
+    const Item it = items[u / tblocks_per_item];
+    const int tb = (int)(u % tblocks_per_item);
+    if (la.formats[it.bank] == kPTQ1)
+      expert_unit<kPTQ1, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of);
+    else
+      expert_unit<kPQ2, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of);
+  }
+}
+
+// Down projection and combine of a batch of at most 4 tokens.  Block = one
+// 16-row tile of the model dimension for every token.  Its sixteen waves take
+// pieces: piece i < n_items is item i (an expert and the positions routed to
+// it, or a shared expert), which multiplies the tile's down rows with the
+// item's h rows and leaves each slot's o * gate weight in shared memory; the
+// pieces after them are 128-wide slices of the correction's inner dimension,
+// each the tile's B rows times z.  The block then adds, per token and row, B z
+// (slices in order) and the slots in slot order (routed in rank order, then
+// shared) in fp32, and rounds once to bf16.
+constexpr int kTinyDownWaves = 16;
+constexpr int kTinyGroups = 8;   // groups of the down rows whose loads are in flight together
+
+template <int FMT>
+__device__ __forceinline__ void tiny_down_piece(const ExpertArgs& a, const Item& it, int tile, const u32x2* lut,
+                                                float* part, int lane) {
+  const int i16 = lane & 15, q = lane >> 4;
+  const int G = a.f / kGroup;
+  constexpr int BB = block_bytes_c<FMT>();
+  const int64_t row_bytes = (int64_t)G * BB;
+  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
+  const uint8_t* wrow = bank + 2 * gu_bytes + (int64_t)tile * 16 * row_bytes + i16 * BB;
+  const uint16_t* hrow = a.h + (int64_t)(it.pos + min(i16, it.n - 1)) * a.f;  // rows past the item repeat its last
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int g0 = 0; g0 < G; g0 += kTinyGroups) {
+    u32x3 wv[kTinyGroups];
+    ActRaw av[kTinyGroups];
+#pragma unroll
+    for (int j = 0; j < kTinyGroups; ++j) {  // every load of the chunk issued first (clamped, in bounds)
+      const int g = min(g0 + j, G - 1);
+      wv[j] = load_block_x3<FMT>(wrow + (int64_t)g * 16 * BB, q);
+      av[j] = load_act_raw<FMT>(hrow, g, q);
+    }
+#pragma unroll
+    for (int j = 0; j < kTinyGroups; ++j) {
+      if (g0 + j >= G) break;
+      u32x4 A[4], W[4];
+      act_operands<FMT>(av[j], A);
+      const float sc = decode_block_x3<FMT>(wv[j], lut, lane, W);
+      f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
+      acc += sc * tmp;
+    }
+  }
+  // lane holds positions it.pos + 4q + j, row i16; the operands encode 2t, hence the 0.5
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int ti = 4 * q + j;
+    if (ti >= it.n) continue;
+    const int64_t p = it.pos + ti;
+    const bool routed = p < a.Tk;
+    const int64_t slot = routed ? a.perm[p] : p;
+    const float w = routed ? a.topk_w[slot] : 1.f;
+    part[slot * 16 + i16] = 0.5f * w * acc[j];
+  }
+}
+
+template <int FS>
+__global__ __launch_bounds__(64 * kTinyDownWaves) void down_combine_kernel(ExpertArgs a, DenseArgs c) {
+  extern __shared__ __align__(16) char smem[];
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  u32x2* lut = (u32x2*)smem;
+  const int T = (int)a.T, d = a.d, r = c.K;
+  const int n_slots = (int)a.Tk + a.S * T;
+  float* part = (float*)(smem + lut_bytes);        // [slot][16 rows]
+  float* partb = part + n_slots * 16;               // [B slice][token][16 rows]
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i16 = lane & 15, q = lane >> 4;
+  const int tile = blockIdx.x, n0 = tile * 16;
+  const bool has_b = c.w0 || c.q0;
+  const int nbs = has_b ? (r + 127) / 128 : 0;
+  const int n_items = *a.n_items;
+  for (int pc = wave; pc < n_items + nbs; pc += kTinyDownWaves) {
+    if (pc < n_items) {
+      const Item it = a.items[pc];
+      if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
+        tiny_down_piece<kPTQ1>(a, it, tile, lut, part, lane);
+      else if (FS != 2)
+        tiny_down_piece<kPQ2>(a, it, tile, lut, part, lane);
+    } else {
+      const int bs = pc - n_items;  // k-steps 4 bs .. 4 bs + 3 of B z
+      const uint16_t* zrow = c.act + (int64_t)min(i16, T - 1) * c.lda;
+      const uint16_t* brow = c.q0 ? nullptr : c.w0 + (int64_t)(n0 + i16) * r;
+      const uint8_t* qrow = c.q0 ? c.q0 + (n0 + i16) * pq2_row_bytes(r) : nullptr;
+      u32x4 wv[4], zv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = 128 * bs + 32 * j + 8 * q;
+        const bool kin = kb < r;
+        if (qrow)
+          wv[j] = kin ? pq2_row_f16x8(qrow, kb) : u32x4{0u, 0u, 0u, 0u};
+        else
+          wv[j] = kin ? *(const u32x4_a4*)(brow + kb) : u32x4{0u, 0u, 0u, 0u};
+        zv[j] = kin ? *(const u32x4*)(zrow + kb) : u32x4{0u, 0u, 0u, 0u};
+      }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 hi, lo;
+        split_f16x8(wv[j], hi, lo);
+        acc = mfma16(zv[j], hi, acc);
+        acc = mfma16(zv[j], lo, acc);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < T) partb[(bs * kTinyMaxT + 4 * q + j) * 16 + i16] = acc[j];
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x >= T * 16) return;
+  const int t = threadIdx.x >> 4, row = threadIdx.x & 15;
+  float v = 0.f;
+  for (int bs = 0; bs < nbs; ++bs) v = bs == 0 ? partb[(t) * 16 + row] : v + partb[(bs * kTinyMaxT + t) * 16 + row];
+  for (int i = 0; i < a.k; ++i) v += part[(t * a.k + i) * 16 + row];
+  for (int sh = 0; sh < a.S; ++sh) v += part[((int)a.Tk + sh * T + t) * 16 + row];
+  c.y[(int64_t)t * d + n0 + row] = (uint16_t)f32_to_bf16(v);
+}
+
 // ============================================================ large batches
-// Work unit = (item of up to 64 positions of one bank, row block).  A block of
+// Work unit = (item of up to 128 positions of one bank, row block).  A block of
 // WAVES waves stages the item's activations one 128-wide group at a time into a
 // double-buffered LDS tile while its waves multiply the previous group.  Each
 // wave owns 4 row tiles (gate/up: 32 features, their gate and up rows; down:
-// 64 model rows), decodes the 4 row tiles of a group once and multiplies them
-// with every token tile of the item, so one decoded weight feeds up to 4 MFMAs.
-// Blocks of 4 waves run two to a CU, so one block's barrier and load waits
-// overlap the other's matrix work.
-constexpr int kGemmWaves = 4;
+// 64 model rows).  Per group it decodes its 4 row tiles once into operands,
+// then walks the item's token tiles: the 4 LDS reads of a token tile's
+// activations feed 16 MFMAs (4 row tiles x 4 k-steps), and each row tile's
+// group scale is applied to the token tile's fp32 partial sums.  One decoded
+// weight feeds up to 8 token tiles.  Blocks of 8 waves run one to a CU.
+constexpr int kGemmWaves = 8;
 constexpr int kGemmRow = 256 + 16;                // staged bytes per token row and group
 constexpr int kGemmBuf = kGemmChunk * kGemmRow;   // one staged group
 constexpr int gemm_rows(int mode, int waves) { return waves * (mode == 0 ? 32 : 64); }  // per unit
@@ -479,11 +723,9 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 }
 
 // NTT: token tiles of the item (a compile-time count keeps the multiply free of
-// branches, so the independent MFMA chains of the token tiles interleave).
-// SD: groups of activations in flight (1: loaded in the step before they are
-// staged; 2: two steps before, so a load has two group steps to land, which
-// only the PQ2_0-only gate/up kernel has the registers for).
-template <int FMT, int MODE, int NTT, int WAVES, int SD>
+// branches).  The activations of group g + 1 are loaded while group g is
+// multiplied and staged after it.
+template <int FMT, int MODE, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                           char* bufs, char* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -519,8 +761,8 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   auto fetch = [&](const uint8_t* p) -> RingT { return load_block_x3<FMT>(p, q); };
 
   // staging roles of the thread: token row si, quarter sq, half sh of the
-  // 64 x 8 half quarters of a group
-  constexpr int P = 512 / (64 * WAVES);
+  // kGemmChunk x 8 half quarters of a group
+  constexpr int P = (kGemmChunk * 8 + 64 * WAVES - 1) / (64 * WAVES);
   int si[P], sq[P], sh[P];
   bool stage_on[P];
   const uint16_t* srow[P];
@@ -530,7 +772,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
     si[pp] = u >> 3;
     sq[pp] = (u >> 1) & 3;
     sh[pp] = u & 1;
-    stage_on[pp] = si[pp] < NTT * 16;
+    stage_on[pp] = si[pp] < NTT * 16;  // (NTT * 16 <= kGemmChunk)
     const int64_t p = it.pos + min(si[pp], it.n - 1);  // rows past the item repeat its last row
     if (MODE == MODE_GATEUP) {
       const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
@@ -547,14 +789,13 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt]);
   }
-  u32x4 s0[P][2], s1[P][SD == 2 ? 2 : 1];  // staged loads in flight (SD = 1: s0 only)
+  u32x4 s0[P][2];  // staged loads in flight
   __syncthreads();  // the previous unit is done with the staging buffers
 #pragma unroll
   for (int pp = 0; pp < P; ++pp)
     if (stage_on[pp]) {
       act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], s0[pp]);
       act_half_store<FMT>(s0[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
-      if constexpr (SD == 2) act_half_load<FMT>(srow[pp], min(1, G - 1), sq[pp], sh[pp], s1[pp]);
     }
   __syncthreads();
 
@@ -564,93 +805,43 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the item's activation operands of group g, then one row tile at a time:
-  // decode it, refill its ring slot with group gn, multiply it with every token tile
-  auto multiply = [&](int g, int gn) {
-    if (!active) return;
-    const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
-    u32x4 A[NTT][4];
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      u32x4 W[4];
-      const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-      ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
-      f32x4 tmp[NTT];
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
-    }
-  };
-  auto load = [&](int g, u32x4 (&raw)[P][2]) {
+  // The last step fetches the last group again (in bounds, unused) and
+  // restages it into the idle buffer, so the loop body has no branch on g.
+  for (int g = 0; g < G; ++g) {
+    const int gn = min(g + 1, G - 1);
 #pragma unroll
     for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp]) act_half_load<FMT>(srow[pp], g, sq[pp], sh[pp], raw[pp]);
-  };
-  auto store = [&](int g, const u32x4 (&raw)[P][2]) {  // into the buffer of group g
+      if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
+    if (active) {
+      // the group's 4 row tiles, decoded once
+      u32x4 W[4][4];
+      float sc[4];
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp]) act_half_store<FMT>(raw[pp], bufs + (g & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
-  };
-  // The last steps fetch the last group again (in bounds, unused) and restage
-  // it into the idle buffer, so the loop bodies have no branch on g.
-  if constexpr (SD == 2) {
-    // step g: issue group g + 2, multiply group g, stage group g + 1 (issued a step ago)
-    for (int g = 0; g < G; g += 2) {
-      load(min(g + 2, G - 1), s0);
-      multiply(g, min(g + 1, G - 1));
-      store(g + 1, s1);
-      __syncthreads();
-      if (g + 1 < G) {
-        load(min(g + 3, G - 1), s1);
-        multiply(g + 1, min(g + 2, G - 1));
-        store(g + 2, s0);
-        __syncthreads();
+      for (int rt = 0; rt < 4; ++rt) {
+        sc[rt] = decode_block_x3<FMT>(ring[rt], lut, lane, W[rt]);
+        ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
       }
-    }
-  } else {
-    for (int g = 0; g < G; ++g) {
-      const int gn = min(g + 1, G - 1);
+      const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
 #pragma unroll
-      for (int pp = 0; pp < P; ++pp)
-        if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
-      if (active) {  // the multiply written out (as a lambda call it spills here)
-        const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
-        u32x4 A[NTT][4];
+      for (int tt = 0; tt < NTT; ++tt) {
+        f32x4 tmp[4];
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt)
+        for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+        for (int m = 0; m < 4; ++m) {
+          const u32x4 A = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          u32x4 W[4];
-          const float sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
-          ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
-          f32x4 tmp[NTT];
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
-#pragma unroll
-          for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
+          for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A, W[rt][m], tmp[rt]);
         }
-      }
 #pragma unroll
-      for (int pp = 0; pp < P; ++pp)
-        if (stage_on[pp])
-          act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
-      __syncthreads();
+        for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+      }
     }
+#pragma unroll
+    for (int pp = 0; pp < P; ++pp)
+      if (stage_on[pp])
+        act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
+    __syncthreads();
   }
   if (!active) return;
 
@@ -693,9 +884,9 @@ template <int MODE, int FS, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                               char* bufs, bool ptq1) {
   if (FS != 1 && ptq1)
-    gemm_unit<kPTQ1, MODE, NTT, WAVES, 1>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
   else if (FS != 2)
-    gemm_unit<kPQ2, MODE, NTT, WAVES, (FS == 1 && MODE == MODE_GATEUP) ? 2 : 1>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
 }
 
 // Persistent blocks over units.  Unit l = (item l / row_blocks, row block
@@ -723,7 +914,9 @@ void expert_gemm_kernel(ExpertArgs a, int row_blocks) {
       case 1: gemm_dispatch<MODE, FS, 1, WAVES>(a, it, rb, lut, bufs, ptq1); break;
       case 2: gemm_dispatch<MODE, FS, 2, WAVES>(a, it, rb, lut, bufs, ptq1); break;
       case 3: gemm_dispatch<MODE, FS, 3, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      default: gemm_dispatch<MODE, FS, 4, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      case 4: gemm_dispatch<MODE, FS, 4, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      case 5: gemm_dispatch<MODE, FS, 5, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      default: gemm_dispatch<MODE, FS, kGemmChunk / 16, WAVES>(a, it, rb, lut, bufs, ptq1); break;
     }
   }
 }
@@ -795,8 +988,8 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 
   // per token row: its slot and half its gate weight (the operands encode 2t),
   // read back through volatile pointers so the quad loop does not hold them
-  int* slot_of = (int*)(xs + kGemmChunk * stride);
-  float* wgt_of = (float*)(slot_of + kGemmChunk);
+  int* slot_of = (int*)(xs + kDownChunk * stride);
+  float* wgt_of = (float*)(slot_of + kDownChunk);
   __syncthreads();  // the previous unit is done with the staged rows
   if (tid < NTT * 16) {
     const int64_t p = it.pos + min(tid, it.n - 1);
@@ -908,7 +1101,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 template <int FS, int NTT, int G>
 __device__ __forceinline__ void down_dispatch(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                               bool ptq1) {
-  char* scratch = xs + kGemmChunk * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
+  char* scratch = xs + kDownChunk * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
   if (FS != 1 && ptq1)
     down_unit<kPTQ1, NTT, G, false>(a, it, lut, xs, scratch);
   else if (FS != 2)
@@ -927,18 +1120,21 @@ void down_resident_kernel(ExpertArgs a) {
   u32x2* lut = (u32x2*)smem;
   char* xs = smem + lut_bytes;
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
-  const int64_t U = *a.n_items;
+  const int64_t U = *a.down_n_items;
   const int64_t per = (U + 7) / 8;
   for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
     const int64_t l = (u & 7) * per + (u >> 3);
     if (l >= U) continue;
-    const Item it = a.items[l];
-    const bool ptq1 = FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1);
-    switch ((it.n + 15) / 16) {
-      case 1: down_dispatch<FS, 1, G>(a, it, lut, xs, ptq1); break;
-      case 2: down_dispatch<FS, 2, G>(a, it, lut, xs, ptq1); break;
-      case 3: down_dispatch<FS, 3, G>(a, it, lut, xs, ptq1); break;
-      default: down_dispatch<FS, 4, G>(a, it, lut, xs, ptq1); break;
+    const Item item = a.down_items[l];
+    const bool ptq1 = FS == 2 || (FS == 3 && a.formats[item.bank] == kPTQ1);
+    for (int h0 = 0; h0 < item.n; h0 += kDownChunk) {  // (down items hold at most kDownChunk positions)
+      const Item it{item.bank, item.pos + h0, min(kDownChunk, item.n - h0), 0};
+      switch ((it.n + 15) / 16) {
+        case 1: down_dispatch<FS, 1, G>(a, it, lut, xs, ptq1); break;
+        case 2: down_dispatch<FS, 2, G>(a, it, lut, xs, ptq1); break;
+        case 3: down_dispatch<FS, 3, G>(a, it, lut, xs, ptq1); break;
+        default: down_dispatch<FS, 4, G>(a, it, lut, xs, ptq1); break;
+      }
     }
   }
 }
@@ -1061,7 +1257,7 @@ static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, s
 // Down projection of a large batch: LDS-resident h rows where the shape is
 // compiled in and the rows fit, else the group-staged kernel.
 static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, hipStream_t s) {
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kGemmChunk * (stage_stride(a.f) + 8) +
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kDownChunk * (stage_stride(a.f) + 8) +
                      (size_t)kDownWaves * kChunkScratch;
   if (lds <= 160 * 1024) {
     switch (a.f / kGroup) {
@@ -1121,7 +1317,68 @@ static hipError_t launch_down(const ExpertArgs& a, int64_t mi, bool small, hipSt
   }
 }
 
-hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream, void** ev) {
+template <int KS, int RT, int D, int GW, int PER>
+static hipError_t launch_route_dec(const ExpertArgs& a, const RouteArgs& r, int64_t max_items, hipStream_t stream) {
+  constexpr int WPB = 8;
+  const int K = a.d;
+  const int n_tiles = a.f / 16;
+  constexpr int TPB = WPB / KS;
+  const int tbpi = (n_tiles + TPB - 1) / TPB;
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
+                     slot_table_bytes(a.nmax) + (KS > 1 ? (size_t)TPB * (KS - 1) * RT * 64 * 16 : 0) +
+                     (size_t)tiny_route_bytes((int)a.T, a.k, a.E, a.S);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  auto kern = expert_route_dec_kernel<WPB, KS, RT, D, GW, PER>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WPB, lds);
+  if (e != hipSuccess || per_cu < 1) per_cu = 1;
+  const int route_blocks = (int)std::min<int64_t>((int64_t)cu_count() * per_cu, max_items * tbpi);
+  const int fold = fold_blocks(r, 64 * WPB);
+  kern<<<dim3((unsigned)(route_blocks + fold)), 64 * WPB, lds, stream>>>(a, r, tbpi, route_blocks);
+  return hipGetLastError();
+}
+
+template <int PER>
+static hipError_t launch_route_gateup(const ExpertArgs& a, const RouteArgs& r, int64_t mi, hipStream_t s) {
+  switch (a.d / kGroup) {
+    case 24: return launch_route_dec<4, 2, 6, 6, PER>(a, r, mi, s);
+    case 16: return launch_route_dec<4, 2, 4, 4, PER>(a, r, mi, s);
+    case 2: return launch_route_dec<2, 2, 1, 1, PER>(a, r, mi, s);
+    default: return launch_route_dec<4, 2, 4, 0, PER>(a, r, mi, s);
+  }
+}
+
+bool tiny_path_fits(int64_t T, int E, int k, int S, int d, int f) {
+  (void)d;
+  (void)f;
+  return T >= 1 && T <= kTinyMaxT && E <= 512 && T * (int64_t)k <= 64 && T * (int64_t)(k + S) <= kTinyMaxSlots;
+}
+
+hipError_t launch_tiny(const ExpertArgs& a, const RouteArgs& r, const DenseArgs& c, int64_t max_items,
+                       hipStream_t stream, void** ev) {
+  auto mark = [&](int i) { return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], stream) : hipSuccess; };
+  hipError_t e = mark(4);
+  if (e == hipSuccess) e = a.E <= 128 ? launch_route_gateup<2>(a, r, max_items, stream)
+                                      : launch_route_gateup<8>(a, r, max_items, stream);
+  if (e == hipSuccess) e = mark(5);
+  if (e == hipSuccess) e = mark(6);
+  if (e == hipSuccess) {
+    const int nbs = (c.w0 || c.q0) ? (c.K + 127) / 128 : 0;
+    const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) +
+                       (size_t)(a.Tk + (int64_t)a.S * a.T) * 16 * 4 + (size_t)nbs * kTinyMaxT * 16 * 4;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.d / 16));
+    if (a.fmt_mask == 1) down_combine_kernel<1><<<grid, 64 * kTinyDownWaves, lds, stream>>>(a, c);
+    else if (a.fmt_mask == 2) down_combine_kernel<2><<<grid, 64 * kTinyDownWaves, lds, stream>>>(a, c);
+    else down_combine_kernel<3><<<grid, 64 * kTinyDownWaves, lds, stream>>>(a, c);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = mark(7);
+  return e;
+}
+
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, int64_t max_down_items, hipStream_t stream,
+                          void** ev) {
   if (max_items <= 0) return hipSuccess;
   hipError_t e = hipSuccess;
   const bool small = a.T <= 4;
@@ -1133,7 +1390,7 @@ hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t st
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess)
-    e = gemm ? launch_down_large(a, max_items, stream) : launch_down(a, max_items, small, stream);
+    e = gemm ? launch_down_large(a, max_down_items, stream) : launch_down(a, max_items, small, stream);
   if (e == hipSuccess) e = mark(7);
   return e;
 }

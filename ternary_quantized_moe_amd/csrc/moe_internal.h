@@ -10,14 +10,18 @@ namespace moe {
 
 constexpr int kGroup = 128;     // weights per container group
 constexpr int kChunk = 16;      // tokens per expert work item of a small batch (one MFMA M tile)
-constexpr int kGemmChunk = 64;  // tokens per expert work item of a large batch (four M tiles)
+constexpr int kGemmChunk = 96;  // tokens per expert work item of a large batch (six M tiles)
 constexpr int kRouteBlock = 256;  // tokens per ranking block
 constexpr int kGroupMaxT = 256;   // largest batch grouped by one block
 constexpr int kMaxExperts = 1024;
 
 // Small batches stream each touched expert's weights once per 16 tokens; large
-// batches multiply each decoded weight group with up to 64 tokens.
+// batches multiply each decoded weight group with up to 96 tokens.
 __host__ __device__ inline int item_chunk(int64_t T) { return T > kGroupMaxT ? kGemmChunk : kChunk; }
+// The down projection of a large batch stages 64 positions at a time and takes
+// work items of that size.
+constexpr int kDownChunk = 64;
+__host__ __device__ inline int down_chunk(int64_t T) { return T > kGroupMaxT ? kDownChunk : kChunk; }
 
 // Work item of the grouped expert kernels: bank, first position in the
 // (expert, token)-ordered slot space, number of tokens (<= item_chunk(T)).
@@ -103,6 +107,11 @@ struct RouteArgs {
   Item* items;          // [max_items]
   int32_t* n_items;     // [1]
   int chunk;            // tokens per work item, item_chunk(T)
+  // NULL, or a second list of work items of chunk2 positions (the down
+  // projection's, for large batches)
+  Item* items2;
+  int32_t* n_items2;
+  int chunk2;
   // NULL, or the x-projection partials [lsplits][T][lN] whose first E columns
   // sum (in slice order) to the logits; the top-k then also stores the sums
   // into logits
@@ -123,6 +132,8 @@ struct ExpertArgs {
   int64_t T, Tk;
   const Item* items;
   const int32_t* n_items;
+  const Item* down_items;      // the down projection's work items (== items for small batches)
+  const int32_t* down_n_items;
   const int32_t* perm;
   const float* topk_w;
   const uint16_t* x;   // bf16 [T x d]
@@ -176,7 +187,17 @@ hipError_t launch_dense_gemm(const DenseArgs& a, int N, hipStream_t stream);
 hipError_t launch_xproj(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_combine(const DenseArgs& a, hipStream_t stream);
 hipError_t launch_route(const RouteArgs& a, int64_t max_items, hipStream_t stream);
+// Batches of at most kTinyMaxT tokens with E <= 512, T k <= 64 and T (k + S) <= kTinyMaxSlots
+// run in three launches: the x-projection, then launch_tiny: the gate/up
+// kernel whose blocks route the batch themselves (and fold z), and the down
+// projection fused with the combine (c: the combine's DenseArgs).
+constexpr int kTinyMaxT = 4;
+constexpr int kTinyMaxSlots = 256;
+bool tiny_path_fits(int64_t T, int E, int k, int S, int d, int f);
+hipError_t launch_tiny(const ExpertArgs& a, const RouteArgs& r, const DenseArgs& c, int64_t max_items,
+                       hipStream_t stream, void** stage_events);
 // stage_events: NULL or the caller's events; [4..7] bracket gate/up and down.
-hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, hipStream_t stream, void** stage_events);
+hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, int64_t max_down_items, hipStream_t stream,
+                          void** stage_events);
 
 }  // namespace moe

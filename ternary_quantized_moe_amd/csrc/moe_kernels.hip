@@ -22,6 +22,7 @@
 #include "device_common.h"
 #include "dense_rows.h"
 #include "moe_internal.h"
+#include "route_device.h"
 #include "wave_ops.h"
 
 namespace moe {
@@ -649,197 +650,6 @@ hipError_t launch_combine(const DenseArgs& a, hipStream_t stream) {
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
 
-// Top-k candidates as 64-bit keys whose unsigned order is the selection
-// order.  High word: the fp32 logit mapped to an order-preserving integer
-// (-0.0 taken as +0.0; logits are finite); low word: the complemented expert
-// index, so of two equal logits the lower expert ranks first.  Key 0 lies
-// below every candidate and marks a used or absent one.
-__device__ __forceinline__ uint64_t route_key(float v, int e) {
-  uint32_t u = __float_as_uint(v);
-  u = u == 0x80000000u ? 0u : u;
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
-}
-__device__ __forceinline__ float key_value(uint64_t key) {
-  const uint32_t u = (uint32_t)(key >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// x from another lane (DPP pattern CTRL) in the rows of ROWS; other rows keep x.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t x) {
-  const int lo = (int)(uint32_t)x, hi = (int)(uint32_t)(x >> 32);
-  const uint32_t l = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xF, false);
-  const uint32_t h = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xF, false);
-  return ((uint64_t)h << 32) | l;
-}
-
-constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
-
-// Wave-wide maximum key, returned in every lane, with compares and selects
-// only: four exchanges inside each row of 16 lanes; then lane 15 of rows 0 and
-// 2 folds into rows 1 and 3, and lane 31 (rows 0-1) into rows 2 and 3, which
-// leaves the maximum in lane 63.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t x) {
-  x = umax64(x, dpp_u64<kDppXor1, 0xF>(x));
-  x = umax64(x, dpp_u64<kDppXor2, 0xF>(x));
-  x = umax64(x, dpp_u64<kDppHalfMirror, 0xF>(x));
-  x = umax64(x, dpp_u64<kDppMirror, 0xF>(x));
-  x = umax64(x, dpp_u64<kDppRowBcast15, 0xA>(x));
-  x = umax64(x, dpp_u64<kDppRowBcast31, 0xC>(x));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, 63);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-// Wave-wide sum: every lane returns the same value (rows summed in row order).
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_f32<kDppXor1>(v);
-  v += dpp_f32<kDppXor2>(v);
-  v += dpp_f32<kDppHalfMirror>(v);
-  v += dpp_f32<kDppMirror>(v);
-  return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
-}
-
-// Inclusive prefix sum over the lanes of a wave: shifts by 1, 2, 4, 8 inside
-// each row (lanes shifted in from outside the row read 0), then each row adds
-// the totals of the rows before it.
-__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
-  v += __builtin_amdgcn_update_dpp(0, v, kDppShr1, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, kDppShr2, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, kDppShr4, 0xF, 0xF, true);
-  v += __builtin_amdgcn_update_dpp(0, v, kDppShr8, 0xF, 0xF, true);
-  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-            r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = lane >> 4;
-  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
-}
-
-// Inclusive prefix sum over the 1024 threads of a block; *total receives the
-// block's sum.  wsum: 16 ints of shared memory.  Every thread must call it.
-__device__ __forceinline__ int block_inclusive_scan(int v, int* wsum, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_inclusive_scan(v, lane);
-  __syncthreads();  // wsum may still be read by a previous scan
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < 16; ++w) {
-    const int s = wsum[w];
-    before += w < wave ? s : 0;
-    all += s;
-  }
-  *total = all;
-  return v + before;
-}
-
-// One wave selects the top k of token t: k rounds of a wave-wide maximum over
-// the candidate keys (lane l holds experts l, l + 64, ...), each round clearing
-// the winner's key.  Lane i % 64 keeps the i-th selected key for the softmax
-// and the coalesced stores at the end.  sidx: NULL, or LDS that also receives
-// the indices.
-template <int PER>  // keys per lane: E <= 64 * PER
-__device__ __forceinline__ void topk_token(const RouteArgs& a, int64_t t, int lane, int* sidx) {
-  const int E = a.E, k = a.k;
-  float lv[PER];  // every load unconditional (clamped index) so all are in flight together
-  if (a.lpart) {
-    // the logits: the x-projection partials added in slice order, SU slices' loads at a time
-    constexpr int SU = PER >= 16 ? 4 : 8;
-    const int64_t stride = a.T * (int64_t)a.lN;
-    const float* base = a.lpart + t * a.lN;
-#pragma unroll
-    for (int c = 0; c < PER; ++c) lv[c] = 0.f;
-    for (int s0 = 0; s0 < a.lsplits; s0 += SU) {
-      float pv[SU][PER];
-#pragma unroll
-      for (int j = 0; j < SU; ++j)
-#pragma unroll
-        for (int c = 0; c < PER; ++c)
-          pv[j][c] = base[min(s0 + j, a.lsplits - 1) * stride + min(lane + 64 * c, E - 1)];
-#pragma unroll
-      for (int j = 0; j < SU; ++j)
-#pragma unroll
-        for (int c = 0; c < PER; ++c)
-          if (s0 + j < a.lsplits) lv[c] += pv[j][c];
-    }
-#pragma unroll
-    for (int c = 0; c < PER; ++c)
-      if (lane + 64 * c < E) a.logits[t * E + lane + 64 * c] = lv[c];
-  } else {
-#pragma unroll
-    for (int c = 0; c < PER; ++c) lv[c] = a.logits[t * E + min(lane + 64 * c, E - 1)];
-  }
-  uint64_t key[PER], sel[PER];  // sel[c] in lane l: the (64 c + l)-th selected key (k <= E)
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int e = lane + 64 * c;
-    key[c] = e < E ? route_key(lv[c], e) : 0ull;
-    sel[c] = 0ull;
-  }
-  float m = 0.f;
-  for (int i = 0; i < k; ++i) {
-    uint64_t best = key[0];
-#pragma unroll
-    for (int c = 1; c < PER; ++c) best = umax64(best, key[c]);
-    const uint64_t w = wave_max_key(best);
-    const int we = key_expert(w);
-    if (i == 0) m = key_value(w);
-#pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      key[c] = we == lane + 64 * c ? 0ull : key[c];
-      sel[c] = i == lane + 64 * c ? w : sel[c];
-    }
-  }
-  // softmax over the selected logits
-  float ev[PER], part = 0.f;
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    ev[c] = 64 * c + lane < k ? __expf(key_value(sel[c]) - m) : 0.f;
-    part += ev[c];
-  }
-  const float inv = 1.f / wave_sum(part);
-#pragma unroll
-  for (int c = 0; c < PER; ++c) {
-    const int i = 64 * c + lane;
-    if (i < k) {
-      const int e = key_expert(sel[c]);
-      a.idx[t * k + i] = e;
-      if (sidx) sidx[t * k + i] = e;
-      a.w[t * k + i] = ev[c] * inv;
-    }
-  }
-}
-
-// z = bf16 of the x-projection partials' columns E .. E + zr - 1, added in
-// slice order.  Fold block b of nb takes elements b * blockDim + thread, then
-// every nb * blockDim-th.
-__device__ __forceinline__ void fold_z(const RouteArgs& a, int b, int nb) {
-  const int n = (int)a.T * a.zr;
-  const int64_t stride = a.T * (int64_t)a.lN;
-  for (int i = b * (int)blockDim.x + (int)threadIdx.x; i < n; i += nb * (int)blockDim.x) {
-    const int t = i / a.zr, c = i - t * a.zr;
-    const float* p = a.lpart + (int64_t)t * a.lN + a.E + c;
-    float v = 0.f;
-    for (int s0 = 0; s0 < a.lsplits; s0 += 8) {
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = p[min(s0 + j, a.lsplits - 1) * stride];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < a.lsplits) v += pv[j];
-    }
-    a.z[i] = (uint16_t)f32_to_bf16(v);
-  }
-}
-
-// Blocks of the first routing launch beyond its routing blocks: fold z.
-inline int fold_blocks(const RouteArgs& a, int threads) {
-  if (!a.z || !a.lpart || a.zr <= 0) return 0;
-  return (int)std::min<int64_t>(256, (a.T * a.zr + threads - 1) / threads);
-}
-
 // One wave per token: k rounds of a wave-wide argmax over the E logits (larger
 // value first, equal values to the lower expert index; -0.0 equals +0.0), then
 // the softmax over the selected logits.
@@ -886,6 +696,37 @@ __global__ __launch_bounds__(256) void rank_kernel(RouteArgs a) {
   }
 }
 
+// Work items of C positions over the experts' runs of the permutation (thread
+// e of the 1024: expert e with `total` slots from off_e), then the shared
+// experts' tokens in runs of C.  Every thread of the block calls it.
+__device__ __forceinline__ void emit_items(const RouteArgs& a, int e, int total, int off_e, int C, Item* items,
+                                           int32_t* n_items, int* wsum) {
+  const int E = a.E;
+  const int chunks = e < E ? (total + C - 1) / C : 0;
+  int routed_items;
+  const int istart = block_inclusive_scan(chunks, wsum, &routed_items) - chunks;
+  for (int c = 0; c < chunks; ++c) {
+    Item it;
+    it.bank = e;
+    it.pos = off_e + c * C;
+    it.n = min(C, total - c * C);
+    it.pad = 0;
+    items[istart + c] = it;
+  }
+  const int per_shared = (int)((a.T + C - 1) / C);
+  const int64_t Tk = a.T * a.k;
+  for (int idx = e; idx < a.S * per_shared; idx += 1024) {
+    const int s = idx / per_shared, c = idx % per_shared;
+    Item it;
+    it.bank = E + s;
+    it.pos = (int)(Tk + (int64_t)s * a.T + (int64_t)c * C);
+    it.n = (int)min((int64_t)C, a.T - (int64_t)c * C);
+    it.pad = 0;
+    items[routed_items + idx] = it;
+  }
+  if (e == 0) *n_items = routed_items + a.S * per_shared;
+}
+
 // One block of 1024 threads, thread = expert.
 __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   __shared__ int wsum[16];
@@ -921,31 +762,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
     }
   }
   if (e == 0) a.offsets[E] = (int)(a.T * a.k);
-  // work items: ceil(count / chunk) per routed expert, then the shared experts
-  const int C = a.chunk;
-  const int chunks = e < E ? (total + C - 1) / C : 0;
-  int routed_items;
-  const int istart = block_inclusive_scan(chunks, wsum, &routed_items) - chunks;
-  for (int c = 0; c < chunks; ++c) {
-    Item it;
-    it.bank = e;
-    it.pos = off_e + c * C;
-    it.n = min(C, total - c * C);
-    it.pad = 0;
-    a.items[istart + c] = it;
-  }
-  const int per_shared = (int)((a.T + C - 1) / C);
-  const int64_t Tk = a.T * a.k;
-  for (int idx = e; idx < a.S * per_shared; idx += 1024) {
-    const int s = idx / per_shared, c = idx % per_shared;
-    Item it;
-    it.bank = E + s;
-    it.pos = (int)(Tk + (int64_t)s * a.T + (int64_t)c * C);
-    it.n = (int)min((int64_t)C, a.T - (int64_t)c * C);
-    it.pad = 0;
-    a.items[routed_items + idx] = it;
-  }
-  if (e == 0) *a.n_items = routed_items + a.S * per_shared;
+  // work items: ceil(count / chunk) per routed expert, then the shared experts;
+  // a second list of the same form for the down projection when it is asked for
+  emit_items(a, e, total, off_e, a.chunk, a.items, a.n_items, wsum);
+  if (a.items2) emit_items(a, e, total, off_e, a.chunk2, a.items2, a.n_items2, wsum);
 }
 
 __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {

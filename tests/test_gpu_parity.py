@@ -152,39 +152,49 @@ def sample_tokens(T, n, seed=0):
     return np.sort(np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), n - 2, replace=False)]))
 
 
-def item_edge_tokens(counts, offsets, perm, T, k, n_shared, chunk=64, hot=5):
+# The large-batch expert kernels split each routed expert's run of slots in
+# the permutation (and each shared expert's tokens) into work items: of ITEM
+# positions for the gate/up projection, of HALF positions for the down one.
+ITEM, HALF = 96, 64
+
+
+def item_edge_tokens(counts, offsets, perm, T, k, n_shared, item=ITEM, half=HALF, hot=5):
     """Tokens where the large-batch expert kernels' work items begin and end.
 
-    A routed expert's work items are consecutive runs of `chunk` slots of its
-    segment of the permutation (the last one partial); a shared expert's are the
-    token ranges [chunk j, chunk (j + 1)).  Returned: for the `hot` experts with
-    the most slots, the first and last token of every item; for every other
-    expert with slots, its first and last token and the first token of its last
-    item; for a shared expert, tokens chunk j - 1 and chunk j for every j."""
+    For the `hot` experts with the most slots: the first and last token of every
+    gate/up and every down item; for every other expert with slots: its first
+    and last token and the first token of its last item of either kind; for a
+    shared expert: both sides of every item boundary of either kind."""
     counts = np.asarray(counts, np.int64)
     offsets = np.asarray(offsets, np.int64)
+
+    def cuts(n):                      # offsets (within a run of n) where an item of either kind starts
+        return sorted(set(range(0, n, item)) | set(range(0, n, half)))
+
     pos = set()
     for e in np.nonzero(counts)[0]:
         o, n = int(offsets[e]), int(counts[e])
-        pos.update([o, o + n - 1, o + (n - 1) // chunk * chunk])
+        pos.update([o, o + n - 1, o + (n - 1) // item * item, o + (n - 1) // half * half])
     for e in np.argsort(-counts, kind="stable")[:hot]:
         o, n = int(offsets[e]), int(counts[e])
-        for j in range(0, n, chunk):
-            pos.update([o + j, o + min(j + chunk, n) - 1])
+        for c in cuts(n):
+            pos.update([o + c, o + max(c - 1, 0)])
+        pos.add(o + n - 1)
     toks = {int(perm[p]) // k for p in pos}
     if n_shared:
-        for j in range(chunk, T, chunk):
-            toks.update([j - 1, j])
+        for c in cuts(T):
+            toks.update([max(c - 1, 0), c])
+        toks.add(T - 1)
     return np.array(sorted(toks), dtype=np.int64)
 
 
 @pytest.mark.parametrize("name,T", CASES)
 def test_forward_parity(name, T):
     """Every token is compared up to 4096 tokens.  At 16384 tokens (Zipf-skewed
-    routing) the compared tokens are the edges of every work item of the five
-    hottest experts (the hottest holds about 37x the mean load), the first and
-    last token and last-item start of every expert, both sides of every shared
-    expert item boundary, and 256 random tokens."""
+    routing) the compared tokens are the edges of every work item and staged
+    part of the five hottest experts (the hottest holds about 37x the mean
+    load), the first and last token and last-item start of every expert, both
+    sides of every shared expert item boundary, and 256 random tokens."""
     tq = tq_mod()
     L = Layer(name)
     c = L.cfg
