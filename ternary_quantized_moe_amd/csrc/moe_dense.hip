@@ -7,10 +7,10 @@
 // The fp16 weight rows are first split once per call into exact bf16 hi/lo
 // operand pairs (device_common.h), stored tile by tile in matrix-core operand
 // order, so a wave reads each operand of a 16-row tile as one contiguous 1 KB.
-// A unit of work is (64 tokens, 128 weight rows); a block of 4 waves stages the
+// A unit of work is (64 tokens, 128 weight rows); a block of 8 waves stages the
 // tokens' activations one 128-wide group at a time into a double-buffered LDS
-// tile and each wave multiplies them with its two 16-row tiles, whose split
-// operands it streams from the workspace one group ahead.
+// tile and each wave multiplies them with its 16-row tile, whose split operands
+// it streams from the workspace one group ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,10 +22,13 @@
 
 namespace moe {
 
-// Blocks of 4 waves run two to a CU, so one block's barrier and load waits
-// overlap the other's matrix work.
-constexpr int kDenseWaves = 4;
-constexpr int kDenseRows = kDenseWaves * 32;      // weight rows per unit (2 tiles per wave)
+// Blocks of 8 waves, one 16-row tile each, run two to a CU (four waves per
+// SIMD at up to 128 registers), so one block's barrier and load waits overlap
+// the other's matrix work even where the units are few (a 4096 x 512 product
+// has 256 units, one per CU).
+constexpr int kDenseWaves = 8;
+constexpr int kDenseRT = 1;                             // row tiles per wave
+constexpr int kDenseRows = kDenseWaves * 16 * kDenseRT;  // weight rows per unit
 constexpr int kDenseTok = 64;                     // tokens per unit (4 MFMA M tiles)
 constexpr int kDenseRow = 256 + 16;               // staged bytes per token row and group
 constexpr int kDenseBuf = kDenseTok * kDenseRow;  // one staged group
@@ -42,7 +45,7 @@ int64_t dense_split_bytes(int N, int K) { return (int64_t)(N + 15) / 16 * 16 * d
 // 16 bytes (8 bf16 of elements g*128 + 32m + 8q .. +7 of row 16 tile + i16) at
 // ((((tile * G + g) * 4 + m) * 2 + hl) * 64 + 16 q + i16) * 16.  Elements past K
 // and rows past N are zero.  Block (tile, g) reads its 16 rows x 128 elements
-// with 256-byte row pieces and writes its 8 KB of operands as one contiguous run
+// with 256-byte row pieces and writes its 8 KB of hi/lo operands as one run
 // after rearranging them in shared memory.
 __global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, u32x4* __restrict__ out) {
   __shared__ u32x4 tile_ops[512];
@@ -83,14 +86,14 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i16 = lane & 15, q = lane >> 4;
   const int G = Kp / kGroup;
-  const int row0 = rb * kDenseRows + wave * 32;
+  const int row0 = rb * kDenseRows + wave * 16 * kDenseRT;
   const bool active = row0 < N;
 
-  // the wave's two row tiles (a tile past the last one repeats it; rows past N
+  // the wave's row tiles (a tile past the last one repeats it; rows past N
   // are zero and not stored); operand (g, m, hl) at + (g * 8 + m * 2 + hl) * 64
-  const u32x4* wp[2];
+  const u32x4* wp[kDenseRT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kDenseRT; ++rt) {
     const int tile = min(row0 / 16 + rt, (N - 1) / 16);
     wp[rt] = w2 + (int64_t)tile * G * 512 + lane;
   }
@@ -120,15 +123,14 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
       if (si[pp] < NTT * 16) *(u32x4*)(buf + si[pp] * kDenseRow + sc[pp] * 16) = raw[pp];
   };
 
-  u32x4 B[2][4][2];  // [row tile][m][hi, lo] of the next group
+  u32x4 B[kDenseRT][4][2];  // [row tile][m][hi, lo] of the next group
   if (active && G > 0) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < kDenseRT; ++rt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        B[rt][m][0] = wp[rt][(m * 2) * 64];
-        B[rt][m][1] = wp[rt][(m * 2 + 1) * 64];
-      }
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) B[rt][m][hl] = wp[rt][(m * 2 + hl) * 64];
   }
   u32x4 s0[kDenseP], s1[kDenseP];  // staged loads of the next two groups
   __syncthreads();  // the previous unit is done with the shared memory
@@ -137,36 +139,39 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
   stage_load(min(1, G - 1), s1);
   __syncthreads();
 
-  f32x4 acc[NTT][2];
+  f32x4 acc[NTT][kDenseRT];
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt][0] = acc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+    for (int rt = 0; rt < kDenseRT; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // step g: issue the loads of group g + 2, multiply group g, store group g + 1
-  // (loaded one step earlier); the last steps refetch the last group (unused)
+  // (loaded one step earlier), load the weights of group g + 1; the last steps
+  // refetch the last group (unused).  The A operands are read from shared
+  // memory one MFMA slice m at a time.
   auto step = [&](int g, u32x4 (&issue)[kDenseP], const u32x4 (&ready)[kDenseP]) {
     const int gn = min(g + 1, G - 1);
     stage_load(min(g + 2, G - 1), issue);
     if (active) {
       const char* ab = smem + (g & 1) * kDenseBuf + i16 * kDenseRow + q * 16;
-      u32x4 A[NTT][4];
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt)
+      for (int m = 0; m < 4; ++m) {
+        u32x4 A[NTT];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * kDenseRow + m * 64);
+        for (int tt = 0; tt < NTT; ++tt) A[tt] = *(const u32x4*)(ab + tt * 16 * kDenseRow + m * 64);
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int rt = 0; rt < kDenseRT; ++rt)
 #pragma unroll
           for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-            for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] = mfma16(A[tt][m], B[rt][m][hl], acc[tt][rt]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          B[rt][m][0] = wp[rt][(gn * 8 + m * 2) * 64];
-          B[rt][m][1] = wp[rt][(gn * 8 + m * 2 + 1) * 64];
-        }
+            for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] = mfma16(A[tt], B[rt][m][hl], acc[tt][rt]);
       }
+#pragma unroll
+      for (int rt = 0; rt < kDenseRT; ++rt)
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl) B[rt][m][hl] = wp[rt][(gn * 8 + m * 2 + hl) * 64];
     }
     stage_store(ready, smem + ((g + 1) & 1) * kDenseBuf);
     __syncthreads();
@@ -186,7 +191,7 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
         const int64_t t = t0 + 16 * tt + 4 * q + j;
         if (t >= a.T) continue;
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
+        for (int rt = 0; rt < kDenseRT; ++rt) {
           const int r = row0 + 16 * rt + i16;
           if (r < a.N0)
             a.logits[t * a.N0 + r] = acc[tt][rt][j];
@@ -204,8 +209,8 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int rt = 0; rt < 2; ++rt)
-            tile[(16 * tt + 4 * q + j) * kOutStride + wave * 32 + 16 * rt + i16] = acc[tt][rt][j];
+          for (int rt = 0; rt < kDenseRT; ++rt)
+            tile[(16 * tt + 4 * q + j) * kOutStride + row0 - rb * kDenseRows + 16 * rt + i16] = acc[tt][rt][j];
     }
     __syncthreads();
     const int d = a.N0;
@@ -238,11 +243,11 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
 
 // Persistent blocks over units l = (row block l / TB, token tile l % TB); the
 // blocks of one XCD (block index mod 8) take a contiguous range of units, so
-// they share one row block's split weights in their L2.
+// they share one row block's split weights in their L2.  (32-token units, which
+// give small products a second block per CU, measured slower.)
 template <int EPI>
-__global__ __launch_bounds__(64 * kDenseWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void dense_gemm_kernel(DenseArgs a, const u32x4* w2, int N,
-                                                                        int Kp) {
+__global__ __launch_bounds__(64 * kDenseWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void dense_gemm_kernel(DenseArgs a, const u32x4* w2, int N, int Kp) {
   extern __shared__ __align__(16) char smem[];
   const int64_t TB = (a.T + kDenseTok - 1) / kDenseTok;
   const int64_t U = TB * ((N + kDenseRows - 1) / kDenseRows);
