@@ -314,6 +314,17 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
   __syncthreads();
 
   const char* arow = xs + min(i16, it.n - 1) * stage_stride(K) + q * 16;
+  // PQ2_0 with a ring of two or more slots: the realigned window of the next
+  // group is taken from the ring one step ahead, so its shared-memory round trip
+  // overlaps this step's decode and products (ring slot j + 1 holds the next
+  // group; after the last slot, slot 0, refilled first, holds it).  A one-slot
+  // ring holds the next group only after this step's refill.
+  constexpr bool PF = CH && D > 1;
+  u32x3 win[RT];
+  if (PF && ntw > 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) win[r] = chunk_window<FMT>(ring[0][r], scratch, lane);
+  }
   for (int t = 0; t < ntw; ++t) {
     const bool more = t + 1 < ntw;
     f32x4 acc[RT], ptmp[RT];
@@ -341,8 +352,15 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
           u32x4 W[4];
-          const u32x3 v = CH ? chunk_window<FMT>(ring[j][r], scratch, lane)
-                             : u32x3{ring[j][r].x, ring[j][r].y, ring[j][r].z};
+          u32x3 v;
+          if (PF) {
+            v = win[r];
+            win[r] = chunk_window<FMT>(ring[(j + 1) % D][r], scratch, lane);
+          } else if (CH) {
+            v = chunk_window<FMT>(ring[j][r], scratch, lane);
+          } else {
+            v = u32x3{ring[j][r].x, ring[j][r].y, ring[j][r].z};
+          }
           ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
           const float s = decode_block_x3<FMT>(v, lut, lane, W);
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
@@ -725,7 +743,7 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 // NTT: token tiles of the item (a compile-time count keeps the multiply free of
 // branches).  The activations of group g + 1 are loaded while group g is
 // multiplied and staged after it.
-template <int FMT, int MODE, int NTT, int WAVES>
+template <int FMT, int MODE, int NTT, int WAVES, bool PIPE_A>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                           char* bufs, char* scratch) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -822,19 +840,49 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
         ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
       }
       const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
-#pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) {
+      if constexpr (PIPE_A) {
+        // A operands (token tile tt, slice m) in order i = 4 tt + m through a
+        // three-slot ring, each read two slices before its products, so the
+        // shared-memory latency overlaps the matrix work instead of preceding
+        // it.  Only the PQ2_0-only kernel: with the byte-table reads of
+        // PTQ1_0 (sharing the LDS and the registers) and in the kernel that
+        // holds both decoders it measured slower.
+        constexpr int NA = NTT * 4;
+        auto a_at = [&](int i) { return *(const u32x4*)(ab + (i >> 2) * 16 * kGemmRow + (i & 3) * 64); };
+        u32x4 Ar[3];
+        Ar[0] = a_at(0);
+        if (NA > 1) Ar[1] = a_at(1);
         f32x4 tmp[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < NA; ++i) {
+          if (i + 2 < NA) Ar[(i + 2) % 3] = a_at(i + 2);
+          const int tt = i >> 2, m = i & 3;
+          if (m == 0) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const u32x4 A = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+            for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A, W[rt][m], tmp[rt]);
+          for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(Ar[i % 3], W[rt][m], tmp[rt]);
+          if (m == 3) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+          }
         }
+      } else {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+        for (int tt = 0; tt < NTT; ++tt) {
+          f32x4 tmp[4];
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const u32x4 A = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A, W[rt][m], tmp[rt]);
+          }
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+        }
       }
     }
 #pragma unroll
@@ -884,9 +932,9 @@ template <int MODE, int FS, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                               char* bufs, bool ptq1) {
   if (FS != 1 && ptq1)
-    gemm_unit<kPTQ1, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPTQ1, MODE, NTT, WAVES, false>(a, it, rb, lut, bufs, nullptr);
   else if (FS != 2)
-    gemm_unit<kPQ2, MODE, NTT, WAVES>(a, it, rb, lut, bufs, nullptr);
+    gemm_unit<kPQ2, MODE, NTT, WAVES, FS == 1>(a, it, rb, lut, bufs, nullptr);
 }
 
 // Persistent blocks over units.  Unit l = (item l / row_blocks, row block
