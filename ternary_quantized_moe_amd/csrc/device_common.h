@@ -28,6 +28,10 @@ typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
 constexpr int kPQ2 = 142;
 constexpr int kPTQ1 = 143;
 constexpr int kLutCopies = 16;   // PTQ1_0 byte table copies (one per LDS bank pair)
+// Kernels with shared memory to spare keep 32 copies: a ds_read_b64 serves 32
+// lanes per cycle, and with lane % 32 as the copy no two of them share a bank
+// pair (with 16 copies lanes l and l + 16 collide when their bytes differ).
+constexpr int kLutCopiesWide = 32;
 
 // D = A(16x32) * B(32x16) + C, fp32 accumulate.  Lane l supplies row l%16 of A
 // and column l%16 of B for its k-slot quarter; D lane l holds column l%16, rows
@@ -108,16 +112,19 @@ __host__ __device__ constexpr Ptq1Table make_ptq1_table() {
 }
 __device__ constexpr Ptq1Table kPtq1Table = make_ptq1_table();
 
-// Fill the LDS byte table (all threads of the block take part; caller syncs).
+// Fill the LDS byte table of NC copies (all threads of the block take part;
+// caller syncs).
+template <int NC = kLutCopies>
 __device__ __forceinline__ void ptq1_lut_fill(u32x2* lut, int tid, int nthreads) {
-  for (int idx = tid; idx < 256 * kLutCopies; idx += nthreads) {
-    const int v = idx / kLutCopies;
+  for (int idx = tid; idx < 256 * NC; idx += nthreads) {
+    const int v = idx / NC;
     lut[idx] = u32x2{kPtq1Table.lo[v], kPtq1Table.hi[v]};
   }
 }
 
+template <int NC = kLutCopies>
 __device__ __forceinline__ u32x2 lut_get(const u32x2* lut, uint32_t v, int copy) {
-  return lut[v * kLutCopies + copy];
+  return lut[v * NC + copy];
 }
 
 // sel for perm_b32 building a bf16 pair from two table bytes: byte `a` of
@@ -127,15 +134,16 @@ __host__ __device__ constexpr uint32_t pair_sel(uint32_t a, uint32_t b) {
 }
 
 // d0, d1: block bytes 6q .. 6q+7; tail: block bytes 24 .. 27.
+template <int NC = kLutCopies>
 __device__ __forceinline__ void decode_ptq1(const u32x2* lut, int copy, uint32_t d0, uint32_t d1,
                                             uint32_t tail, int q, u32x4 out[4]) {
   u32x2 L[6];
 #pragma unroll
   for (int b = 0; b < 6; ++b) {
     const uint32_t src = b < 4 ? d0 : d1;
-    L[b] = lut_get(lut, (src >> (8 * (b & 3))) & 0xFFu, copy);
+    L[b] = lut_get<NC>(lut, (src >> (8 * (b & 3))) & 0xFFu, copy);
   }
-  const u32x2 Lt = lut_get(lut, (tail >> (8 * (q >> 1))) & 0xFFu, copy);
+  const u32x2 Lt = lut_get<NC>(lut, (tail >> (8 * (q >> 1))) & 0xFFu, copy);
   uint32_t P[16];
 #pragma unroll
   for (int bp = 0; bp < 3; ++bp) {
@@ -187,7 +195,7 @@ __device__ __forceinline__ u32x3 load_block_x3_a4(const uint8_t* blk, int q) {
 // Decode one lane's quarter of a block fetched with load_block_x3 into the
 // B operands; returns the group scale.  The operands encode 2t, so results
 // carry a factor 2 that the caller removes once.
-template <int FMT>
+template <int FMT, int NC = kLutCopies>
 __device__ __forceinline__ float decode_block_x3(u32x3 v, const u32x2* lut, int lane, u32x4 out[4]) {
   const int q = lane >> 4;
   // PQ2_0: quarter 3's third dword holds bytes 32..35 (scale low half);
@@ -198,7 +206,7 @@ __device__ __forceinline__ float decode_block_x3(u32x3 v, const u32x2* lut, int 
     decode_pq2(v.x, v.y, out);
     return f16_to_f32(shared & 0xFFFFu);
   } else {
-    decode_ptq1(lut, lane % kLutCopies, v.x, v.y, shared, q, out);
+    decode_ptq1<NC>(lut, lane % NC, v.x, v.y, shared, q, out);
     return f16_to_f32(shared >> 16);
   }
 }

@@ -836,7 +836,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
       float sc[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        sc[rt] = decode_block_x3<FMT>(ring[rt], lut, lane, W[rt]);
+        sc[rt] = decode_block_x3<FMT, kLutCopiesWide>(ring[rt], lut, lane, W[rt]);
         ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
       }
       const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
@@ -946,10 +946,10 @@ template <int MODE, int FS, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expert_gemm_kernel(ExpertArgs a, int row_blocks) {
   extern __shared__ __align__(16) char smem[];
-  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopiesWide * 8 : 0;
   u32x2* lut = (u32x2*)smem;
   char* bufs = smem + lut_bytes;
-  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  if (a.fmt_mask & 2) ptq1_lut_fill<kLutCopiesWide>(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
   const int64_t U = (int64_t)(*a.n_items) * row_blocks;
   const int64_t per = (U + 7) / 8;
   for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
@@ -986,7 +986,7 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
-template <int FMT, int NTT, int G, bool CHK>
+template <int FMT, int NTT, int G, bool CHK, int NC>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                           char* scratch) {
   const int tid = opaque_tid();
@@ -1099,9 +1099,9 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
         if constexpr (CH) {
           const u32x3 v = window(ring[rt]);
           ring[rt] = fetch(rows[rt] + nxt);
-          sc = decode_block_x3<FMT>(v, lut, lane, W);
+          sc = decode_block_x3<FMT, NC>(v, lut, lane, W);
         } else {
-          sc = decode_block_x3<FMT>(ring[rt], lut, lane, W);
+          sc = decode_block_x3<FMT, NC>(ring[rt], lut, lane, W);
           ring[rt] = fetch(rows[rt] + nxt);
         }
         f32x4 tmp[NTT];
@@ -1146,28 +1146,28 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
   }
 }
 
-template <int FS, int NTT, int G>
+template <int FS, int NTT, int G, int NC>
 __device__ __forceinline__ void down_dispatch(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                               bool ptq1) {
   char* scratch = xs + kDownChunk * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
   if (FS != 1 && ptq1)
-    down_unit<kPTQ1, NTT, G, false>(a, it, lut, xs, scratch);
+    down_unit<kPTQ1, NTT, G, false, NC>(a, it, lut, xs, scratch);
   else if (FS != 2)
-    down_unit<kPQ2, NTT, G, FS == 1>(a, it, lut, xs, scratch);
+    down_unit<kPQ2, NTT, G, FS == 1, NC>(a, it, lut, xs, scratch);
 }
 
 // Persistent blocks over items, the blocks of one XCD taking a contiguous range
 // (so the items of one expert share its down weights in one L2).
 // Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][64 staged rows][64 slots][64 weights]
 // [per-wave chunk scratch]
-template <int FS, int G>
+template <int FS, int G, int NC>
 __global__ __launch_bounds__(64 * kDownWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void down_resident_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) char smem[];
-  const int lut_bytes = (a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0;
+  const int lut_bytes = (a.fmt_mask & 2) ? 256 * NC * 8 : 0;
   u32x2* lut = (u32x2*)smem;
   char* xs = smem + lut_bytes;
-  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  if (a.fmt_mask & 2) ptq1_lut_fill<NC>(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
   const int64_t U = *a.down_n_items;
   const int64_t per = (U + 7) / 8;
   for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
@@ -1178,10 +1178,10 @@ void down_resident_kernel(ExpertArgs a) {
     for (int h0 = 0; h0 < item.n; h0 += kDownChunk) {  // (down items hold at most kDownChunk positions)
       const Item it{item.bank, item.pos + h0, min(kDownChunk, item.n - h0), 0};
       switch ((it.n + 15) / 16) {
-        case 1: down_dispatch<FS, 1, G>(a, it, lut, xs, ptq1); break;
-        case 2: down_dispatch<FS, 2, G>(a, it, lut, xs, ptq1); break;
-        case 3: down_dispatch<FS, 3, G>(a, it, lut, xs, ptq1); break;
-        default: down_dispatch<FS, 4, G>(a, it, lut, xs, ptq1); break;
+        case 1: down_dispatch<FS, 1, G, NC>(a, it, lut, xs, ptq1); break;
+        case 2: down_dispatch<FS, 2, G, NC>(a, it, lut, xs, ptq1); break;
+        case 3: down_dispatch<FS, 3, G, NC>(a, it, lut, xs, ptq1); break;
+        default: down_dispatch<FS, 4, G, NC>(a, it, lut, xs, ptq1); break;
       }
     }
   }
@@ -1267,7 +1267,7 @@ template <int MODE, int FS, int WAVES>
 static hipError_t launch_gemm_fs(const ExpertArgs& a, int64_t max_items, hipStream_t stream) {
   const int N = MODE == MODE_GATEUP ? a.f : a.d;
   const int row_blocks = (N + gemm_rows(MODE, WAVES) - 1) / gemm_rows(MODE, WAVES);
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + 2 * (size_t)kGemmBuf;
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopiesWide * 8 : 0) + 2 * (size_t)kGemmBuf;
   auto kern = expert_gemm_kernel<MODE, FS, WAVES>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * WAVES, lds);
@@ -1284,9 +1284,9 @@ static hipError_t launch_gemm(const ExpertArgs& a, int64_t max_items, hipStream_
   return launch_gemm_fs<MODE, 3, kGemmWaves>(a, max_items, stream);
 }
 
-template <int FS, int G>
+template <int FS, int G, int NC>
 static hipError_t launch_down_resident_fs(const ExpertArgs& a, int64_t max_items, size_t lds, hipStream_t stream) {
-  auto kern = down_resident_kernel<FS, G>;
+  auto kern = down_resident_kernel<FS, G, NC>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kDownWaves, lds);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
@@ -1295,24 +1295,32 @@ static hipError_t launch_down_resident_fs(const ExpertArgs& a, int64_t max_items
   return hipGetLastError();
 }
 
+// wide: the byte table in kLutCopiesWide copies (layers with PTQ1_0 banks
+// whose staged rows leave room for it)
 template <int G>
-static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, size_t lds, hipStream_t stream) {
-  if (a.fmt_mask == 1) return launch_down_resident_fs<1, G>(a, max_items, lds, stream);
-  if (a.fmt_mask == 2) return launch_down_resident_fs<2, G>(a, max_items, lds, stream);
-  return launch_down_resident_fs<3, G>(a, max_items, lds, stream);
+static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, size_t lds, bool wide,
+                                       hipStream_t stream) {
+  if (a.fmt_mask == 1) return launch_down_resident_fs<1, G, kLutCopies>(a, max_items, lds, stream);
+  if (wide) {
+    if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopiesWide>(a, max_items, lds, stream);
+    return launch_down_resident_fs<3, G, kLutCopiesWide>(a, max_items, lds, stream);
+  }
+  if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopies>(a, max_items, lds, stream);
+  return launch_down_resident_fs<3, G, kLutCopies>(a, max_items, lds, stream);
 }
 
 // Down projection of a large batch: LDS-resident h rows where the shape is
 // compiled in and the rows fit, else the group-staged kernel.
 static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, hipStream_t s) {
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)kDownChunk * (stage_stride(a.f) + 8) +
-                     (size_t)kDownWaves * kChunkScratch;
+  const size_t rows = (size_t)kDownChunk * (stage_stride(a.f) + 8) + (size_t)kDownWaves * kChunkScratch;
+  const bool wide = (a.fmt_mask & 2) && 256 * kLutCopiesWide * 8 + rows <= 160 * 1024;
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * (wide ? kLutCopiesWide : kLutCopies) * 8 : 0) + rows;
   if (lds <= 160 * 1024) {
     switch (a.f / kGroup) {
-      case 8: return launch_down_resident<8>(a, mi, lds, s);
-      case 6: return launch_down_resident<6>(a, mi, lds, s);
-      case 4: return launch_down_resident<4>(a, mi, lds, s);
-      case 1: return launch_down_resident<1>(a, mi, lds, s);
+      case 8: return launch_down_resident<8>(a, mi, lds, wide, s);
+      case 6: return launch_down_resident<6>(a, mi, lds, wide, s);
+      case 4: return launch_down_resident<4>(a, mi, lds, wide, s);
+      case 1: return launch_down_resident<1>(a, mi, lds, wide, s);
       default: break;
     }
   }
