@@ -732,18 +732,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   __shared__ int wsum[16];
   const int e = threadIdx.x;
   const int E = a.E;
+  // the expert's per-block counts are read in batches of 32 with every load
+  // of a batch in flight (two passes: the total, then the bases), so a batch
+  // costs one memory round trip
+  constexpr int NBB = 32;
   int total = 0;
   if (e < E) {
-    // the expert's per-block counts, eight loads in flight at a time
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      int c[8];
+    for (int b0 = 0; b0 < nb; b0 += NBB) {
+      int c[NBB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = b0 + j < nb ? a.block_cnt[(int64_t)(b0 + j) * E + e] : 0;
+      for (int j = 0; j < NBB; ++j) c[j] = b0 + j < nb ? a.block_cnt[(int64_t)(b0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (b0 + j < nb) a.block_base[(int64_t)(b0 + j) * E + e] = total;
-        total += c[j];
-      }
+      for (int j = 0; j < NBB; ++j) total += c[j];
     }
   }
   // exclusive scan of totals
@@ -752,13 +752,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(RouteArgs a, int nb) {
   if (e < E) {
     a.counts[e] = total;
     a.offsets[e] = off_e;
-    for (int b0 = 0; b0 < nb; b0 += 8) {
-      int v[8];
+    int run = off_e;
+    for (int b0 = 0; b0 < nb; b0 += NBB) {
+      int c[NBB];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = b0 + j < nb ? a.block_base[(int64_t)(b0 + j) * E + e] : 0;
+      for (int j = 0; j < NBB; ++j) c[j] = b0 + j < nb ? a.block_cnt[(int64_t)(b0 + j) * E + e] : 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (b0 + j < nb) a.block_base[(int64_t)(b0 + j) * E + e] = v[j] + off_e;
+      for (int j = 0; j < NBB; ++j) {
+        if (b0 + j < nb) a.block_base[(int64_t)(b0 + j) * E + e] = run;
+        run += c[j];
+      }
     }
   }
   if (e == 0) a.offsets[E] = (int)(a.T * a.k);
