@@ -869,19 +869,26 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
           }
         }
       } else {
+        // one slice ahead (two slots): the byte-table reads leave no room for more
+        constexpr int NA = NTT * 4;
+        auto a_at = [&](int i) { return *(const u32x4*)(ab + (i >> 2) * 16 * kGemmRow + (i & 3) * 64); };
+        u32x4 Ar[2];
+        Ar[0] = a_at(0);
+        f32x4 tmp[4];
 #pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) {
-          f32x4 tmp[4];
+        for (int i = 0; i < NA; ++i) {
+          if (i + 1 < NA) Ar[(i + 1) & 1] = a_at(i + 1);
+          const int tt = i >> 2, m = i & 3;
+          if (m == 0) {
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const u32x4 A = *(const u32x4*)(ab + tt * 16 * kGemmRow + m * 64);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A, W[rt][m], tmp[rt]);
+            for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+          for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(Ar[i & 1], W[rt][m], tmp[rt]);
+          if (m == 3) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+          }
         }
       }
     }
