@@ -46,6 +46,7 @@ struct Plan {
   int64_t logits, z, idx, w, rank, bcnt, bbase, counts, offsets, perm, items, nitems, items2, nitems2, wsplit, xpart,
       vpart, h, slots;
   int rd;  // rank of a factorised router delta, 0 for none
+  int chunk, chunk2;  // tokens per gate/up and per down work item (set_chunk for small batches)
   bool large;
   int64_t route_end, total;
 };
@@ -57,9 +58,12 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   p.Tk = T * k;
   p.n_pos = p.Tk + (int64_t)S * T;
   p.nb = (T + moe::kRouteBlock - 1) / moe::kRouteBlock;
-  const int64_t C = moe::item_chunk(T), C2 = moe::down_chunk(T);
+  p.chunk = moe::item_chunk(T);
+  p.chunk2 = moe::down_chunk(T);
+  // small batches: room for the smallest chunk set_chunk can choose
+  const int64_t C = T > moe::kGroupMaxT ? p.chunk : moe::kSmallChunkMin, C2 = p.chunk2;
   p.max_items = p.Tk / C + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C - 1) / C);
-  p.max_items2 = C2 == C ? p.max_items : p.Tk / C2 + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C2 - 1) / C2);
+  p.max_items2 = p.Tk / C2 + std::min<int64_t>(E, p.Tk) + (int64_t)S * ((T + C2 - 1) / C2);
   int64_t o = 0;
   p.logits = o; o += up(T * E * 4);
   p.idx = o; o += up(p.Tk * 4);
@@ -72,10 +76,10 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   p.perm = o; o += up(p.Tk * 4);
   p.items = o; o += up(std::max<int64_t>(p.max_items, 1) * (int64_t)sizeof(moe::Item));
   p.nitems = o; o += up(4);
-  // the down projection's own work items when they differ from gate/up's
+  // the down projection's own work items (when its chunk differs from gate/up's)
   p.items2 = o;
   p.nitems2 = o;
-  if (C2 != C) {
+  {
     o += up(std::max<int64_t>(p.max_items2, 1) * (int64_t)sizeof(moe::Item));
     p.nitems2 = o;
     o += up(4);
@@ -101,6 +105,15 @@ Plan make_plan(int64_t T, int d, int E, int S, int f, int k, int r, int rd = 0) 
   p.slots = o; o += up(p.n_pos * d * 2);
   p.total = o;
   return p;
+}
+
+// The work-item sizes of a small batch for this layer: gate/up small_chunk,
+// the down projection (whose staged rows are short) 16 tokens.  Up to four
+// tokens the items hold at most four tokens either way: one list.
+void set_chunk(Plan& p, int d, int E, int k, bool ptq1) {
+  if (p.large) return;
+  p.chunk = p.T <= moe::kTinyMaxT ? moe::kChunk : moe::small_chunk(p.T, d, E, k, ptq1);
+  p.chunk2 = moe::kChunk;
 }
 
 template <class T>
@@ -425,11 +438,11 @@ static int32_t route_impl(const uint16_t* x, int64_t T, int d, int E, int S, con
   ra.perm = perm;
   ra.items = at<moe::Item>(ws, p.items);
   ra.n_items = at<int32_t>(ws, p.nitems);
-  ra.chunk = moe::item_chunk(T);
-  if (moe::down_chunk(T) != ra.chunk) {
+  ra.chunk = p.chunk;
+  if (p.chunk2 != p.chunk) {
     ra.items2 = at<moe::Item>(ws, p.items2);
     ra.n_items2 = at<int32_t>(ws, p.nitems2);
-    ra.chunk2 = moe::down_chunk(T);
+    ra.chunk2 = p.chunk2;
   }
   if (!p.large) {  // the routing adds up the partials: the logits, and z for the combine
     ra.lpart = da.part;
@@ -542,9 +555,12 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     if (x == y) return fail(MOE_E_ARG, "y must not alias x");
     if ((uintptr_t)ws % kAlign) return fail(MOE_E_ARG, "workspace must be 256-byte aligned");
     if ((uintptr_t)x % 16 || (uintptr_t)y % 4) return fail(MOE_E_ARG, "x must be 16-byte and y 4-byte aligned");
-    const Plan p = make_plan(T, d, E, S, f, k, r, rd);
+    Plan p = make_plan(T, d, E, S, f, k, r, rd);
     if (ws_bytes < p.total)
       return fail(MOE_E_SPACE, "workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)p.total);
+    bool any_ptq1 = false;
+    for (int e = 0; e < E + S; ++e) any_ptq1 |= banks->formats_host[e] != MOE_PQ2_0;
+    set_chunk(p, d, E, k, any_ptq1);
     const hipStream_t st = (hipStream_t)stream;
     // up to four tokens: the gate/up kernel routes the batch itself and the
     // down projection carries the combine (three launches instead of five)
@@ -570,7 +586,7 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     ea.Tk = T * k;
     ea.items = at<moe::Item>(ws, p.items);
     ea.n_items = at<int32_t>(ws, p.nitems);
-    const bool two_lists = moe::down_chunk(T) != moe::item_chunk(T);
+    const bool two_lists = p.chunk2 != p.chunk;
     ea.down_items = two_lists ? at<moe::Item>(ws, p.items2) : ea.items;
     ea.down_n_items = two_lists ? at<int32_t>(ws, p.nitems2) : ea.n_items;
     ea.perm = at<int32_t>(ws, p.perm);
@@ -578,7 +594,7 @@ static int32_t forward_impl(const uint16_t* x, int64_t T, const uint16_t* router
     ea.x = x;
     ea.h = at<uint16_t>(ws, p.h);
     ea.slots = at<uint16_t>(ws, p.slots);
-    ea.chunk = moe::item_chunk(T);
+    ea.chunk = p.chunk;
     ea.nmax = (int)std::min<int64_t>(T, ea.chunk);
     ea.fmt_mask = 0;
     for (int e = 0; e < E + S; ++e) ea.fmt_mask |= banks->formats_host[e] == MOE_PQ2_0 ? 1 : 2;

@@ -1220,7 +1220,7 @@ constexpr double kCoResidentGain = 1.4;  // streaming blocks sharing a CU, measu
 static double expected_items(const ExpertArgs& a) {
   const double slots = (double)a.T * a.k;
   const double touched = a.E * (1.0 - std::exp(-slots / a.E));
-  return std::max(touched, slots / kChunk) + (double)a.S * ((a.T + kChunk - 1) / kChunk);
+  return std::max(touched, slots / a.chunk) + (double)a.S * ((a.T + a.chunk - 1) / a.chunk);
 }
 
 template <int MODE, int WPB, int RT, int D, int G, int FS, int WPE>
@@ -1347,7 +1347,9 @@ static hipError_t launch_gateup(const ExpertArgs& a, int64_t mi, bool small, hip
     }
   }
   switch (G) {
-    case 24: return launch_stream<MODE_GATEUP, 8, 2, 8, 24>(a, mi, s);
+    case 24:  // up to 4 tokens per item: two blocks per CU fit beside the byte table
+      if (a.nmax <= kSmallChunkMin) return launch_stream<MODE_GATEUP, 8, 2, 4, 24, 4>(a, mi, s);
+      return launch_stream<MODE_GATEUP, 8, 2, 8, 24>(a, mi, s);
     case 16:  // PQ2_0-only layers: two blocks per CU at 128 registers (no byte table)
       if (a.fmt_mask == 1) return launch_stream_fs<MODE_GATEUP, 8, 2, 4, 16, 1, 4>(a, mi, s);
       return launch_stream<MODE_GATEUP, 8, 2, 8, 16>(a, mi, s);
@@ -1374,7 +1376,7 @@ static hipError_t launch_down(const ExpertArgs& a, int64_t mi, bool small, hipSt
     case 6:
       if (a.fmt_mask == 1) return launch_stream_fs<MODE_DOWN, 8, 2, 3, 6, 1, 4>(a, mi, s);
       return launch_stream<MODE_DOWN, 8, 4, 3, 6>(a, mi, s);
-    case 4: return launch_stream<MODE_DOWN, 8, 4, 4, 4>(a, mi, s);
+    case 4: return launch_stream<MODE_DOWN, 8, 2, 4, 4, 4>(a, mi, s);  // two blocks per CU beside the byte table
     case 1: return launch_stream<MODE_DOWN, 8, 4, 1, 1>(a, mi, s);
     default: return launch_dec<MODE_DOWN, 8, 1, 4, 4, 0>(a, mi, s);
   }
@@ -1452,8 +1454,19 @@ hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, int64_t max_do
     e = gemm ? launch_gemm<MODE_GATEUP>(a, max_items, stream) : launch_gateup(a, max_items, small, stream);
   if (e == hipSuccess) e = mark(5);
   if (e == hipSuccess) e = mark(6);
-  if (e == hipSuccess)
-    e = gemm ? launch_down_large(a, max_down_items, stream) : launch_down(a, max_items, small, stream);
+  if (e == hipSuccess) {
+    if (gemm) {
+      e = launch_down_large(a, max_down_items, stream);
+    } else {
+      // the down projection's own items (16 tokens) where gate/up takes smaller ones
+      ExpertArgs d = a;
+      d.items = a.down_items;
+      d.n_items = a.down_n_items;
+      d.chunk = kChunk;
+      d.nmax = (int)std::min<int64_t>(a.T, kChunk);
+      e = launch_down(d, max_down_items, small, stream);
+    }
+  }
   if (e == hipSuccess) e = mark(7);
   return e;
 }

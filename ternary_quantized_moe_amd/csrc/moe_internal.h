@@ -22,6 +22,20 @@ __host__ __device__ inline int item_chunk(int64_t T) { return T > kGroupMaxT ? k
 // work items of that size.
 constexpr int kDownChunk = 64;
 __host__ __device__ inline int down_chunk(int64_t T) { return T > kGroupMaxT ? kDownChunk : kChunk; }
+// Small batches take 4-token work items where a streaming block with 16 staged
+// token rows (2 d + 16 bytes each) and the PTQ1_0 byte table would fill more
+// than half of a CU's 160 KB of LDS, but four rows leave room for two blocks,
+// and the batch puts at most two tokens per expert on average (so few items
+// split: mostly the shared experts' tokens).  The workspace is sized for this
+// smallest chunk, so its size does not depend on the bank formats.
+constexpr int kSmallChunkMin = 4;
+inline int small_chunk(int64_t T, int d, int E, int k, bool ptq1) {
+  const int64_t lut = ptq1 ? 256 * 16 * 8 : 0, rest = 8 * 1024 + 256;  // byte table; chunk scratch, slot table
+  const int64_t row = 2 * (int64_t)d + 16;
+  if (16 * row + lut + rest <= 80 * 1024) return kChunk;
+  if (4 * row + lut + rest <= 80 * 1024 && T * k <= 2 * (int64_t)E) return kSmallChunkMin;
+  return kChunk;
+}
 
 // Work item of the grouped expert kernels: bank, first position in the
 // (expert, token)-ordered slot space, number of tokens (<= item_chunk(T)).
@@ -106,7 +120,7 @@ struct RouteArgs {
   int32_t* perm;        // [T x k]
   Item* items;          // [max_items]
   int32_t* n_items;     // [1]
-  int chunk;            // tokens per work item, item_chunk(T)
+  int chunk;            // tokens per work item (item_chunk(T), or small_chunk for small batches)
   // NULL, or a second list of work items of chunk2 positions (the down
   // projection's, for large batches)
   Item* items2;
@@ -140,7 +154,7 @@ struct ExpertArgs {
   uint16_t* h;         // bf16 [(Tk + S*T) x f]
   uint16_t* slots;     // bf16 [(Tk + S*T) x d]
   int nmax;            // most tokens any work item holds (<= chunk)
-  int chunk;           // tokens per work item, item_chunk(T)
+  int chunk;           // tokens per work item (item_chunk(T), or small_chunk for small batches)
   int fmt_mask;        // 1: some bank is PQ2_0, 2: some bank is PTQ1_0
 };
 

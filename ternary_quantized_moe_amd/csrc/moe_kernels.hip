@@ -782,8 +782,8 @@ __global__ __launch_bounds__(256) void scatter_kernel(RouteArgs a) {
 
 // Grouping of a small batch (T <= kGroupMaxT) in one block: per-expert counts,
 // offsets, ranks (ballot masks per 64-token chunk, the same order rule as the
-// multi-block path), permutation and work items of kChunk tokens (item_chunk(T)
-// for such a batch).  PER = 0: after topk_kernel.  PER > 0 (T <= kFusedMaxT
+// multi-block path), permutation and work items of a.chunk tokens (and of
+// a.chunk2 for the down projection when a.items2 is set).  PER = 0: after topk_kernel.  PER > 0 (T <= kFusedMaxT
 // and T k <= kFusedMaxSlots): the block's 16 waves first select the top k of
 // the tokens themselves, keeping the indices in LDS, which saves a launch.
 constexpr int kFusedMaxT = 16;  // one token per wave: beyond that one CU does too much of the top-k
@@ -827,28 +827,10 @@ __global__ __launch_bounds__(1024) void group_small_kernel(RouteArgs a) {
     a.offsets[e] = off_e;
   }
   if (e == 0) a.offsets[E] = T * k;
-  const int chunks = e < E ? (total + kChunk - 1) / kChunk : 0;
-  int routed_items;
-  const int istart = block_inclusive_scan(chunks, wsum, &routed_items) - chunks;
-  for (int c = 0; c < chunks; ++c) {
-    Item it;
-    it.bank = e;
-    it.pos = off_e + c * kChunk;
-    it.n = min(kChunk, total - c * kChunk);
-    it.pad = 0;
-    a.items[istart + c] = it;
-  }
-  const int per_shared = (T + kChunk - 1) / kChunk;
-  for (int idx = e; idx < a.S * per_shared; idx += 1024) {
-    const int sh = idx / per_shared, c = idx % per_shared;
-    Item it;
-    it.bank = E + sh;
-    it.pos = T * k + sh * T + c * kChunk;
-    it.n = min(kChunk, T - c * kChunk);
-    it.pad = 0;
-    a.items[routed_items + idx] = it;
-  }
-  if (e == 0) *a.n_items = routed_items + a.S * per_shared;
+  // work items of a.chunk tokens, and (when asked for) the down projection's
+  // of a.chunk2
+  emit_items(a, e, total, off_e, a.chunk, a.items, a.n_items, wsum);
+  if (a.items2) emit_items(a, e, total, off_e, a.chunk2, a.items2, a.n_items2, wsum);
   __syncthreads();
   scan_buf[e] = off_e;
   __syncthreads();
