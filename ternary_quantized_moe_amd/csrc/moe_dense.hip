@@ -83,7 +83,10 @@ __global__ __launch_bounds__(256) void split_kernel(DenseArgs a, int N, int Kp, 
 template <int EPI, int NTT>
 __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __restrict__ w2, int N, int Kp,
                                            int64_t t0, int rb, char* smem) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane: the compiler then knows it (and
+  // `active`) to be uniform, so the branch on it is scalar and does not break
+  // the counting of loads in flight
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, q = lane >> 4;
   const int G = Kp / kGroup;
   const int row0 = rb * kDenseRows + wave * 16 * kDenseRT;
@@ -109,18 +112,22 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
     sc[pp] = u & 15;
     srow[pp] = a.act + std::min<int64_t>(t0 + si[pp], a.T - 1) * a.lda;
   }
+  // Every lane stages (rows past the unit's tokens repeat the last token and
+  // are not read), with no branch: loads under a lane condition would make the
+  // compiler wait for every load in flight, the next group's weights included,
+  // before each staging store.  K is a multiple of 8 (of 128 but for the
+  // combine's K = r, whose tail past K is zero-filled by the compare).
   auto stage_load = [&](int g, u32x4 (&raw)[kDenseP]) {
 #pragma unroll
-    for (int pp = 0; pp < kDenseP; ++pp)
-      if (si[pp] < NTT * 16) {
-        const int k = g * kGroup + 8 * sc[pp];
-        raw[pp] = k < a.K ? *(const u32x4*)(srow[pp] + k) : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int pp = 0; pp < kDenseP; ++pp) {
+      const int k = g * kGroup + 8 * sc[pp];
+      const u32x4 v = *(const u32x4*)(srow[pp] + min(k, a.K - 8));
+      raw[pp] = k < a.K ? v : u32x4{0u, 0u, 0u, 0u};
+    }
   };
   auto stage_store = [&](const u32x4 (&raw)[kDenseP], char* buf) {
 #pragma unroll
-    for (int pp = 0; pp < kDenseP; ++pp)
-      if (si[pp] < NTT * 16) *(u32x4*)(buf + si[pp] * kDenseRow + sc[pp] * 16) = raw[pp];
+    for (int pp = 0; pp < kDenseP; ++pp) *(u32x4*)(buf + si[pp] * kDenseRow + sc[pp] * 16) = raw[pp];
   };
 
   u32x4 B[kDenseRT][4][2];  // [row tile][m][hi, lo] of the next group
@@ -134,9 +141,11 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
   }
   u32x4 s0[kDenseP], s1[kDenseP];  // staged loads of the next two groups
   __syncthreads();  // the previous unit is done with the shared memory
-  stage_load(0, s0);
-  stage_store(s0, smem);
-  stage_load(min(1, G - 1), s1);
+  if (G > 0) {      // (K = 0: a combine without correction, the slots alone)
+    stage_load(0, s0);
+    stage_store(s0, smem);
+    stage_load(min(1, G - 1), s1);
+  }
   __syncthreads();
 
   f32x4 acc[NTT][kDenseRT];

@@ -746,7 +746,9 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 template <int FMT, int MODE, int NTT, int WAVES, bool PIPE_A>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                           char* bufs, char* scratch) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane, so branches on it are scalar (a
+  // lane-divergent branch makes the compiler wait for every load in flight)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, q = lane >> 4;
   const int K = MODE == MODE_GATEUP ? a.d : a.f;
   const int G = K / kGroup;
@@ -779,18 +781,20 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   auto fetch = [&](const uint8_t* p) -> RingT { return load_block_x3<FMT>(p, q); };
 
   // staging roles of the thread: token row si, quarter sq, half sh of the
-  // kGemmChunk x 8 half quarters of a group
+  // kGemmChunk x 8 half quarters of a group.  Every thread stages, with no
+  // branch (a lane condition would make every staging store wait for all loads
+  // in flight, the next group's weights included): rows past the item repeat
+  // its last row, and threads past the buffer's last row repeat that row's
+  // work (the same values to the same place); rows past NTT tiles are not read.
   constexpr int P = (kGemmChunk * 8 + 64 * WAVES - 1) / (64 * WAVES);
   int si[P], sq[P], sh[P];
-  bool stage_on[P];
   const uint16_t* srow[P];
 #pragma unroll
   for (int pp = 0; pp < P; ++pp) {
     const int u = threadIdx.x + pp * 64 * WAVES;
-    si[pp] = u >> 3;
+    si[pp] = min(u >> 3, kGemmChunk - 1);
     sq[pp] = (u >> 1) & 3;
     sh[pp] = u & 1;
-    stage_on[pp] = si[pp] < NTT * 16;  // (NTT * 16 <= kGemmChunk)
     const int64_t p = it.pos + min(si[pp], it.n - 1);  // rows past the item repeat its last row
     if (MODE == MODE_GATEUP) {
       const int64_t tok = p < a.Tk ? a.perm[p] / a.k : (p - a.Tk) % a.T;
@@ -810,11 +814,10 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   u32x4 s0[P][2];  // staged loads in flight
   __syncthreads();  // the previous unit is done with the staging buffers
 #pragma unroll
-  for (int pp = 0; pp < P; ++pp)
-    if (stage_on[pp]) {
-      act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], s0[pp]);
-      act_half_store<FMT>(s0[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
-    }
+  for (int pp = 0; pp < P; ++pp) {
+    act_half_load<FMT>(srow[pp], 0, sq[pp], sh[pp], s0[pp]);
+    act_half_store<FMT>(s0[pp], bufs + si[pp] * kGemmRow, sq[pp], sh[pp]);
+  }
   __syncthreads();
 
   f32x4 acc[NTT][4];
@@ -828,8 +831,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
   for (int g = 0; g < G; ++g) {
     const int gn = min(g + 1, G - 1);
 #pragma unroll
-    for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp]) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
+    for (int pp = 0; pp < P; ++pp) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
     if (active) {
       // the group's 4 row tiles, decoded once
       u32x4 W[4][4];
@@ -894,8 +896,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
     }
 #pragma unroll
     for (int pp = 0; pp < P; ++pp)
-      if (stage_on[pp])
-        act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
+      act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
     __syncthreads();
   }
   if (!active) return;
