@@ -88,7 +88,7 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Item& it, 
 template <int FMT, int MODE, int WPB, int KS, int RT, int D, int GW>
 __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it, int tblock, const u32x2* lut,
                                             char* xs, f32x4* red, int* slot_of, float* wgt_of) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar rows
   const int i16 = lane & 15, q = lane >> 4;
   const int K = MODE == MODE_GATEUP ? a.d : a.f;
   const int G = K / kGroup;
@@ -176,13 +176,13 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
         for (int j = 0; j < D; ++j) {
           const int i = i0 + j;
           if (i >= n) break;
-          u32x3 cur[RT];
-#pragma unroll
-          for (int r = 0; r < RT; ++r) cur[r] = ring[j][r];
+          // the slot is used before it is refilled: in this rolled loop a refill
+          // while the old value is live would move the ring through copies at
+          // every turn, each waiting for all loads in flight
+          step(i, ring[j]);
           if (i + D < n)
 #pragma unroll
             for (int r = 0; r < RT; ++r) ring[j][r] = fetch(rows[r] + (int64_t)(i + D) * 16 * BB);
-          step(i, cur);
         }
       }
     }
@@ -268,7 +268,11 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
                                                    const u32x2* lut, char* xs, char* scratch, int* slot_of,
                                                    float* wgt_of) {
   static_assert(G % D == 0 && D <= G, "the ring depth must divide the group count");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index through readfirstlane: the rows are then scalar, the loads
+  // take a scalar base and a fixed lane offset, and no refill overwrites a
+  // register that a later address needs (which made the compiler wait for every
+  // load in flight at each ring turn)
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, q = lane >> 4;
   constexpr int K = G * kGroup;
   constexpr int BB = block_bytes_c<FMT>();
@@ -361,8 +365,18 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
           } else {
             v = u32x3{ring[j][r].x, ring[j][r].y, ring[j][r].z};
           }
-          ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
-          const float s = decode_block_x3<FMT>(v, lut, lane, W);
+          float s;
+          if (CH) {
+            ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
+            s = decode_block_x3<FMT>(v, lut, lane, W);
+          } else {
+            // PTQ1_0 decodes the slot before refilling it: with the old value
+            // dead at the refill, the load lands in the slot's own registers and
+            // the ring needs no copies (and no wait for every load) at its turn
+            s = decode_block_x3<FMT>(v, lut, lane, W);
+            __builtin_amdgcn_sched_barrier(0);
+            ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
+          }
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
