@@ -43,10 +43,14 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16, rounded to nearest even (NaN stays a quiet NaN): CDNA4 converts
+// in one instruction, two values at a time in the packed form
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// the pair (lo, hi) as one packed word, lo in the low half
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float f16_to_f32(uint32_t h) {
@@ -274,10 +278,9 @@ __device__ __forceinline__ void split_sum_f16x8(u32x4 w, u32x4 v, u32x4& hi, u32
   for (int i = 0; i < 4; ++i) {
     const float a = f16_to_f32(w[i] & 0xFFFFu) + f16_to_f32(v[i] & 0xFFFFu);
     const float b = f16_to_f32(w[i] >> 16) + f16_to_f32(v[i] >> 16);
-    const uint32_t ha = f32_to_bf16(a), hb = f32_to_bf16(b);
-    const uint32_t la = f32_to_bf16(a - bf16_to_f32(ha)), lb = f32_to_bf16(b - bf16_to_f32(hb));
-    hi[i] = ha | (hb << 16);
-    lo[i] = la | (lb << 16);
+    const uint32_t h = f32x2_to_bf16x2(a, b);
+    hi[i] = h;
+    lo[i] = f32x2_to_bf16x2(a - bf16_to_f32(h & 0xFFFFu), b - bf16_to_f32(h >> 16));
   }
 }
 

@@ -244,7 +244,7 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
       for (int s = 0; s < a.n_shared; ++s) add(Tk + s * a.T + t);
       u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(v[2 * e]) | (f32_to_bf16(v[2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
       *(u32x4_a4*)(a.y + t * d + n0) = o;
     }
   }

@@ -1012,23 +1012,25 @@ template <int FMT, int NTT, int G, bool CHK, int NC>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                           char* scratch) {
   const int tid = opaque_tid();
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i16 = lane & 15, q = lane >> 4;
   constexpr int K = G * kGroup;
   constexpr int stride = stage_stride(K);
   constexpr int BB = block_bytes_c<FMT>();
   constexpr int64_t row_bytes = (int64_t)G * BB;
-  constexpr int D = 1;  // groups in flight (D = 2 takes 12 more registers than the wave has)
+  constexpr int D = 1;  // groups in flight (two spill at four token tiles)
   const uint8_t* bank = a.banks + a.offsets[it.bank];
   const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
   const int nquads = a.d / 64;
   const int nqw = wave < nquads ? (nquads - wave + kDownWaves - 1) / kDownWaves : 0;
   constexpr int64_t quad_stride = (int64_t)64 * kDownWaves * row_bytes;
 
+  // the tiles' bases are wave-uniform (scalar registers); the window path adds
+  // the lane's row at each load
   const uint8_t* rows[4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)  // chunk path: the tile's base; window path: the lane's row
-    rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt) * row_bytes + (CHK && FMT == kPQ2 ? 0 : i16 * BB);
+  for (int rt = 0; rt < 4; ++rt) rows[rt] = bank + 2 * gu_bytes + (int64_t)(wave * 64 + 16 * rt) * row_bytes;
+  const uint32_t lane_row = CHK && FMT == kPQ2 ? 0u : (uint32_t)(i16 * BB);
   // CHK (kernels for PQ2_0-only layers): aligned chunk pieces rearranged
   // through the wave's LDS scratch; otherwise the lane's 12-byte window directly
   // (the PTQ1_0 decoder already leans on LDS, and the mixed kernel has no
@@ -1039,7 +1041,7 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     if constexpr (CH)
       return load_chunk<FMT>(chunk, lane);
     else
-      return load_block_x3<FMT>(chunk, q);
+      return load_block_x3<FMT>(chunk + lane_row, q);
   };
   auto window = [&](const RingT& r) -> u32x3 {
     if constexpr (CH)

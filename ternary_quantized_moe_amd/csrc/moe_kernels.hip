@@ -415,7 +415,7 @@ __global__ __launch_bounds__(256 * RTB) void combine_small_kernel(DenseArgs a) {
   }
   u32x4 o;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(v[2 * e]) | (f32_to_bf16(v[2 * e + 1]) << 16);
+  for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
   *(u32x4_a4*)(a.y + t * d + n0) = o;
 }
 
