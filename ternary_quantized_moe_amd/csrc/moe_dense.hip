@@ -232,16 +232,27 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
       float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = tile[tl * kOutStride + 8 * c + e];
-      auto add = [&](int64_t slot) {
-        const u32x4 s = *(const u32x4*)(a.slots + slot * d + n0);
+      // the token's slots (routed in rank order, then shared) in batches of 8
+      // loads in flight, added in slot order; slots past the last re-read it
+      const int ns = a.top_k + a.n_shared;
+      for (int i0 = 0; i0 < ns; i0 += 8) {
+        u32x4 sv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v[2 * e] += bf16_to_f32(s[e] & 0xFFFFu);
-          v[2 * e + 1] += bf16_to_f32(s[e] >> 16);
+        for (int u = 0; u < 8; ++u) {
+          const int i = min(i0 + u, ns - 1);
+          const int64_t slot = i < a.top_k ? t * a.top_k + i : Tk + (int64_t)(i - a.top_k) * a.T + t;
+          sv[u] = *(const u32x4*)(a.slots + slot * d + n0);
         }
-      };
-      for (int i = 0; i < a.top_k; ++i) add(t * a.top_k + i);
-      for (int s = 0; s < a.n_shared; ++s) add(Tk + s * a.T + t);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (i0 + u >= ns) break;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] += bf16_to_f32(sv[u][e] & 0xFFFFu);
+            v[2 * e + 1] += bf16_to_f32(sv[u][e] >> 16);
+          }
+        }
+      }
       u32x4 o;
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
