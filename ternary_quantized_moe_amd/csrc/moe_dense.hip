@@ -224,39 +224,62 @@ __device__ __forceinline__ void dense_unit(const DenseArgs& a, const u32x4* __re
     __syncthreads();
     const int d = a.N0;
     const int64_t Tk = a.T * a.top_k;
-    for (int item = threadIdx.x; item < NTT * 16 * (kDenseRows / 8); item += 64 * kDenseWaves) {
-      const int tl = item / (kDenseRows / 8), c = item % (kDenseRows / 8);
-      const int64_t t = t0 + tl;
-      const int n0 = rb * kDenseRows + 8 * c;
-      if (t >= a.T || n0 >= d) continue;
-      float v[8];
+    // a thread takes two items (a token's 8 consecutive rows) at a time and reads
+    // their slots (routed in rank order, then shared) in batches of 8 per item,
+    // 16 loads in flight, added in slot order.  Loads past the last slot, and
+    // those of an item past the tile, re-read a valid row and are not used.
+    constexpr int kItems = NTT * 16 * (kDenseRows / 8), kStep = 64 * kDenseWaves;
+    const int ns = a.top_k + a.n_shared;
+    for (int item = threadIdx.x; item < kItems; item += 2 * kStep) {
+      bool ok[2];
+      int64_t t[2];
+      int n0[2];
+      const uint16_t* rbase[2];  // routed slot i of the token: rbase + i d
+      const uint16_t* sbase[2];  // shared slot s: sbase + s T d
+      float v[2][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = tile[tl * kOutStride + 8 * c + e];
-      // the token's slots (routed in rank order, then shared) in batches of 8
-      // loads in flight, added in slot order; slots past the last re-read it
-      const int ns = a.top_k + a.n_shared;
+      for (int p = 0; p < 2; ++p) {
+        const int ip = item + p * kStep;
+        const int tl = ip / (kDenseRows / 8), c = ip % (kDenseRows / 8);
+        t[p] = t0 + tl;
+        n0[p] = rb * kDenseRows + 8 * c;
+        ok[p] = ip < kItems && t[p] < a.T && n0[p] < d;
+        const int64_t tc = ok[p] ? t[p] : t0;
+        const int nc = ok[p] ? n0[p] : rb * kDenseRows;
+        rbase[p] = a.slots + tc * a.top_k * d + nc;
+        sbase[p] = a.slots + (Tk + tc) * d + nc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[p][e] = ok[p] ? tile[(ok[p] ? tl : 0) * kOutStride + 8 * (ok[p] ? c : 0) + e] : 0.f;
+      }
       for (int i0 = 0; i0 < ns; i0 += 8) {
-        u32x4 sv[8];
+        u32x4 sv[8][2];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int i = min(i0 + u, ns - 1);
-          const int64_t slot = i < a.top_k ? t * a.top_k + i : Tk + (int64_t)(i - a.top_k) * a.T + t;
-          sv[u] = *(const u32x4*)(a.slots + slot * d + n0);
+          const int64_t off = i < a.top_k ? (int64_t)i * d : (int64_t)(i - a.top_k) * a.T * d;
+#pragma unroll
+          for (int p = 0; p < 2; ++p) sv[u][p] = *(const u32x4*)((i < a.top_k ? rbase[p] : sbase[p]) + off);
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           if (i0 + u >= ns) break;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] += bf16_to_f32(sv[u][e] & 0xFFFFu);
-            v[2 * e + 1] += bf16_to_f32(sv[u][e] >> 16);
-          }
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              v[p][2 * e] += bf16_to_f32(sv[u][p][e] & 0xFFFFu);
+              v[p][2 * e + 1] += bf16_to_f32(sv[u][p][e] >> 16);
+            }
         }
       }
-      u32x4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2(v[2 * e], v[2 * e + 1]);
-      *(u32x4_a4*)(a.y + t * d + n0) = o;
+      for (int p = 0; p < 2; ++p) {
+        if (!ok[p]) continue;
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = f32x2_to_bf16x2(v[p][2 * e], v[p][2 * e + 1]);
+        *(u32x4_a4*)(a.y + t[p] * d + n0[p]) = o;
+      }
     }
   }
 }

@@ -1008,7 +1008,7 @@ __device__ __forceinline__ int opaque_tid() {
   return t;
 }
 
-template <int FMT, int NTT, int G, bool CHK, int NC>
+template <int FMT, int NTT, int G, bool CHK, int NC, int CAP>
 __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                           char* scratch) {
   const int tid = opaque_tid();
@@ -1060,8 +1060,8 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
 
   // per token row: its slot and half its gate weight (the operands encode 2t),
   // read back through volatile pointers so the quad loop does not hold them
-  int* slot_of = (int*)(xs + kDownChunk * stride);
-  float* wgt_of = (float*)(slot_of + kDownChunk);
+  int* slot_of = (int*)(xs + CAP * stride);
+  float* wgt_of = (float*)(slot_of + CAP);
   __syncthreads();  // the previous unit is done with the staged rows
   if (tid < NTT * 16) {
     const int64_t p = it.pos + min(tid, it.n - 1);
@@ -1107,15 +1107,20 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // refill with group g + D of this quad, else of the next quad (the last
+    // quad refetches its own groups: in bounds, unused)
+    auto next_off = [&](int g) -> int64_t {
+      return g + D < G ? (int64_t)(g + D) * 16 * BB : (more ? quad_stride : 0) + (int64_t)(g + D - G) * 16 * BB;
+    };
+    // up to four token tiles: the step's A operands stay in registers while
+    // each row tile is decoded and multiplied
     auto step = [&](int g, RingT (&ring)[4]) {
       u32x4 A[NTT][4];
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
 #pragma unroll
         for (int m = 0; m < 4; ++m) A[tt][m] = *(const u32x4*)(ab + tt * 16 * stride + g * 256 + m * 64);
-      // refill with group g + D of this quad, else of the next quad (the last
-      // quad refetches its own groups: in bounds, unused)
-      const int64_t nxt = g + D < G ? (int64_t)(g + D) * 16 * BB : (more ? quad_stride : 0) + (int64_t)(g + D - G) * 16 * BB;
+      const int64_t nxt = next_off(g);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
         u32x4 W[4];
@@ -1139,10 +1144,49 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
         for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
       }
     };
+    // five or six token tiles: the step's four row tiles are decoded once and
+    // stay in registers while the token tiles are walked, the four shared-memory
+    // reads of each feeding 16 MFMAs (the same products, summed in the same order)
+    auto step_walk = [&](int g, RingT (&ring)[4]) {
+      u32x4 W[4][4];
+      float sc[4];
+      const int64_t nxt = next_off(g);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if constexpr (CH) {
+          const u32x3 v = window(ring[rt]);
+          ring[rt] = fetch(rows[rt] + nxt);
+          sc[rt] = decode_block_x3<FMT, NC>(v, lut, lane, W[rt]);
+        } else {
+          sc[rt] = decode_block_x3<FMT, NC>(ring[rt], lut, lane, W[rt]);
+          ring[rt] = fetch(rows[rt] + nxt);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) {
+        u32x4 A[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) A[m] = *(const u32x4*)(ab + tt * 16 * stride + g * 256 + m * 64);
+        f32x4 tmp[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A[m], W[rt][m], tmp[rt]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
+      }
+    };
 #pragma unroll 1
     for (int g = 0; g < G; g += D) {
-      step(g, ring0);
-      if (D == 2) step(g + 1, ring1);
+      if constexpr (NTT > 4) {
+        step_walk(g, ring0);
+        if (D == 2) step_walk(g + 1, ring1);
+      } else {
+        step(g, ring0);
+        if (D == 2) step(g + 1, ring1);
+      }
     }
     // lane holds positions it.pos + 16 tt + 4q + j, column i16 of each row tile
     const int row0 = (wave + t * kDownWaves) * 64;
@@ -1152,17 +1196,21 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     typedef const volatile float __attribute__((address_space(3))) lds_float;
     lds_int* vslot = (lds_int*)slot_of;
     lds_float* vwgt = (lds_float*)wgt_of;
+    // the lane's indices taken anew here, so the per-token tests and table
+    // addresses are not hoisted out of the quad loop, where they would hold
+    // registers (a pair per token) for the whole unit
+    const int el = opaque_tid() & 63, eq = el >> 4, ei = el & 15;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ti = 16 * tt + 4 * q + j;
+        const int ti = 16 * tt + 4 * eq + j;
         if (ti >= it.n) continue;
         const int64_t slot = vslot[ti];
         const float wgt = vwgt[ti];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
-          a.slots[slot * a.d + row0 + 16 * rt + i16] = (uint16_t)f32_to_bf16(wgt * acc[tt][rt][j]);
+          a.slots[slot * a.d + row0 + 16 * rt + ei] = (uint16_t)f32_to_bf16(wgt * acc[tt][rt][j]);
       }
     }
 #pragma unroll
@@ -1170,21 +1218,23 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
   }
 }
 
-template <int FS, int NTT, int G, int NC>
+template <int FS, int NTT, int G, int NC, int CAP>
 __device__ __forceinline__ void down_dispatch(const ExpertArgs& a, const Item& it, const u32x2* lut, char* xs,
                                               bool ptq1) {
-  char* scratch = xs + kDownChunk * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
+  char* scratch = xs + CAP * (stage_stride(G * kGroup) + 8) + (threadIdx.x >> 6) * kChunkScratch;
   if (FS != 1 && ptq1)
-    down_unit<kPTQ1, NTT, G, false, NC>(a, it, lut, xs, scratch);
+    down_unit<kPTQ1, NTT, G, false, NC, CAP>(a, it, lut, xs, scratch);
   else if (FS != 2)
-    down_unit<kPQ2, NTT, G, FS == 1, NC>(a, it, lut, xs, scratch);
+    down_unit<kPQ2, NTT, G, FS == 1, NC, CAP>(a, it, lut, xs, scratch);
 }
 
 // Persistent blocks over items, the blocks of one XCD taking a contiguous range
 // (so the items of one expert share its down weights in one L2).
-// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][64 staged rows][64 slots][64 weights]
+// CAP: staged rows, the most positions of a unit (64, or 96 where the items
+// hold up to six token tiles).
+// Dynamic LDS: [PTQ1_0 byte table if the layer has PTQ1_0 banks][CAP staged rows][CAP slots][CAP weights]
 // [per-wave chunk scratch]
-template <int FS, int G, int NC>
+template <int FS, int G, int NC, int CAP>
 __global__ __launch_bounds__(64 * kDownWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void down_resident_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) char smem[];
@@ -1199,13 +1249,15 @@ void down_resident_kernel(ExpertArgs a) {
     if (l >= U) continue;
     const Item item = a.down_items[l];
     const bool ptq1 = FS == 2 || (FS == 3 && a.formats[item.bank] == kPTQ1);
-    for (int h0 = 0; h0 < item.n; h0 += kDownChunk) {  // (down items hold at most kDownChunk positions)
-      const Item it{item.bank, item.pos + h0, min(kDownChunk, item.n - h0), 0};
+    for (int h0 = 0; h0 < item.n; h0 += CAP) {  // (the items hold at most CAP positions)
+      const Item it{item.bank, item.pos + h0, min(CAP, item.n - h0), 0};
       switch ((it.n + 15) / 16) {
-        case 1: down_dispatch<FS, 1, G, NC>(a, it, lut, xs, ptq1); break;
-        case 2: down_dispatch<FS, 2, G, NC>(a, it, lut, xs, ptq1); break;
-        case 3: down_dispatch<FS, 3, G, NC>(a, it, lut, xs, ptq1); break;
-        default: down_dispatch<FS, 4, G, NC>(a, it, lut, xs, ptq1); break;
+        case 1: down_dispatch<FS, 1, G, NC, CAP>(a, it, lut, xs, ptq1); break;
+        case 2: down_dispatch<FS, 2, G, NC, CAP>(a, it, lut, xs, ptq1); break;
+        case 3: down_dispatch<FS, 3, G, NC, CAP>(a, it, lut, xs, ptq1); break;
+        case 4: down_dispatch<FS, 4, G, NC, CAP>(a, it, lut, xs, ptq1); break;
+        case 5: if constexpr (CAP > 64) down_dispatch<FS, 5, G, NC, CAP>(a, it, lut, xs, ptq1); break;
+        default: if constexpr (CAP > 64) down_dispatch<FS, 6, G, NC, CAP>(a, it, lut, xs, ptq1); break;
       }
     }
   }
@@ -1308,9 +1360,9 @@ static hipError_t launch_gemm(const ExpertArgs& a, int64_t max_items, hipStream_
   return launch_gemm_fs<MODE, 3, kGemmWaves>(a, max_items, stream);
 }
 
-template <int FS, int G, int NC>
+template <int FS, int G, int NC, int CAP>
 static hipError_t launch_down_resident_fs(const ExpertArgs& a, int64_t max_items, size_t lds, hipStream_t stream) {
-  auto kern = down_resident_kernel<FS, G, NC>;
+  auto kern = down_resident_kernel<FS, G, NC, CAP>;
   int per_cu = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * kDownWaves, lds);
   if (e != hipSuccess || per_cu < 1) per_cu = 1;
@@ -1321,33 +1373,50 @@ static hipError_t launch_down_resident_fs(const ExpertArgs& a, int64_t max_items
 
 // wide: the byte table in kLutCopiesWide copies (layers with PTQ1_0 banks
 // whose staged rows leave room for it)
-template <int G>
+template <int G, int CAP>
 static hipError_t launch_down_resident(const ExpertArgs& a, int64_t max_items, size_t lds, bool wide,
                                        hipStream_t stream) {
-  if (a.fmt_mask == 1) return launch_down_resident_fs<1, G, kLutCopies>(a, max_items, lds, stream);
+  if (a.fmt_mask == 1) return launch_down_resident_fs<1, G, kLutCopies, CAP>(a, max_items, lds, stream);
   if (wide) {
-    if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopiesWide>(a, max_items, lds, stream);
-    return launch_down_resident_fs<3, G, kLutCopiesWide>(a, max_items, lds, stream);
+    if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopiesWide, CAP>(a, max_items, lds, stream);
+    return launch_down_resident_fs<3, G, kLutCopiesWide, CAP>(a, max_items, lds, stream);
   }
-  if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopies>(a, max_items, lds, stream);
-  return launch_down_resident_fs<3, G, kLutCopies>(a, max_items, lds, stream);
+  if (a.fmt_mask == 2) return launch_down_resident_fs<2, G, kLutCopies, CAP>(a, max_items, lds, stream);
+  return launch_down_resident_fs<3, G, kLutCopies, CAP>(a, max_items, lds, stream);
+}
+
+template <int CAP>
+static hipError_t launch_down_cap(const ExpertArgs& a, int64_t mi, hipStream_t s) {
+  const size_t rows = (size_t)CAP * (stage_stride(a.f) + 8) + (size_t)kDownWaves * kChunkScratch;
+  const bool wide = (a.fmt_mask & 2) && 256 * kLutCopiesWide * 8 + rows <= 160 * 1024;
+  const size_t lds = ((a.fmt_mask & 2) ? 256 * (wide ? kLutCopiesWide : kLutCopies) * 8 : 0) + rows;
+  if (lds > 160 * 1024) return hipErrorNotSupported;
+  switch (a.f / kGroup) {
+    case 8: return launch_down_resident<8, CAP>(a, mi, lds, wide, s);
+    case 6: return launch_down_resident<6, CAP>(a, mi, lds, wide, s);
+    case 4: return launch_down_resident<4, CAP>(a, mi, lds, wide, s);
+    case 1: return launch_down_resident<1, CAP>(a, mi, lds, wide, s);
+    default: return hipErrorNotSupported;
+  }
 }
 
 // Down projection of a large batch: LDS-resident h rows where the shape is
-// compiled in and the rows fit, else the group-staged kernel.
-static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, hipStream_t s) {
-  const size_t rows = (size_t)kDownChunk * (stage_stride(a.f) + 8) + (size_t)kDownWaves * kChunkScratch;
-  const bool wide = (a.fmt_mask & 2) && 256 * kLutCopiesWide * 8 + rows <= 160 * 1024;
-  const size_t lds = ((a.fmt_mask & 2) ? 256 * (wide ? kLutCopiesWide : kLutCopies) * 8 : 0) + rows;
-  if (lds <= 160 * 1024) {
-    switch (a.f / kGroup) {
-      case 8: return launch_down_resident<8>(a, mi, lds, wide, s);
-      case 6: return launch_down_resident<6>(a, mi, lds, wide, s);
-      case 4: return launch_down_resident<4>(a, mi, lds, wide, s);
-      case 1: return launch_down_resident<1>(a, mi, lds, wide, s);
-      default: break;
-    }
+// compiled in and the rows fit, else the group-staged kernel.  The resident
+// kernel takes the gate/up items (up to 96 positions) where their rows fit in
+// shared memory: each weight group decoded then feeds up to six token tiles, and
+// an expert whose load is one such item streams its down weights once (measured
+// faster than 64-position units at every prefill shape here, skewed routing
+// included); else the down projection's own 64-position items.
+static hipError_t launch_down_large(const ExpertArgs& a, int64_t mi, int64_t mi_gateup, hipStream_t s) {
+  {
+    ExpertArgs g = a;
+    g.down_items = a.items;
+    g.down_n_items = a.n_items;
+    const hipError_t e = launch_down_cap<kGemmChunk>(g, mi_gateup, s);
+    if (e != hipErrorNotSupported) return e;
   }
+  const hipError_t e = launch_down_cap<kDownChunk>(a, mi, s);
+  if (e != hipErrorNotSupported) return e;
   return launch_gemm<MODE_DOWN>(a, mi, s);
 }
 
@@ -1473,7 +1542,7 @@ hipError_t launch_experts(const ExpertArgs& a, int64_t max_items, int64_t max_do
   if (e == hipSuccess) e = mark(6);
   if (e == hipSuccess) {
     if (gemm) {
-      e = launch_down_large(a, max_down_items, stream);
+      e = launch_down_large(a, max_down_items, max_items, stream);
     } else {
       // the down projection's own items (16 tokens) where gate/up takes smaller ones
       ExpertArgs d = a;

@@ -154,7 +154,8 @@ def sample_tokens(T, n, seed=0):
 
 # The large-batch expert kernels split each routed expert's run of slots in
 # the permutation (and each shared expert's tokens) into work items: of ITEM
-# positions for the gate/up projection, of HALF positions for the down one.
+# positions for the gate/up projection, and for the down one the same items
+# where their rows fit in shared memory, else items of HALF positions.
 ITEM, HALF = 96, 64
 
 
