@@ -720,16 +720,16 @@ __device__ __forceinline__ void act_half_load(const uint16_t* row, int g, int q,
     raw[0] = p[0];
     raw[1] = p[1];
   } else {
+    // the same three loads in every lane (a lane-dependent branch here would
+    // make the compiler wait for every load in flight before the staging
+    // stores): elements 30q + 16h .. + 15 of the group, and the quarter's tail
+    // pair (elements 120 + 2q, + 1), which half 1 takes in place of its last two
+    // (past the quarter's 30: up to element 121 of the group's 128)
     const uint16_t* p = row + g * 128 + 30 * q + 16 * h;  // 4-byte aligned
     raw[0] = *(const u32x4_a4*)p;
-    if (h == 0) {
-      raw[1] = *(const u32x4_a4*)(p + 8);
-    } else {
-      const u32x2 w = *(const u32x2_a4*)(p + 8);
-      const uint32_t w2 = *(const uint32_t*)(p + 12);
-      const uint32_t t = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
-      raw[1] = u32x4{w.x, w.y, w2, t};
-    }
+    const u32x4 v = *(const u32x4_a4*)(p + 8);
+    const uint32_t t = *(const uint32_t*)(row + g * 128 + 120 + 2 * q);
+    raw[1] = u32x4{v.x, v.y, v.z, h ? t : v.w};
   }
 }
 
@@ -846,15 +846,18 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
     const int gn = min(g + 1, G - 1);
 #pragma unroll
     for (int pp = 0; pp < P; ++pp) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
+    // the group's 4 row tiles, decoded once; then the next group's weights,
+    // fetched in every wave (an idle wave's rows are the bank's first, in
+    // bounds), so the waits before the staging stores count them exactly
+    u32x4 W[4][4];
+    float sc[4];
     if (active) {
-      // the group's 4 row tiles, decoded once
-      u32x4 W[4][4];
-      float sc[4];
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        sc[rt] = decode_block_x3<FMT, kLutCopiesWide>(ring[rt], lut, lane, W[rt]);
-        ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
-      }
+      for (int rt = 0; rt < 4; ++rt) sc[rt] = decode_block_x3<FMT, kLutCopiesWide>(ring[rt], lut, lane, W[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
+    if (active) {
       const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
       if constexpr (PIPE_A) {
         // A operands (token tile tt, slice m) in order i = 4 tt + m through a
