@@ -87,14 +87,15 @@ __device__ __forceinline__ void stage_rows(const ExpertArgs& a, const Item& it, 
 // ring, the load offsets and the LDS offsets are static.  GW = 0: any K.
 template <int FMT, int MODE, int WPB, int KS, int RT, int D, int GW>
 __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it, int tblock, const u32x2* lut,
-                                            char* xs, f32x4* red, int* slot_of, float* wgt_of) {
+                                            char* xs, f32x4* red, int* slot_of, float* wgt_of,
+                                            const uint8_t* bank_in = nullptr) {
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar rows
   const int i16 = lane & 15, q = lane >> 4;
   const int K = MODE == MODE_GATEUP ? a.d : a.f;
   const int G = K / kGroup;
   constexpr int BB = block_bytes_c<FMT>();
   const int64_t row_bytes = (int64_t)G * BB;
-  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const uint8_t* bank = bank_in ? bank_in : a.banks + a.offsets[it.bank];  // (the caller's, if given)
   const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
 
   constexpr int TPB = WPB / KS;  // tiles per block
@@ -473,6 +474,14 @@ __host__ __device__ constexpr int tiny_route_bytes(int T, int k, int E, int S) {
   return (T * E + 2 * T * k + 4) * 4 + (std::min(E, T * k) + S) * (int)sizeof(Item);
 }
 
+// The byte offsets and container formats of the layer's nb = E + S banks,
+// copied into LDS at the start of the small-batch kernels, where reading them
+// after the routing (or the work item) would add one dependent memory round
+// trip before the first weight load.  [offsets: nb int64][formats: nb bytes,
+// padded to 8]
+__host__ __device__ constexpr int bank_table_bytes(int nb) { return nb * 8 + ((nb + 7) & ~7); }
+__host__ __device__ constexpr int align8(int b) { return (b + 7) & ~7; }
+
 // The batch's top k per token (waves 0 .. T-1, one token each), then the
 // grouping by one wave with one slot per lane (T k <= 64): slot s of token
 // t = s / k and expert e sorts by the key 4 e + t, so its position in the
@@ -556,6 +565,14 @@ __global__ __launch_bounds__(64 * WPB) void expert_route_dec_kernel(ExpertArgs a
   float* wgt_of = (float*)(slot_of + a.nmax);
   f32x4* red = (f32x4*)(xs + a.nmax * stage_stride(K) + slot_table_bytes(a.nmax));
   char* area = (char*)red + (KS > 1 ? (WPB / KS) * (KS - 1) * RT * 64 * 16 : 0);
+  const int nbk = a.E + a.S;
+  int64_t* soff = (int64_t*)(area + align8(tiny_route_bytes((int)a.T, a.k, a.E, a.S)));
+  uint8_t* sfmt = (uint8_t*)(soff + nbk);
+  // the bank table's loads go out with the routing's own (visible after its syncs)
+  for (int i = threadIdx.x; i < nbk; i += blockDim.x) {
+    soff[i] = a.offsets[i];
+    sfmt[i] = a.formats[i];
+  }
   if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);  // visible after the routing's syncs
   const int* perm;
   const Item* items;
@@ -567,10 +584,11 @@ __global__ __launch_bounds__(64 * WPB) void expert_route_dec_kernel(ExpertArgs a
   for (int64_t u = blockIdx.x; u < units; u += route_blocks) {
     const Item it = items[u / tblocks_per_item];
     const int tb = (int)(u % tblocks_per_item);
-    if (la.formats[it.bank] == kPTQ1)
-      expert_unit<kPTQ1, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of);
+    const uint8_t* bank = a.banks + soff[it.bank];
+    if (sfmt[it.bank] == kPTQ1)
+      expert_unit<kPTQ1, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of, bank);
     else
-      expert_unit<kPQ2, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of);
+      expert_unit<kPQ2, MODE_GATEUP, WPB, KS, RT, D, GW>(la, it, tb, lut, xs, red, slot_of, wgt_of, bank);
   }
 }
 
@@ -586,14 +604,17 @@ __global__ __launch_bounds__(64 * WPB) void expert_route_dec_kernel(ExpertArgs a
 constexpr int kTinyDownWaves = 16;
 constexpr int kTinyGroups = 8;   // groups of the down rows whose loads are in flight together
 
+// soff: the bank offsets, sperm / swgt: the batch's permutation and gate weights
+// (T k entries), all in LDS.
 template <int FMT>
 __device__ __forceinline__ void tiny_down_piece(const ExpertArgs& a, const Item& it, int tile, const u32x2* lut,
-                                                float* part, int lane) {
+                                                float* part, int lane, const int64_t* soff, const int* sperm,
+                                                const float* swgt) {
   const int i16 = lane & 15, q = lane >> 4;
   const int G = a.f / kGroup;
   constexpr int BB = block_bytes_c<FMT>();
   const int64_t row_bytes = (int64_t)G * BB;
-  const uint8_t* bank = a.banks + a.offsets[it.bank];
+  const uint8_t* bank = a.banks + soff[it.bank];
   const int64_t gu_bytes = (int64_t)a.f * (a.d / kGroup) * BB;
   const uint8_t* wrow = bank + 2 * gu_bytes + (int64_t)tile * 16 * row_bytes + i16 * BB;
   const uint16_t* hrow = a.h + (int64_t)(it.pos + min(i16, it.n - 1)) * a.f;  // rows past the item repeat its last
@@ -626,8 +647,8 @@ __device__ __forceinline__ void tiny_down_piece(const ExpertArgs& a, const Item&
     if (ti >= it.n) continue;
     const int64_t p = it.pos + ti;
     const bool routed = p < a.Tk;
-    const int64_t slot = routed ? a.perm[p] : p;
-    const float w = routed ? a.topk_w[slot] : 1.f;
+    const int64_t slot = routed ? sperm[p] : p;
+    const float w = routed ? swgt[slot] : 1.f;
     part[slot * 16 + i16] = 0.5f * w * acc[j];
   }
 }
@@ -641,21 +662,39 @@ __global__ __launch_bounds__(64 * kTinyDownWaves) void down_combine_kernel(Exper
   const int n_slots = (int)a.Tk + a.S * T;
   float* part = (float*)(smem + lut_bytes);        // [slot][16 rows]
   float* partb = part + n_slots * 16;               // [B slice][token][16 rows]
-  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i16 = lane & 15, q = lane >> 4;
-  const int tile = blockIdx.x, n0 = tile * 16;
   const bool has_b = c.w0 || c.q0;
   const int nbs = has_b ? (r + 127) / 128 : 0;
+  const int nbk = a.E + a.S, Tk = (int)a.Tk;
+  int64_t* soff = (int64_t*)(partb + nbs * kTinyMaxT * 16);  // [bank offsets][formats][perm][gate weights]
+  uint8_t* sfmt = (uint8_t*)(soff + nbk);
+  int* sperm = (int*)((char*)soff + bank_table_bytes(nbk));
+  float* swgt = (float*)(sperm + Tk);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // every read the pieces depend on goes out at once, before the first barrier:
+  // the item count, each wave's first item (the workspace rounds the item list
+  // up to 256 bytes, so it holds at least kTinyDownWaves items; an entry past
+  // the count is not used), the bank table, the permutation and gate weights
   const int n_items = *a.n_items;
+  const Item first = a.items[wave];
+  for (int i = threadIdx.x; i < nbk; i += blockDim.x) {
+    soff[i] = a.offsets[i];
+    sfmt[i] = a.formats[i];
+  }
+  for (int i = threadIdx.x; i < Tk; i += blockDim.x) {
+    sperm[i] = a.perm[i];
+    swgt[i] = a.topk_w[i];
+  }
+  if (a.fmt_mask & 2) ptq1_lut_fill(lut, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const int i16 = lane & 15, q = lane >> 4;
+  const int tile = blockIdx.x, n0 = tile * 16;
   for (int pc = wave; pc < n_items + nbs; pc += kTinyDownWaves) {
     if (pc < n_items) {
-      const Item it = a.items[pc];
-      if (FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1))
-        tiny_down_piece<kPTQ1>(a, it, tile, lut, part, lane);
+      const Item it = pc == wave ? first : a.items[pc];
+      if (FS == 2 || (FS == 3 && sfmt[it.bank] == kPTQ1))
+        tiny_down_piece<kPTQ1>(a, it, tile, lut, part, lane, soff, sperm, swgt);
       else if (FS != 2)
-        tiny_down_piece<kPQ2>(a, it, tile, lut, part, lane);
+        tiny_down_piece<kPQ2>(a, it, tile, lut, part, lane, soff, sperm, swgt);
     } else {
       const int bs = pc - n_items;  // k-steps 4 bs .. 4 bs + 3 of B z
       const uint16_t* zrow = c.act + (int64_t)min(i16, T - 1) * c.lda;
@@ -1480,7 +1519,7 @@ static hipError_t launch_route_dec(const ExpertArgs& a, const RouteArgs& r, int6
   const int tbpi = (n_tiles + TPB - 1) / TPB;
   const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) + (size_t)a.nmax * stage_stride(K) +
                      slot_table_bytes(a.nmax) + (KS > 1 ? (size_t)TPB * (KS - 1) * RT * 64 * 16 : 0) +
-                     (size_t)tiny_route_bytes((int)a.T, a.k, a.E, a.S);
+                     (size_t)align8(tiny_route_bytes((int)a.T, a.k, a.E, a.S)) + (size_t)bank_table_bytes(a.E + a.S);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kern = expert_route_dec_kernel<WPB, KS, RT, D, GW, PER>;
   int per_cu = 0;
@@ -1519,7 +1558,8 @@ hipError_t launch_tiny(const ExpertArgs& a, const RouteArgs& r, const DenseArgs&
   if (e == hipSuccess) {
     const int nbs = (c.w0 || c.q0) ? (c.K + 127) / 128 : 0;
     const size_t lds = ((a.fmt_mask & 2) ? 256 * kLutCopies * 8 : 0) +
-                       (size_t)(a.Tk + (int64_t)a.S * a.T) * 16 * 4 + (size_t)nbs * kTinyMaxT * 16 * 4;
+                       (size_t)(a.Tk + (int64_t)a.S * a.T) * 16 * 4 + (size_t)nbs * kTinyMaxT * 16 * 4 +
+                       (size_t)bank_table_bytes(a.E + a.S) + (size_t)a.Tk * 8;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(a.d / 16));
     if (a.fmt_mask == 1) down_combine_kernel<1><<<grid, 64 * kTinyDownWaves, lds, stream>>>(a, c);
