@@ -269,10 +269,8 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
                                                    const u32x2* lut, char* xs, char* scratch, int* slot_of,
                                                    float* wgt_of) {
   static_assert(G % D == 0 && D <= G, "the ring depth must divide the group count");
-  // the wave index through readfirstlane: the rows are then scalar, the loads
-  // take a scalar base and a fixed lane offset, and no refill overwrites a
-  // register that a later address needs (which made the compiler wait for every
-  // load in flight at each ring turn)
+  // the wave index through readfirstlane, so the wave's row bases are known to
+  // be uniform (scalar registers, scalar branches)
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i16 = lane & 15, q = lane >> 4;
   constexpr int K = G * kGroup;
