@@ -30,7 +30,7 @@ constexpr int kDenseWaves = 8;
 constexpr int kDenseRT = 1;                             // row tiles per wave
 constexpr int kDenseRows = kDenseWaves * 16 * kDenseRT;  // weight rows per unit
 constexpr int kDenseTok = 64;                     // tokens per unit (4 MFMA M tiles)
-constexpr int kDenseRow = 256 + 16;               // staged bytes per token row and group
+constexpr int kDenseRow = 256 + 32;               // staged bytes per token row and group (32 bytes of padding: 16 left a third of the LDS cycles bank conflicts)
 constexpr int kDenseBuf = kDenseTok * kDenseRow;  // one staged group
 constexpr int kOutStride = kDenseRows + 4;        // floats per token row of the combine tile
 constexpr size_t kDenseLds = std::max<size_t>(2 * (size_t)kDenseBuf, (size_t)kDenseTok * kOutStride * 4);

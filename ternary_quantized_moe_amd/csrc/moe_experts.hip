@@ -39,9 +39,10 @@ constexpr int MODE_DOWN = 1;
 // Stage the item's activation rows (n tokens x K) into LDS as matrix-core A
 // operands in the container format's k-slot order: row i, group g, MFMA m,
 // quarter q -> 16 bytes at i * stride + ((g * 4 + m) * 4 + q) * 16.  The
-// 16-byte row padding puts the 16 token rows of one operand read on different
-// LDS banks.
-__host__ __device__ constexpr int stage_stride(int K) { return 2 * K + 16; }
+// rows are padded by 32 bytes (a row stride of 8 mod 64 dwords): with 16 bytes
+// the operand reads of lanes 16 apart (quarters q and q + 1) met on the same
+// banks, and the LDS counted a third of its cycles as bank conflicts.
+__host__ __device__ constexpr int stage_stride(int K) { return 2 * K + 32; }
 
 // Per-item table of the down projection, after the staged rows: each token
 // row's slot and half its gate weight (the operands encode 2t).  It is filled
@@ -743,7 +744,7 @@ __global__ __launch_bounds__(64 * kTinyDownWaves) void down_combine_kernel(Exper
 // group scale is applied to the token tile's fp32 partial sums.  One decoded
 // weight feeds up to 8 token tiles.  Blocks of 8 waves run one to a CU.
 constexpr int kGemmWaves = 8;
-constexpr int kGemmRow = 256 + 16;                // staged bytes per token row and group
+constexpr int kGemmRow = 256 + 32;                // staged bytes per token row and group (padded as stage_stride)
 constexpr int kGemmBuf = kGemmChunk * kGemmRow;   // one staged group
 constexpr int gemm_rows(int mode, int waves) { return waves * (mode == 0 ? 32 : 64); }  // per unit
 

@@ -23,7 +23,7 @@ __host__ __device__ inline int item_chunk(int64_t T) { return T > kGroupMaxT ? k
 constexpr int kDownChunk = 64;
 __host__ __device__ inline int down_chunk(int64_t T) { return T > kGroupMaxT ? kDownChunk : kChunk; }
 // Small batches take 4-token work items where a streaming block with 16 staged
-// token rows (2 d + 16 bytes each) and the PTQ1_0 byte table would fill more
+// token rows (2 d + 32 bytes each) and the PTQ1_0 byte table would fill more
 // than half of a CU's 160 KB of LDS, but four rows leave room for two blocks,
 // and the batch puts at most two tokens per expert on average (so few items
 // split: mostly the shared experts' tokens).  The workspace is sized for this
@@ -31,7 +31,7 @@ __host__ __device__ inline int down_chunk(int64_t T) { return T > kGroupMaxT ? k
 constexpr int kSmallChunkMin = 4;
 inline int small_chunk(int64_t T, int d, int E, int k, bool ptq1) {
   const int64_t lut = ptq1 ? 256 * 16 * 8 : 0, rest = 8 * 1024 + 256;  // byte table; chunk scratch, slot table
-  const int64_t row = 2 * (int64_t)d + 16;
+  const int64_t row = 2 * (int64_t)d + 32;
   if (16 * row + lut + rest <= 80 * 1024) return kChunk;
   if (4 * row + lut + rest <= 80 * 1024 && T * k <= 2 * (int64_t)E) return kSmallChunkMin;
   return kChunk;
