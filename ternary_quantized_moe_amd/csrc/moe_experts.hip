@@ -378,8 +378,12 @@ __device__ __forceinline__ void expert_stream_unit(const ExpertArgs& a, const It
             ring[j][r] = fetch(rows[r] + nxt + j * 16 * BB);
           }
           f32x4 tmp = {0.f, 0.f, 0.f, 0.f};
+          // the wave issues its products at a raised priority, so a wave of the
+          // SIMD that is ready to multiply goes ahead of the others' decode work
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int m = 0; m < 4; ++m) tmp = mfma16(A[m], W[m], tmp);
+          __builtin_amdgcn_s_setprio(0);
           if (PIPE) {
             acc[r] += ps[r] * ptmp[r];
             ptmp[r] = tmp;
