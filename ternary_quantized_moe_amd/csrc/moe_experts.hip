@@ -1181,10 +1181,14 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
         f32x4 tmp[NTT];
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // products at a raised wave priority, as in the streaming decode (the
+        // waves here run without a block barrier, so they drift out of phase)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int tt = 0; tt < NTT; ++tt) tmp[tt] = mfma16(A[tt][m], W[m], tmp[tt]);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt) acc[tt][rt] += sc * tmp[tt];
       }
@@ -1215,10 +1219,12 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
         f32x4 tmp[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) tmp[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) tmp[rt] = mfma16(A[m], W[rt][m], tmp[rt]);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) acc[tt][rt] += sc[rt] * tmp[rt];
       }
