@@ -126,3 +126,78 @@ def test_container_decodes_to_scale_times_code(fmt, method):
     assert data.size == 64 * codec.block_bytes(fmt)
     t, sb, _, _ = quant.quantize_groups(w, method)
     assert np.array_equal(codec.decode(fmt, data, w.size), np.repeat(codec.f16_to_f64(sb), 128) * t)
+
+
+# --- the float32 decisions against the rule taken exactly --------------------
+# The oracle decides codes in float32 with a fixed summation tree (its reading
+# of the pages, which fix no precision).  Here the same rules are evaluated in
+# float64 from the exact bfloat16 inputs: a group sum of 128 terms has a
+# float32 relative error of at most 7 ulp-halves (seven tree levels, u = 2^-24)
+# and the division one more, so a float32 decision can differ from the exact
+# one only for weights whose 2|w| lies within 8u s of the exact scale s.  Away
+# from that band the codes (and for Lloyd the round count) must be identical,
+# and the stored binary16 scale must equal the exact scale's rounding unless
+# that scale lies within the same band of a binary16 rounding boundary.
+U = 2.0 ** -24
+BAND = 8 * U
+
+
+def exact_groups(w_bits, method):
+    """Per group: codes (int8) and exact scale from the rules in float64, the
+    rounds taken, and whether every decision was clear of the near-tie band."""
+    w = quant.bf16_to_f32(np.asarray(w_bits).reshape(-1, 128)).astype(np.float64)
+    a = np.abs(w)
+    out_t, out_s, out_r, clear = [], [], [], []
+    for g in range(w.shape[0]):
+        s = math.fsum(a[g]) / 128.0
+        ok = True
+
+        def decide(s):
+            nonlocal ok
+            if s > 0 and np.any(np.abs(2 * a[g] - s) <= BAND * s):
+                ok = False
+            return np.where(2 * a[g] > s, np.sign(w[g]), 0.0).astype(np.int8)
+
+        t = decide(s)
+        rounds = 0
+        if method == quant.LLOYD:
+            for _ in range(32):  # the reading's cap of 32 rounds, restated here
+                nz = t != 0
+                s_new = math.fsum(a[g][nz]) / nz.sum() if nz.any() else 0.0
+                t_new = decide(s_new)
+                rounds += 1
+                s = s_new
+                if np.array_equal(t_new, t):
+                    break
+                t = t_new
+            nz = t != 0
+            s = math.fsum(a[g][nz]) / nz.sum() if nz.any() else 0.0
+        out_t.append(t)
+        out_s.append(s)
+        out_r.append(rounds)
+        clear.append(ok)
+    return np.array(out_t), np.array(out_s), np.array(out_r), np.array(clear)
+
+
+def f16_bits_of(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("method", [quant.ABSMEAN, quant.LLOYD])
+def test_float32_decisions_equal_the_exact_rule_away_from_ties(method):
+    rng = np.random.default_rng(11)
+    n = 768
+    w = np.concatenate([rng.standard_normal(n * 64), rng.laplace(size=n * 32), 0.01 * rng.standard_t(3, size=n * 32)])
+    w_bits = bf16_bits(w)
+    t32, s_bits, _, rounds32 = quant.quantize_groups(w_bits, method)
+    t64, s64, rounds64, clear = exact_groups(w_bits, method)
+    t32 = t32.reshape(-1, 128)
+    assert clear.mean() > 0.9, clear.mean()
+    assert np.array_equal(t32[clear], t64[clear])
+    if method == quant.LLOYD:
+        assert np.array_equal(rounds32[clear], rounds64[clear])
+    # the binary16 scale, where the exact scale is clear of a rounding boundary
+    lo, hi = f16_bits_of(s64 * (1 - BAND)), f16_bits_of(s64 * (1 + BAND))
+    firm = clear & (lo == hi)
+    assert firm.mean() > 0.9
+    assert np.array_equal(s_bits[firm], f16_bits_of(s64)[firm])
