@@ -43,6 +43,18 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// SwiGLU's silu(g) * u (Shazeer 2020, "GLU Variants Improve Transformer"),
+// with the hardware reciprocal (within 1 ulp) in place of an IEEE division: a
+// very negative g gives exp(-g) = inf, a reciprocal of 0 and a zero result, as
+// the division does.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __expf(-g)) * u;
+}
+
+// s_getreg operand reading the SIMD field (bits 5:4) of the hardware-ID
+// register (id 4): size - 1 in bits 15:11, bit offset in 10:6, id in 5:0
+constexpr int kHwIdSimd = (1 << 11) | (4 << 6) | 4;
+
 // fp32 -> bf16, rounded to nearest even (NaN stays a quiet NaN): CDNA4 converts
 // in one instruction, two values at a time in the packed form
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -217,7 +217,7 @@ __device__ __forceinline__ void expert_unit(const ExpertArgs& a, const Item& it,
     const int64_t p = it.pos + ti;
     if (MODE == MODE_GATEUP) {
       const float g = 0.5f * acc[0][j], u = 0.5f * acc[1][j];
-      const float hv = g / (1.f + __expf(-g)) * u;
+      const float hv = silu_mul(g, u);
       a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
     } else {
       const int64_t slot = slot_of[ti];
@@ -244,7 +244,7 @@ __device__ __forceinline__ void tile_epilogue(const ExpertArgs& a, const Item& i
     const int64_t p = it.pos + ti;
     if (MODE == MODE_GATEUP) {
       const float g = 0.5f * acc[0][j], u = 0.5f * acc[1][j];
-      const float hv = g / (1.f + __expf(-g)) * u;
+      const float hv = silu_mul(g, u);
       a.h[p * a.f + (int64_t)tile * 16 + i16] = (uint16_t)f32_to_bf16(hv);
     } else {
       const int64_t slot = slot_of[ti];
@@ -799,7 +799,14 @@ __device__ __forceinline__ void act_half_store(const u32x4 (&raw)[2], char* dst_
 // NTT: token tiles of the item (a compile-time count keeps the multiply free of
 // branches).  The activations of group g + 1 are loaded while group g is
 // multiplied and staged after it.
-template <int FMT, int MODE, int NTT, int WAVES, bool PIPE_A>
+//
+// MF: the wave's phase within a group step.  A wave with MF = false decodes
+// group g and then multiplies it; a wave with MF = true multiplies group g
+// (decoded in the previous step) and then decodes group g + 1.  The block
+// barrier of each step keeps all waves in step, so with one wave of each kind
+// on a SIMD one of them issues matrix instructions while the other runs its
+// decode on the vector ALU, instead of both decoding and then both multiplying.
+template <int FMT, int MODE, int NTT, int WAVES, bool PIPE_A, bool MF>
 __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
                                           char* bufs, char* scratch) {
   // the wave index through readfirstlane, so branches on it are scalar (a
@@ -882,24 +889,33 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[tt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // the group's 4 row tiles, decoded once (the byte table is visible after
+  // the first barrier above); then the weights of a later group, fetched in
+  // every wave (an idle wave's rows are the bank's first, in bounds), so the
+  // waits before the staging stores count them exactly
+  u32x4 W[4][4];
+  float sc[4];
+  auto decode_fetch = [&](int gf) {
+    if (active) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) sc[rt] = decode_block_x3<FMT, kLutCopiesWide>(ring[rt], lut, lane, W[rt]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt] + (int64_t)gf * 16 * BB);
+  };
+  if (MF) decode_fetch(min(1, G - 1));  // group 0 decoded, group 1 in flight
+
   // The last step fetches the last group again (in bounds, unused) and
   // restages it into the idle buffer, so the loop body has no branch on g.
   for (int g = 0; g < G; ++g) {
     const int gn = min(g + 1, G - 1);
 #pragma unroll
     for (int pp = 0; pp < P; ++pp) act_half_load<FMT>(srow[pp], gn, sq[pp], sh[pp], s0[pp]);
-    // the group's 4 row tiles, decoded once; then the next group's weights,
-    // fetched in every wave (an idle wave's rows are the bank's first, in
-    // bounds), so the waits before the staging stores count them exactly
-    u32x4 W[4][4];
-    float sc[4];
+    if (!MF) decode_fetch(gn);  // group g decoded, group g + 1 in flight
     if (active) {
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) sc[rt] = decode_block_x3<FMT, kLutCopiesWide>(ring[rt], lut, lane, W[rt]);
-    }
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) ring[rt] = fetch(wrow[rt] + (int64_t)gn * 16 * BB);
-    if (active) {
+      // the products at a raised wave priority, so the SIMD's other wave
+      // decodes in the gaps between them
+      __builtin_amdgcn_s_setprio(1);
       const char* ab = bufs + (g & 1) * kGemmBuf + i16 * kGemmRow + q * 16;
       if constexpr (PIPE_A) {
         // A operands (token tile tt, slice m) in order i = 4 tt + m through a
@@ -952,7 +968,9 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
+    if (MF) decode_fetch(min(g + 2, G - 1));  // group g + 1 decoded, group g + 2 in flight
 #pragma unroll
     for (int pp = 0; pp < P; ++pp)
       act_half_store<FMT>(s0[pp], bufs + ((g + 1) & 1) * kGemmBuf + si[pp] * kGemmRow, sq[pp], sh[pp]);
@@ -973,7 +991,7 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 #pragma unroll
         for (int ft = 0; ft < 2; ++ft) {
           const float gv = 0.5f * acc[tt][ft][j], uv = 0.5f * acc[tt][2 + ft][j];
-          const float hv = gv / (1.f + __expf(-gv)) * uv;
+          const float hv = silu_mul(gv, uv);
           a.h[p * a.f + row0 + 16 * ft + i16] = (uint16_t)f32_to_bf16(hv);
         }
       } else {
@@ -997,11 +1015,17 @@ __device__ __forceinline__ void gemm_unit(const ExpertArgs& a, const Item& it, i
 
 template <int MODE, int FS, int NTT, int WAVES>
 __device__ __forceinline__ void gemm_dispatch(const ExpertArgs& a, const Item& it, int rb, const u32x2* lut,
-                                              char* bufs, bool ptq1) {
-  if (FS != 1 && ptq1)
-    gemm_unit<kPTQ1, MODE, NTT, WAVES, false>(a, it, rb, lut, bufs, nullptr);
-  else if (FS != 2)
-    gemm_unit<kPQ2, MODE, NTT, WAVES, FS == 1>(a, it, rb, lut, bufs, nullptr);
+                                              char* bufs, bool ptq1, bool mf) {
+  if (FS != 1 && ptq1) {
+    // (PTQ1_0: the two phases measured no faster, the byte-table reads of the
+    // decode sharing the LDS with the other wave's operand reads)
+    gemm_unit<kPTQ1, MODE, NTT, WAVES, false, false>(a, it, rb, lut, bufs, nullptr);
+  } else if (FS != 2) {
+    if (mf)
+      gemm_unit<kPQ2, MODE, NTT, WAVES, FS == 1, true>(a, it, rb, lut, bufs, nullptr);
+    else
+      gemm_unit<kPQ2, MODE, NTT, WAVES, FS == 1, false>(a, it, rb, lut, bufs, nullptr);
+  }
 }
 
 // Persistent blocks over units.  Unit l = (item l / row_blocks, row block
@@ -1017,6 +1041,20 @@ void expert_gemm_kernel(ExpertArgs a, int row_blocks) {
   u32x2* lut = (u32x2*)smem;
   char* bufs = smem + lut_bytes;
   if (a.fmt_mask & 2) ptq1_lut_fill<kLutCopiesWide>(lut, threadIdx.x, blockDim.x);  // visible after the unit's first sync
+  // The wave's phase (see gemm_unit): the first wave of the block to arrive on
+  // a SIMD multiplies first, the next one decodes first.  The SIMD comes from
+  // the hardware-ID register, the order of arrival from a counter per SIMD in
+  // shared memory (an initialisation only: any outcome is a correct result).
+  __shared__ int simd_waves[4];
+  if (threadIdx.x < 4) simd_waves[threadIdx.x] = 0;
+  __syncthreads();
+  bool mf;
+  {
+    const int simd = (int)((__builtin_amdgcn_s_getreg(kHwIdSimd) >> 0) & 3);
+    int arrived = 0;
+    if ((threadIdx.x & 63) == 0) arrived = atomicAdd(&simd_waves[simd], 1);
+    mf = (__builtin_amdgcn_readfirstlane(arrived) & 1) == 0;
+  }
   const int64_t U = (int64_t)(*a.n_items) * row_blocks;
   const int64_t per = (U + 7) / 8;
   for (int64_t u = blockIdx.x; u < 8 * per; u += gridDim.x) {
@@ -1026,12 +1064,12 @@ void expert_gemm_kernel(ExpertArgs a, int row_blocks) {
     const int rb = (int)(l % row_blocks);
     const bool ptq1 = FS == 2 || (FS == 3 && a.formats[it.bank] == kPTQ1);
     switch ((it.n + 15) / 16) {
-      case 1: gemm_dispatch<MODE, FS, 1, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      case 2: gemm_dispatch<MODE, FS, 2, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      case 3: gemm_dispatch<MODE, FS, 3, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      case 4: gemm_dispatch<MODE, FS, 4, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      case 5: gemm_dispatch<MODE, FS, 5, WAVES>(a, it, rb, lut, bufs, ptq1); break;
-      default: gemm_dispatch<MODE, FS, kGemmChunk / 16, WAVES>(a, it, rb, lut, bufs, ptq1); break;
+      case 1: gemm_dispatch<MODE, FS, 1, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
+      case 2: gemm_dispatch<MODE, FS, 2, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
+      case 3: gemm_dispatch<MODE, FS, 3, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
+      case 4: gemm_dispatch<MODE, FS, 4, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
+      case 5: gemm_dispatch<MODE, FS, 5, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
+      default: gemm_dispatch<MODE, FS, kGemmChunk / 16, WAVES>(a, it, rb, lut, bufs, ptq1, mf); break;
     }
   }
 }
