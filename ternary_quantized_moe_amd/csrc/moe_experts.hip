@@ -1291,15 +1291,23 @@ __device__ __forceinline__ void down_unit(const ExpertArgs& a, const Item& it, c
     const int el = opaque_tid() & 63, eq = el >> 4, ei = el & 15;
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) {
+      // the token tile's four slots and weights read together (positions past
+      // the item read its last one, unused), so their shared-memory round trips
+      // overlap instead of one per token before its stores
+      int slot[4];
+      float wgt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ti = 16 * tt + 4 * eq + j;
-        if (ti >= it.n) continue;
-        const int64_t slot = vslot[ti];
-        const float wgt = vwgt[ti];
+        const int ti = min(16 * tt + 4 * eq + j, it.n - 1);
+        slot[j] = vslot[ti];
+        wgt[j] = vwgt[ti];
+      }
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-          a.slots[slot * a.d + row0 + 16 * rt + ei] = (uint16_t)f32_to_bf16(wgt * acc[tt][rt][j]);
+      for (int j = 0; j < 4; ++j) {
+        if (16 * tt + 4 * eq + j >= it.n) continue;
+        uint16_t* dst = a.slots + (int64_t)slot[j] * a.d + row0 + ei;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) dst[16 * rt] = (uint16_t)f32_to_bf16(wgt[j] * acc[tt][rt][j]);
       }
     }
 #pragma unroll
